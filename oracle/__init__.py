@@ -1,0 +1,220 @@
+"""CPU oracle for the mixed chunked-prefill + decode step (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this package.
+The product path never does.  The arithmetic lives in oracle.c (fp64, plain loops); this file
+only marshals numpy arrays and keeps the oracle's own dense, per-request view of the cache.
+
+Parity pins for every function here are in tests/test_oracle_pins.py (values fixed by the pages'
+worked example, closed forms, brute force and library routines).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Iterable, List, Optional
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+OK, INVALID_ARG, NO_PAGES, CAPACITY = 0, 1, 2, 3
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        src = os.path.join(_HERE, "oracle.c")
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_plan.restype = ctypes.c_int
+        L.oracle_plan.argtypes = [ctypes.c_int32, _i32p, _i32p, _i32p, _i64p, _i32p,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32,
+                                  _i32p, _i32p, _i32p, _i32p, _i32p, _i32p]
+        L.oracle_rope.restype = None
+        L.oracle_rope.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                  ctypes.c_double, _f64p, _f64p]
+        L.oracle_attention.restype = ctypes.c_int
+        L.oracle_attention.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _f64p, _i32p, _f64p, _f64p,
+                                       ctypes.c_double, _f64p, _f64p, ctypes.c_int32]
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [ctypes.c_double]
+        L.oracle_round.restype = None
+        L.oracle_round.argtypes = [ctypes.c_int64, ctypes.c_int32, _f64p, _f64p]
+        _LIB = L
+    return _LIB
+
+
+def _p(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+# ---------------------------------------------------------------------------------------------
+# Plan
+# ---------------------------------------------------------------------------------------------
+
+def plan(num_computed, num_prompt_left, block_tables: List[np.ndarray], token_budget: int,
+         max_chunk: int, page_size: int, num_pool_pages: int,
+         cap_seqs: Optional[int] = None, cap_pages: Optional[int] = None) -> Dict:
+    """Decode-first budget plan.  Returns {"status", and on OK the metadata arrays + counts}."""
+    nc = np.ascontiguousarray(num_computed, dtype=np.int32)
+    nl = np.ascontiguousarray(num_prompt_left, dtype=np.int32)
+    n = int(nc.shape[0])
+    npg = np.asarray([len(b) for b in block_tables], dtype=np.int32)
+    off = np.zeros(n + 1, dtype=np.int64)
+    off[1:] = np.cumsum(npg)
+    bt = (np.concatenate([np.asarray(b, dtype=np.int32) for b in block_tables])
+          if n and off[-1] > 0 else np.zeros(1, dtype=np.int32))
+    if cap_seqs is None:
+        cap_seqs = n
+    if cap_pages is None:
+        cap_pages = int(off[-1])
+    req_ids = np.zeros(max(cap_seqs, 1), dtype=np.int32)
+    qo = np.zeros(cap_seqs + 1, dtype=np.int32)
+    kvp = np.zeros(cap_seqs + 1, dtype=np.int32)
+    idx = np.zeros(max(cap_pages, 1), dtype=np.int32)
+    last = np.zeros(max(cap_seqs, 1), dtype=np.int32)
+    counts = np.zeros(5, dtype=np.int32)
+    st = lib().oracle_plan(n, _p(nc, _i32p), _p(nl, _i32p), _p(npg, _i32p), _p(off, _i64p),
+                           _p(bt, _i32p), token_budget, max_chunk, page_size, num_pool_pages,
+                           cap_seqs, cap_pages, _p(req_ids, _i32p), _p(qo, _i32p),
+                           _p(kvp, _i32p), _p(idx, _i32p), _p(last, _i32p), _p(counts, _i32p))
+    out = {"status": int(st)}
+    if st in (OK, CAPACITY):
+        ns, nd, nt, npages, ndef = (int(c) for c in counts)
+        out.update(num_seqs=ns, num_decodes=nd, num_tokens=nt, num_pages=npages,
+                   num_deferred_decodes=ndef)
+    if st == OK:
+        out.update(req_ids=req_ids[:ns].copy(), qo_indptr=qo[:ns + 1].copy(),
+                   kv_page_indptr=kvp[:ns + 1].copy(), kv_page_indices=idx[:npages].copy(),
+                   kv_last_page_len=last[:ns].copy())
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Rotary embedding, rounding, attention
+# ---------------------------------------------------------------------------------------------
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float = 10000.0) -> np.ndarray:
+    """x: [ntok, nheads, d]; pos: [ntok] absolute positions.  fp64 result, not rounded."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    ntok, nh, d = x.shape
+    out = np.empty_like(x)
+    lib().oracle_rope(ntok, nh, d, _p(pos, _i32p), float(theta), _p(x, _f64p), _p(out, _f64p))
+    return out
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """One rounding of fp64 values to bf16 or fp32, returned as fp64 values."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    lib().oracle_round(x.size, 1 if dtype == "bf16" else 0, _p(x, _f64p), _p(out, _f64p))
+    return out
+
+
+def bf16_value(x: float) -> float:
+    return float(lib().oracle_bf16_value(float(x)))
+
+
+def attention(q: np.ndarray, pos: np.ndarray, k: np.ndarray, v: np.ndarray,
+              scale: Optional[float] = None, nthreads: Optional[int] = None):
+    """One request: q [nrows, Hq, d], k/v [kv_len, Hkv, d].  Returns (out [nrows,Hq,d], lse)."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    nrows, hq, d = q.shape
+    kv_len, hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.empty((nrows, hq, d), dtype=np.float64)
+    lse = np.empty((nrows, hq), dtype=np.float64)
+    st = lib().oracle_attention(nrows, hq, hkv, d, kv_len, _p(q, _f64p), _p(pos, _i32p),
+                                _p(k, _f64p), _p(v, _f64p), float(scale), _p(out, _f64p),
+                                _p(lse, _f64p), nthreads or default_threads())
+    if st != OK:
+        raise ValueError(f"oracle_attention: invalid arguments (status {st})")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# A session: the oracle's own dense cache, advanced step by step
+# ---------------------------------------------------------------------------------------------
+
+class Session:
+    """Dense fp64 K/V per tracked request, plus the request progress the plan needs.
+
+    requests -- the request indices whose cache is kept (default: all).  Untracked requests are
+                still planned (the plan only needs their sizes) but get no attention output.
+    """
+
+    def __init__(self, wl, requests: Optional[Iterable[int]] = None):
+        self.wl = wl
+        self.num_computed = wl.num_computed.astype(np.int32).copy()
+        self.num_prompt_left = wl.num_prompt_left.astype(np.int32).copy()
+        tracked = range(wl.n) if requests is None else requests
+        self.k: Dict[int, np.ndarray] = {}
+        self.v: Dict[int, np.ndarray] = {}
+        for r in tracked:
+            hk, hv = wl.history(r)
+            self.k[r] = hk.astype(np.float64)
+            self.v[r] = hv.astype(np.float64)
+
+    def plan(self) -> Dict:
+        wl = self.wl
+        return plan(self.num_computed, self.num_prompt_left, wl.block_tables, wl.token_budget,
+                    wl.max_chunk, wl.page_size, wl.num_pool_pages)
+
+    def step(self, p: Dict, q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray,
+             rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> Dict:
+        """Run one step from the oracle's own plan `p` on the raw new-token rows (plan order).
+
+        Appends the rotated, rounded keys and the values of every scheduled token of tracked
+        requests, then attends the chosen rows (default: every row of tracked requests).
+        Returns q_rot [T,Hq,d], k_rot [T,Hkv,d], o [T,Hq,d], lse [T,Hq], pos [T] (fp64; rows not
+        attended hold NaN) and, per tracked request, nothing else: the cache is self.k / self.v.
+        """
+        wl = self.wl
+        T = int(p["num_tokens"])
+        qo = p["qo_indptr"]
+        pos = np.empty(T, dtype=np.int32)
+        for s, r in enumerate(p["req_ids"]):
+            b, e = int(qo[s]), int(qo[s + 1])
+            pos[b:e] = self.num_computed[r] + np.arange(e - b, dtype=np.int32)
+        q_rot = round_to(rope(q_raw, pos, wl.rope_theta), wl.dtype)
+        k_rot = round_to(rope(k_raw, pos, wl.rope_theta), wl.dtype)
+        v_new = np.asarray(v_raw, dtype=np.float64)
+        o = np.full((T, wl.num_q_heads, wl.head_dim), np.nan)
+        lse = np.full((T, wl.num_q_heads), np.nan)
+        want = np.ones(T, dtype=bool) if rows is None else np.isin(np.arange(T), rows)
+        for s, r in enumerate(p["req_ids"]):
+            r = int(r)
+            b, e = int(qo[s]), int(qo[s + 1])
+            if r in self.k:
+                self.k[r] = np.concatenate([self.k[r], k_rot[b:e]], axis=0)
+                self.v[r] = np.concatenate([self.v[r], v_new[b:e]], axis=0)
+                sel = np.nonzero(want[b:e])[0] + b
+                if sel.size:
+                    oo, ll = attention(q_rot[sel], pos[sel], self.k[r], self.v[r],
+                                       wl.sm_scale, nthreads)
+                    o[sel] = oo
+                    lse[sel] = ll
+            self.num_computed[r] += e - b
+            if self.num_prompt_left[r] > 0:
+                self.num_prompt_left[r] -= e - b
+        return {"q_rot": q_rot, "k_rot": k_rot, "o": o, "lse": lse, "pos": pos}
