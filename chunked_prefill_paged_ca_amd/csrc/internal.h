@@ -1,0 +1,55 @@
+// internal.h -- declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "ca.h"
+
+namespace ca {
+
+// Thread-local detail message behind ca_last_error().
+void set_error(const std::string& msg);
+void clear_error();
+
+// Device view of a plan (the four ragged metadata arrays plus counts).  Kernels derive
+//   kv_len(s) = (kv_page_indptr[s+1] - kv_page_indptr[s] - 1) * P + kv_last_page_len[s]
+//   q_len(s)  = qo_indptr[s+1] - qo_indptr[s]
+//   position of row t of s = kv_len(s) - q_len(s) + (t - qo_indptr[s]).
+struct DevPlan {
+    const int32_t* qo_indptr;
+    const int32_t* kv_page_indptr;
+    const int32_t* kv_page_indices;
+    const int32_t* kv_last_page_len;
+    int32_t num_seqs;
+    int32_t num_decodes;
+    int32_t num_tokens;
+    int32_t num_pages;
+    int32_t page_size;
+};
+
+struct Shape {
+    int32_t hq, hkv, d, P;
+    float scale;
+    double theta;
+    ca_dtype dtype;
+};
+
+// ---- launchers (each enqueues on `stream`; returns hipSuccess or the launch error) ----
+hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const void* q_in, void* q_out,
+                              const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, hipStream_t stream);
+
+// Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
+// partial: fp32 workspace of num_tokens * hq * nsplit * (d + 2) floats.
+hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, const void* q,
+                                    const void* k_cache, const void* v_cache, void* o,
+                                    float* lse, float* partial, int nsplit,
+                                    hipStream_t stream);
+
+size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
+
+}  // namespace ca

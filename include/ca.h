@@ -1,0 +1,167 @@
+/*
+ * ca.h -- C ABI of the MI355X (gfx950) mixed chunked-prefill + decode paged-attention library.
+ *
+ * One call of ca_plan_batch + ca_append_kv_rope + ca_mixed_attention is one step of the
+ * Sarathi-Serve style mixed batch: running decodes contribute one query each, prefill prompts
+ * contribute a chunk of queries at absolute positions [s_{k-1}, s_k), and every query attends
+ * causally to all keys of its own request up to and including itself, read from a paged KV
+ * cache (history pages plus the pages the current chunk was just appended to).
+ *
+ * Sources (page title, then the section the call follows):
+ *   [SS] pinghaoyang.com.cn/aigc/posts/sarathi-serve/  "Sarathi-Serve 完全拆解"
+ *   [CP] blog.vllbc.top/visual-reading/chunked-prefill-pd-disaggregation/  "Chunked Prefill 与 PD 分离"
+ *   [SF] magicnetworld.com/tech/articles/2026-10-02-chunked-prefill-stall-free-scheduling/
+ *        "分块预填充与 Stall-free 调度"
+ *
+ * Conventions shared by every entry point:
+ *   - The caller owns every buffer.  Host arrays are plain pointers; device buffers are device
+ *     pointers (e.g. from hipMalloc or a framework allocator).  No pointer is retained after a
+ *     call returns.  A ca_ctx owns only its internal workspace (pinned staging memory, device
+ *     metadata and split-KV partials), grown on demand and freed by ca_destroy.
+ *   - Device work is enqueued asynchronously on the given hipStream_t (passed as void*; NULL is
+ *     the null stream) and never synchronised by the library.  One ctx must not be used from
+ *     two streams concurrently unless the caller orders those streams.
+ *   - Errors: every call returns a ca_status; ca_last_error() gives a detail message for the
+ *     calling thread.  Arguments are validated before anything is enqueued; on an error
+ *     nothing is launched.
+ *
+ * Paged KV cache layout (element type per ca_dtype, page size P, head dim d, Hkv kv heads):
+ *   k_cache: [num_pool_pages][Hkv][P][d]   -- token-major inside a page
+ *   v_cache: [num_pool_pages][Hkv][d][P]   -- dimension-major inside a page ("transposed" V page)
+ * Each (page, kv head) block is one contiguous P*d run in both caches.  Token at absolute
+ * position p of a request lives in logical page p / P, slot p % P.
+ */
+#ifndef CA_H
+#define CA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CA_OK = 0,
+    CA_ERR_INVALID_ARG = 1, /* null pointer, bad size, page id outside the pool, ... */
+    CA_ERR_NO_PAGES = 2,    /* a decode's block table has no free slot for its new token */
+    CA_ERR_CAPACITY = 3,    /* caller arrays too small; required sizes are in the counts */
+    CA_ERR_UNSUPPORTED = 4, /* a valid but unimplemented shape (e.g. head_dim not 64/128) */
+    CA_ERR_DEVICE = 5       /* a HIP runtime error */
+} ca_status;
+
+typedef enum { CA_BF16 = 0, CA_FP32 = 1 } ca_dtype;
+
+/* One request as the scheduler sees it at the start of a step ([SS] "分块不等于截断上下文", last
+ * paragraph: processed length, chunk length, absolute positions, block table, last-page length). */
+typedef struct {
+    int32_t num_computed;       /* tokens already in the KV cache (prefix hits included) */
+    int32_t num_prompt_left;    /* prompt tokens not yet computed; 0 marks a decode */
+    int32_t num_pages;          /* entries in block_table */
+    int32_t reserved;
+    const int32_t* block_table; /* host memory: physical page id of logical page i */
+} ca_request;
+
+typedef struct {
+    int32_t token_budget;   /* tau: total query tokens of the step, decodes included (> 0) */
+    int32_t max_chunk;      /* per-request cap on a prefill chunk; 0 = no cap */
+    int32_t page_size;      /* P (> 0) */
+    int32_t reserved;
+    int64_t num_pool_pages; /* page ids must lie in [0, num_pool_pages) */
+} ca_plan_params;
+
+/* Plan output.  The caller allocates the arrays (host memory) and sets the capacities; the
+ * library fills the arrays and the counts.  Scheduled sequence s (s < num_seqs) is request
+ * req_ids[s]; sequences [0, num_decodes) are decodes ([SS] "混合批不是把两类注意力强行做成同一个形状"
+ * names the four metadata arrays). */
+typedef struct {
+    int32_t cap_seqs;          /* capacity of req_ids, kv_last_page_len; indptrs hold cap_seqs+1 */
+    int32_t cap_pages;         /* capacity of kv_page_indices */
+    int32_t* req_ids;          /* [num_seqs] index into the request array */
+    int32_t* qo_indptr;        /* [num_seqs+1] rows of sequence s in the flat token arrays */
+    int32_t* kv_page_indptr;   /* [num_seqs+1] */
+    int32_t* kv_page_indices;  /* [num_pages] physical pages of each sequence after the append */
+    int32_t* kv_last_page_len; /* [num_seqs] valid slots of the last page, in [1, P] */
+    int32_t num_seqs;          /* out */
+    int32_t num_decodes;       /* out */
+    int32_t num_tokens;        /* out: T = qo_indptr[num_seqs] */
+    int32_t num_pages;         /* out: kv_page_indptr[num_seqs] */
+    int32_t num_deferred_decodes; /* out: decodes left out because the budget ran out */
+    int32_t page_size;         /* out: P the plan was made for */
+    uint64_t generation;       /* out: unique per successful plan; keys the device-side copy */
+} ca_plan;
+
+typedef struct {
+    int32_t num_q_heads;  /* Hq */
+    int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0, q head h reads kv head h / (Hq / Hkv) */
+    int32_t head_dim;     /* d: 64 or 128 */
+    int32_t page_size;    /* P: must equal the plan's */
+    ca_dtype dtype;       /* storage type of q, k, v, caches and o; accumulation is fp32 */
+    float sm_scale;       /* 0 => 1 / sqrt(d) */
+    float rope_theta;     /* 0 => 10000 */
+} ca_attn_desc;
+
+typedef struct ca_ctx ca_ctx;
+
+/* Create a context bound to HIP device `device`.  *out receives the handle. */
+ca_status ca_create(int device, ca_ctx** out);
+/* Free the context's workspace (waits for nothing: the caller must have synchronised the
+ * streams it used with this context). */
+ca_status ca_destroy(ca_ctx* ctx);
+
+/*
+ * ca_plan_batch -- decode-first token-budget packing of one step (host only, no device work).
+ * Follows [SS] "一个 512-token 预算的例子", [CP] "3.1 Algorithm 3 的顺序" and [SF] "六·补二":
+ *   1. decodes (num_prompt_left == 0), in caller order, one token each, while budget remains;
+ *      the rest are deferred and counted in num_deferred_decodes;
+ *   2. prefills, in caller order (list in-progress chunks before new requests), each getting
+ *      min(num_prompt_left, budget left, max_chunk if > 0, free slots of its block table);
+ *      the scan stops when the budget is used up.  Several chunks may share a step.
+ * For each scheduled sequence: kv_len = num_computed + q, pages = ceil(kv_len / P) taken from
+ * the front of its block table, kv_last_page_len = kv_len - (pages - 1) * P.
+ * Errors: CA_ERR_INVALID_ARG (n < 0, budget/page size <= 0, negative fields, missing table,
+ * a scheduled page id outside the pool), CA_ERR_NO_PAGES (a decode whose table has fewer than
+ * num_computed + 1 slots), CA_ERR_CAPACITY (num_seqs > cap_seqs or num_pages > cap_pages; the
+ * counts then hold the required sizes).
+ */
+ca_status ca_plan_batch(const ca_request* reqs, int32_t n, const ca_plan_params* params,
+                        ca_plan* plan);
+
+/*
+ * ca_append_kv_rope -- rotary embedding at absolute positions, then append the step's K/V.
+ * ([SS] "分块不等于截断上下文": positions continue across chunks, and a chunk's K/V is in the paged
+ * cache before its queries read the history pages together with the chunk's own pages.)
+ * Row t of sequence s sits at absolute position p = kv_len_s - q_s + (t - qo_indptr[s]).
+ *   q_in, q_out : [T, Hq, d]  (q_out may equal q_in)   q_out = RoPE_p(q_in)
+ *   k_new, v_new: [T, Hkv, d]                           k_cache <- RoPE_p(k_new), v_cache <- v_new
+ * RoPE pairs element i with i + d/2 and turns the pair by p * theta^(-2i/d); angles are formed
+ * in fp64 and each result is rounded once to the storage type.  V is not rotated.
+ * The slots written are those of positions [kv_len - q, kv_len) of every scheduled sequence.
+ */
+ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                            const void* q_in, void* q_out, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, int64_t num_pool_pages,
+                            void* hip_stream);
+
+/*
+ * ca_mixed_attention -- causal attention of every row of the step over the paged cache.
+ * For row t at position p of sequence s and q head h (kv head g = h / (Hq/Hkv)):
+ *   s_j      = scale * (q[t,h,:] . k_j[g,:])  for keys j = 0..p of sequence s
+ *   o[t,h,:] = sum_{j<=p} softmax_j(s) v_j[g,:]     (scale = desc->sm_scale)
+ *   lse[t,h] = log sum_{j<=p} exp(s_j)  (natural log; pass NULL to skip)
+ * ([SS] "分块不等于截断上下文"; decodes are the case p = kv_len - 1.)
+ *   q: [T, Hq, d] (already rotated), o: [T, Hq, d], lse: [T, Hq] fp32 or NULL.
+ * Decode rows use a split-KV kernel whose partials are merged by log-sum-exp weights; chunk
+ * rows use an LDS-staged bf16 MFMA kernel (fp32 storage uses a plain fp32 kernel).
+ */
+ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             int64_t num_pool_pages, void* o, float* lse, void* hip_stream);
+
+const char* ca_status_string(ca_status s);
+/* Detail message of the calling thread's last failed call ("" if none). */
+const char* ca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CA_H */

@@ -1,0 +1,113 @@
+"""Test/bench harness: lay workload inputs into the library's paged layout and read them back.
+
+Page layout of the library (include/ca.h): k_cache [pool][Hkv][P][d], v_cache [pool][Hkv][d][P].
+These helpers only move data (scatter / gather by block table); they compute nothing.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional
+
+import numpy as np
+
+
+def torch_dtype(dt: str):
+    import torch
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def alloc_pool(wl, device="cuda", fill: Optional[float] = float("nan")):
+    import torch
+    td = torch_dtype(wl.dtype)
+    P, H, d = wl.page_size, wl.num_kv_heads, wl.head_dim
+    k = torch.empty((wl.num_pool_pages, H, P, d), dtype=td, device=device)
+    v = torch.empty((wl.num_pool_pages, H, d, P), dtype=td, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def random_pool(wl, seed: int, device="cuda"):
+    """Whole pool filled with N(0,1) values drawn on the device (background for big configs)."""
+    import torch
+    k, v = alloc_pool(wl, device, fill=None)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    for t in (k, v):
+        flat = t.view(-1)
+        step = 1 << 28
+        for b in range(0, flat.numel(), step):
+            e = min(b + step, flat.numel())
+            flat[b:e] = torch.randn(e - b, generator=gen, device=device, dtype=torch.float32).to(t.dtype)
+    return k, v
+
+
+def _slots(table: np.ndarray, P: int, start: int, stop: int):
+    pos = np.arange(start, stop)
+    return table[pos // P].astype(np.int64), (pos % P).astype(np.int64)
+
+
+def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None):
+    """Scatter each request's drawn history (positions 0..nc-1) into its pages."""
+    import torch
+    reqs = range(wl.n) if requests is None else requests
+    dev = k_cache.device
+    for r in reqs:
+        nc = int(wl.num_computed[r])
+        if nc == 0:
+            continue
+        hk, hv = wl.history(r)
+        pages, slots = _slots(wl.block_tables[r], wl.page_size, 0, nc)
+        pi = torch.from_numpy(pages).to(dev)
+        si = torch.from_numpy(slots).to(dev)
+        k_cache[pi, :, si, :] = torch.from_numpy(hk).to(dev, k_cache.dtype)
+        v_cache[pi, :, :, si] = torch.from_numpy(hv).to(dev, v_cache.dtype)
+
+
+def read_dense(k_cache, v_cache, table: np.ndarray, P: int, kv_len: int):
+    """Gather positions 0..kv_len-1 of one request back into dense [kv_len, Hkv, d] float64."""
+    import torch
+    pages, slots = _slots(table, P, 0, kv_len)
+    pi = torch.from_numpy(pages).to(k_cache.device)
+    si = torch.from_numpy(slots).to(k_cache.device)
+    k = k_cache[pi, :, si, :].float().cpu().numpy().astype(np.float64)
+    v = v_cache[pi, :, :, si].float().cpu().numpy().astype(np.float64)
+    return k, v
+
+
+def to_device(x: np.ndarray, dt: str, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device).to(torch_dtype(dt))
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray, dt: str) -> np.ndarray:
+    """|a - b| in units of the storage type's spacing at b (both hold storage-type values)."""
+    mant = 7 if dt == "bf16" else 23
+    b = np.asarray(b, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -126)))
+    return np.abs(np.asarray(a, dtype=np.float64) - b) / np.exp2(e - mant)
+
+
+def gpu_step(ctx, wl, plan, q_raw, k_raw, v_raw, k_cache, v_cache, want_lse=True, stream=None):
+    """One step through the C ABI: append + RoPE, then mixed attention.  Returns device tensors."""
+    import torch
+    from chunked_prefill_paged_ca_amd import make_desc
+    desc = make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
+    q_in = to_device(q_raw, wl.dtype)
+    k_in = to_device(k_raw, wl.dtype)
+    v_in = to_device(v_raw, wl.dtype)
+    q_out = torch.empty_like(q_in)
+    ctx.append_kv_rope(desc, plan, q_in, q_out, k_in, v_in, k_cache, v_cache, wl.num_pool_pages,
+                       stream=stream)
+    o = torch.empty_like(q_out)
+    lse = (torch.empty((plan.num_tokens, wl.num_q_heads), dtype=torch.float32, device=q_in.device)
+           if want_lse else None)
+    ctx.mixed_attention(desc, plan, q_out, k_cache, v_cache, wl.num_pool_pages, o, lse,
+                        stream=stream)
+    return q_out, o, lse
+
+
+def lib_plan(wl, num_computed, num_prompt_left):
+    import chunked_prefill_paged_ca_amd as ca
+    return ca.plan_batch(num_computed, num_prompt_left, wl.block_tables, wl.token_budget,
+                         wl.max_chunk, wl.page_size, wl.num_pool_pages)

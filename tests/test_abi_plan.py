@@ -1,0 +1,106 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and its host plan
+equals the oracle's plan bit for bit (statuses, counts and every metadata array)."""
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import chunked_prefill_paged_ca_amd as ca
+from chunked_prefill_paged_ca_amd import binding
+from chunked_prefill_paged_ca_amd.workload import make_config
+
+
+@pytest.fixture(scope="module")
+def L():
+    from __graft_entry__ import ensure_built
+    ensure_built()
+    return ca.lib()
+
+
+def test_exports_every_header_symbol(L):
+    syms = ca.header_symbols()
+    assert {"ca_plan_batch", "ca_append_kv_rope", "ca_mixed_attention", "ca_create",
+            "ca_destroy", "ca_status_string", "ca_last_error"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert binding.status_string(s)
+
+
+def _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=None, cap_pages=None):
+    o = oracle_mod.plan(nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, cap_pages=cap_pages)
+    p = ca.plan_batch(nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, cap_pages=cap_pages,
+                      raise_on_error=False)
+    assert p.status == o["status"], (p.status, o["status"], binding.last_error())
+    if o["status"] in (0, 3):
+        for k in ("num_seqs", "num_decodes", "num_tokens", "num_pages", "num_deferred_decodes"):
+            assert getattr(p, k) == o[k], k
+    if o["status"] == 0:
+        a = p.arrays()
+        for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
+            assert np.array_equal(a[k], o[k]), k
+        assert p.generation > 0
+    return p, o
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+def test_plan_matches_oracle_on_configs(L, oracle_mod, cfg):
+    wl = make_config(cfg)
+    p, o = _compare(oracle_mod, wl.num_computed, wl.num_prompt_left, wl.block_tables,
+                    wl.token_budget, wl.max_chunk, wl.page_size, wl.num_pool_pages)
+    assert o["status"] == 0 and o["num_tokens"] <= wl.token_budget
+
+
+@pytest.mark.parametrize("c", [64, 256, 2048, 8192])
+def test_plan_sweep_matches_oracle(L, oracle_mod, c):
+    wl = make_config(3, chunk=c)
+    nc, left = wl.num_computed.copy(), wl.num_prompt_left.copy()
+    for _ in range(wl.steps):
+        p, o = _compare(oracle_mod, nc, left, wl.block_tables, wl.token_budget, 0, 16,
+                        wl.num_pool_pages)
+        q = o["num_tokens"]
+        assert q == min(c, int(left[0]))
+        nc[0] += q
+        left[0] -= q
+    assert left[0] == 0
+
+
+req = st.tuples(st.integers(0, 200), st.integers(0, 300), st.integers(0, 3))
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(reqs=st.lists(req, min_size=0, max_size=30), tau=st.integers(1, 700),
+       mc=st.sampled_from([0, 0, 1, 7, 64]), P=st.sampled_from([1, 16, 5]),
+       decode_frac=st.floats(0, 1), seed=st.integers(0, 2 ** 31 - 1),
+       bad_page=st.booleans(), cap_cut=st.integers(0, 3))
+def test_plan_matches_oracle_random(L, oracle_mod, reqs, tau, mc, P, decode_frac, seed,
+                                    bad_page, cap_cut):
+    rng = np.random.default_rng(seed)
+    nc, left, tables = [], [], []
+    next_page = 0
+    for (c, lft, extra) in reqs:
+        is_dec = rng.random() < decode_frac
+        lft = 0 if is_dec else max(1, lft)
+        need = -(-(c + max(1, lft)) // P)
+        npg = max(0, need + extra - 1)  # sometimes one page short (NO_PAGES / room cap)
+        tables.append(np.arange(next_page, next_page + npg, dtype=np.int32))
+        next_page += npg
+        nc.append(c)
+        left.append(lft)
+    pool = max(next_page, 1)
+    if bad_page and tables and tables[0].size:
+        tables[0] = tables[0].copy()
+        tables[0][0] = pool + 3
+    cap_seqs = max(0, len(reqs) - cap_cut) if cap_cut == 3 else None
+    _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs)
+
+
+def test_plan_rejects_bad_params(L, oracle_mod):
+    t = [np.array([0], np.int32)]
+    for args in ((t, 0, 0, 16, 4), (t, 8, -1, 16, 4), (t, 8, 0, 0, 4), (t, 8, 0, 16, 0)):
+        _compare(oracle_mod, [1], [0], *args)
+    _compare(oracle_mod, [-3], [0], t, 8, 0, 16, 4)
+    _compare(oracle_mod, [3], [-1], t, 8, 0, 16, 4)

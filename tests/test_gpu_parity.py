@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the same seeded inputs.
+
+Bars (fixed before any kernel ran):
+  * plan metadata and page indices: bit-exact;
+  * rotated q and the appended K/V: at most 1 unit in the last place of the storage type (both
+    sides round an fp64 rotation once; only a near-tie in the last bit may differ), history
+    bit-exact;
+  * attention output: max |o - o_oracle| <= 2e-2 in bf16 storage, <= 1e-4 in fp32 storage;
+    lse within 2e-3 (bf16) / 1e-5 (fp32) -- scores are exact products of stored values summed in
+    fp32, so lse error is fp32 summation error only.
+Unused pool pages and the unused tail of every last page hold NaN, so a kernel that reads a
+slot it should not see, or lets a masked slot's value through, fails.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"bf16": 2e-2, "fp32": 1e-4}
+TOL_LSE = {"bf16": 2e-3, "fp32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from __graft_entry__ import ensure_built
+    ensure_built()
+    import chunked_prefill_paged_ca_amd as ca
+    import oracle
+    assert torch.cuda.is_available()
+    ctx = ca.create(0)
+    yield ctx, oracle
+    ctx.close()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def run_and_check(ctx, oracle, wl, steps=None, rows_per_seq=None, track=None, pool=None,
+                  check_cache=True, label=""):
+    """Run `steps` steps on GPU and oracle; compare everything compared in the module docstring.
+
+    rows_per_seq -- if set, attend-check only this many rows per sequence (sampled, incl. last).
+    track        -- request indices the oracle keeps a cache for (default all).
+    Returns per-step outputs for further checks.
+    """
+    import torch
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor
+    from tests import harness as H
+
+    dt = wl.dtype
+    if pool is None:
+        k_cache, v_cache = H.alloc_pool(wl)
+        H.write_history(wl, k_cache, v_cache)
+    else:
+        k_cache, v_cache = pool
+    sess = oracle.Session(wl, requests=track)
+    cur = StreamCursor(wl)
+    rng = np.random.default_rng(1234)
+    results = []
+    for step in range(steps or wl.steps):
+        ref_plan = sess.plan()
+        plan = H.lib_plan(wl, sess.num_computed, sess.num_prompt_left)
+        a = plan.arrays()
+        for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
+            assert np.array_equal(a[k], ref_plan[k]), (label, step, k)
+        q, k, v = cur.take(ref_plan["req_ids"], np.diff(ref_plan["qo_indptr"]))
+        q_out, o, lse = H.gpu_step(ctx, wl, plan, q, k, v, k_cache, v_cache)
+        torch.cuda.synchronize()
+        rows = None
+        if rows_per_seq is not None:
+            sel = []
+            qo = ref_plan["qo_indptr"]
+            for s_ in range(len(qo) - 1):
+                b, e = int(qo[s_]), int(qo[s_ + 1])
+                pick = set([e - 1, b])
+                if e - b > 2:
+                    pick |= set(rng.choice(np.arange(b, e), size=min(rows_per_seq, e - b), replace=False).tolist())
+                sel += sorted(pick)
+            rows = np.asarray(sel)
+        ref = sess.step(ref_plan, q, k, v, rows=rows)
+        go = o.float().cpu().numpy().astype(np.float64)
+        gl = lse.cpu().numpy().astype(np.float64)
+        gq = q_out.float().cpu().numpy().astype(np.float64)
+        uq = H.ulp_distance(gq, ref["q_rot"], dt)
+        assert uq.max() <= 1.0, (label, step, "q_rot ulp", uq.max())
+        mask = ~np.isnan(ref["o"][:, 0, 0])
+        err = np.abs(go[mask] - ref["o"][mask]).max() if mask.any() else 0.0
+        lerr = np.abs(gl[mask] - ref["lse"][mask]).max() if mask.any() else 0.0
+        _log(f"[{label}] step {step}: T={plan.num_tokens} seqs={plan.num_seqs} "
+             f"decodes={plan.num_decodes} rows checked={int(mask.sum())} max|do|={err:.3e} "
+             f"max|dlse|={lerr:.3e} q-rot mismatches={int((uq > 0).sum())}")
+        assert np.all(np.isfinite(go)), (label, step, "non-finite output")
+        assert err <= TOL_O[dt], (label, step, err)
+        assert lerr <= TOL_LSE[dt], (label, step, lerr)
+        if check_cache:
+            for r in (sess.k.keys()):
+                kv_len = int(sess.num_computed[r])
+                gk, gv = H.read_dense(k_cache, v_cache, wl.block_tables[r], wl.page_size, kv_len)
+                uk = H.ulp_distance(gk, sess.k[r], dt)
+                assert uk.max() <= 1.0, (label, step, r, "k cache ulp", uk.max())
+                assert np.array_equal(gv, sess.v[r]), (label, step, r, "v cache")
+        results.append((ref_plan, go, gl, ref))
+    return results, (k_cache, v_cache), sess
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_tiny_chunked_matches_oracle_and_one_shot(env, dt):
+    """Config 1: 4 steps of (3 decodes + a 16-row chunk), then the same prompt one-shot."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    from tests import harness as H
+    ctx, oracle = env
+    wl = make_config(1, dtype=dt)
+    res, (kc, vc), sess = run_and_check(ctx, oracle, wl, label=f"tiny-{dt}")
+    one = make_config(1, one_shot=True, dtype=dt)
+    res1, (kc1, vc1), sess1 = run_and_check(ctx, oracle, one, label=f"tiny-oneshot-{dt}")
+    # chunked == one-shot on the GPU: the prompt's final cache bit-exact, outputs within tolerance
+    gk, gv = H.read_dense(kc, vc, wl.block_tables[3], 16, 64)
+    gk1, gv1 = H.read_dense(kc1, vc1, one.block_tables[0], 16, 64)
+    assert np.array_equal(gk, gk1) and np.array_equal(gv, gv1)
+    chunk_o = np.concatenate([go[p["qo_indptr"][p["num_decodes"]]:] for p, go, gl, ref in res])
+    one_o = res1[0][1]
+    assert np.abs(chunk_o - one_o).max() <= TOL_O[dt]
+
+
+@pytest.mark.parametrize("variant", ["base", "peaky"])
+def test_mistral_mixed_full(env, variant):
+    """Config 2 at full size: 80 decodes + P(300 on 1200) + Q(132 on 2048), every row checked."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    ctx, oracle = env
+    wl = make_config(2, peaky=(variant == "peaky"))
+    res, _, _ = run_and_check(ctx, oracle, wl, label=f"mistral-{variant}")
+    p = res[0][0]
+    assert list(np.diff(p["qo_indptr"])[-2:]) == [300, 132] and p["num_tokens"] == 512
+
+
+def test_mistral_value_one_every_row(env):
+    """V == 1 everywhere: every output of every row must be exactly representable 1 (softmax
+    weights sum to one) -- a property checked on all T x Hq x d outputs."""
+    import torch
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, make_config
+    from tests import harness as H
+    ctx, oracle = env
+    wl = make_config(2, kv_value=1.0)
+    kc, vc = H.alloc_pool(wl)
+    H.write_history(wl, kc, vc)
+    plan = H.lib_plan(wl, wl.num_computed, wl.num_prompt_left)
+    q, k, v = StreamCursor(wl).take(plan.arrays()["req_ids"], np.diff(plan.arrays()["qo_indptr"]))
+    _, o, lse = H.gpu_step(ctx, wl, plan, q, k, v, kc, vc)
+    torch.cuda.synchronize()
+    err = (o.float() - 1.0).abs().max().item()
+    _log(f"[mistral V=1] max|o-1| = {err:.3e}")
+    assert err <= 2 ** -8
+
+
+def test_yi_share_sampled(env):
+    """Config 4 at full size: 128 decodes + one 1920-row chunk at 14336, sampled rows."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    ctx, oracle = env
+    wl = make_config(4)
+    dec = list(range(0, 128, 8))
+    run_and_check(ctx, oracle, wl, rows_per_seq=48, track=dec + [128], label="yi-share")
+
+
+def test_llama70b_share_sampled(env):
+    """Config 5 at full size on a fragmented 128K-page pool: 256 decodes + 3 chunks, sampled
+    requests (the rest of the pool holds device-drawn random values)."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    from tests import harness as H
+    ctx, oracle = env
+    wl = make_config(5)
+    kc, vc = H.random_pool(wl, seed=5)
+    track = list(range(0, 256, 16)) + [int(np.argmax(wl.num_computed[:256]))] + [256, 257, 258]
+    H.write_history(wl, kc, vc, track)
+    run_and_check(ctx, oracle, wl, rows_per_seq=24, track=track, pool=(kc, vc), label="70b-share")
+
+
+@pytest.mark.parametrize("c", [512, 2048])
+def test_sweep_chunked_vs_one_shot(env, c):
+    """Config 3: one 8192-token prompt in chunks of c against the oracle (sampled rows each
+    step), then against the GPU's own one-shot run: same final cache bit for bit."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    from tests import harness as H
+    ctx, oracle = env
+    wl = make_config(3, chunk=c)
+    res, (kc, vc), _ = run_and_check(ctx, oracle, wl, rows_per_seq=6, check_cache=False,
+                                     label=f"sweep-c{c}")
+    one = make_config(3, one_shot=True)
+    res1, (kc1, vc1), _ = run_and_check(ctx, oracle, one, rows_per_seq=16, check_cache=False,
+                                        label="sweep-oneshot")
+    gk, gv = H.read_dense(kc, vc, wl.block_tables[0], 16, 8192)
+    gk1, gv1 = H.read_dense(kc1, vc1, one.block_tables[0], 16, 8192)
+    assert np.array_equal(gk, gk1) and np.array_equal(gv, gv1)
+    chunk_o = np.concatenate([go for p, go, gl, ref in res])
+    assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
+
+
+def test_edge_cases(env):
+    """kv_len 1 decode, a decode filling its last page exactly, 1-row chunks, a chunk starting
+    on a page boundary, GQA group 8 with d = 64, and page-permutation invariance."""
+    import torch
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, Workload
+    from tests import harness as H
+    ctx, oracle = env
+    for hq, hkv, d in ((8, 1, 64), (4, 4, 128), (12, 4, 128)):
+        nc = np.array([0, 15, 31, 0, 16, 40], np.int32)
+        left = np.array([0, 0, 0, 1, 1, 33], np.int32)
+        stream = np.array([1, 1, 1, 1, 1, 33], np.int32)
+        pool = 64
+        perm = np.random.default_rng(9).permutation(pool).astype(np.int32)
+        tabs, it = [], 0
+        for r in range(6):
+            n = -(-int(nc[r] + stream[r]) // 16)
+            tabs.append(perm[it:it + n]); it += n
+        wl = Workload(name="edge", config=0, seed=77, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      page_size=16, dtype="bf16", token_budget=64, max_chunk=0,
+                      num_pool_pages=pool, num_computed=nc, num_prompt_left=left,
+                      block_tables=tabs, stream_len=stream)
+        res, _, _ = run_and_check(ctx, oracle, wl, label=f"edge-{hq}/{hkv}/{d}")
+        # same data on a different page placement: bit-identical outputs
+        perm2 = np.random.default_rng(10).permutation(pool).astype(np.int32)
+        tabs2, it = [], 0
+        for r in range(6):
+            tabs2.append(perm2[it:it + len(tabs[r])]); it += len(tabs[r])
+        wl2 = Workload(**{**wl.__dict__, "block_tables": tabs2})
+        res2, _, _ = run_and_check(ctx, oracle, wl2, label=f"edge-perm-{hq}/{hkv}/{d}")
+        assert np.array_equal(res[0][1], res2[0][1]) and np.array_equal(res[0][2], res2[0][2])
+
+
+def test_empty_step_is_noop(env):
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    ctx, _ = env
+    plan = ca.plan_batch([], [], [], 16, 0, 16, 8)
+    assert plan.num_tokens == 0
+    desc = ca.make_desc(2, 2, 64, 16, "bf16")
+    kc = torch.zeros((8, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros((8, 2, 64, 16), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((1, 2, 64), dtype=torch.bfloat16, device="cuda")
+    ctx.append_kv_rope(desc, plan, x, x, x[:, :2], x[:, :2], kc, vc, 8)
+    ctx.mixed_attention(desc, plan, x, kc, vc, 8, x)
+    torch.cuda.synchronize()
