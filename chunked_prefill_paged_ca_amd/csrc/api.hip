@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -115,13 +116,35 @@ struct Staging {
 
 }  // namespace
 
+// Work lists of one attention call, built on the host from the plan (decode splits, merges).
+struct WorkKey {
+    uint64_t generation = 0;
+    int32_t hq = 0, hkv = 0, d = 0, split = 0;
+    bool operator==(const WorkKey& o) const {
+        return generation == o.generation && hq == o.hq && hkv == o.hkv && d == o.d && split == o.split;
+    }
+};
+
+struct DevWork {
+    const int4* dec_items = nullptr;
+    const int32_t* dec_out = nullptr;
+    const int4* merges = nullptr;
+    int32_t num_dec_items = 0, num_merges = 0, num_slots = 0;
+};
+
 struct ca_ctx {
     int device = 0;
     Staging staging;
     DevBuf plan_buf;        // int32: qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices
     uint64_t plan_generation = 0;
     DevPlan dplan{};
-    DevBuf partial_buf;     // fp32 split-KV partials
+    DevBuf partial_buf;     // fp32 split-KV partials of the generic path
+    DevBuf work_buf;        // decode items | item outputs | merges
+    WorkKey work_key{};
+    DevWork dwork{};
+    DevBuf dec_acc_buf;     // fp32 [slots][G][d]
+    DevBuf dec_ml_buf;      // float2 [slots][G]
+    int32_t split_override = 0;  // CA_DECODE_SPLIT (keys per decode split), 0 = automatic
 };
 
 namespace {
@@ -272,6 +295,83 @@ ca_status upload_plan(ca_ctx* ctx, const ca_plan* plan, int64_t pool, hipStream_
     return CA_OK;
 }
 
+// Keys per decode split: enough work items to cover every CU several times over, in whole
+// 32-key blocks, and long enough that the partial (G x (d + 2) floats) stays a few percent of
+// the K/V bytes the split reads.
+int32_t decode_split_keys(const ca_plan* plan, const Shape& sh, int32_t override_keys) {
+    if (override_keys > 0) return ((override_keys + 31) / 32) * 32;
+    int64_t total = 0;
+    for (int32_t s = 0; s < plan->num_decodes; ++s) {
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        total += static_cast<int64_t>(np - 1) * plan->page_size + plan->kv_last_page_len[s];
+    }
+    total *= sh.hkv;
+    const int64_t target_items = 6144;
+    int64_t L = (total + target_items - 1) / target_items;
+    L = ((L + 31) / 32) * 32;
+    if (L < 256) L = 256;
+    if (L > 4096) L = 4096;
+    return static_cast<int32_t>(L);
+}
+
+// Build (or reuse) the decode work list of this plan and shape and copy it to the device.
+ca_status prepare_decode_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh,
+                              hipStream_t stream) {
+    WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d, decode_split_keys(plan, sh, ctx->split_override)};
+    if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
+    const int32_t L = key.split;
+    std::vector<int4> items;
+    std::vector<int32_t> outs;
+    std::vector<int4> merges;
+    int32_t slots = 0;
+    for (int32_t s = 0; s < plan->num_decodes; ++s) {
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        const int32_t nsplit = (kv_len + L - 1) / L;
+        for (int32_t g = 0; g < sh.hkv; ++g) {
+            if (nsplit == 1) {
+                items.push_back(make_int4(s, g, 0, kv_len));
+                outs.push_back(-1);
+                continue;
+            }
+            merges.push_back(make_int4(s, g, slots, nsplit));
+            for (int32_t i = 0; i < nsplit; ++i) {
+                const int32_t b = i * L, e = (b + L < kv_len) ? b + L : kv_len;
+                items.push_back(make_int4(s, g, b, e));
+                outs.push_back(slots++);
+            }
+        }
+    }
+    const size_t n_items = items.size(), n_merges = merges.size();
+    const size_t out_words = (n_items + 3) / 4 * 4;
+    const size_t bytes = n_items * sizeof(int4) + out_words * sizeof(int32_t) + n_merges * sizeof(int4) + 16;
+    hipError_t e = ctx->work_buf.reserve(bytes, stream);
+    if (e != hipSuccess) return device_error("work list allocation", e);
+    int slot = 0;
+    e = ctx->staging.acquire(bytes, &slot);
+    if (e != hipSuccess) return device_error("staging allocation", e);
+    char* h = static_cast<char*>(ctx->staging.host[slot]);
+    std::memcpy(h, items.data(), n_items * sizeof(int4));
+    std::memcpy(h + n_items * sizeof(int4), outs.data(), n_items * sizeof(int32_t));
+    std::memcpy(h + n_items * sizeof(int4) + out_words * sizeof(int32_t), merges.data(), n_merges * sizeof(int4));
+    e = ctx->staging.copy(slot, ctx->work_buf.ptr, bytes, stream);
+    if (e != hipSuccess) return device_error("work list copy", e);
+    const char* d = static_cast<const char*>(ctx->work_buf.ptr);
+    ctx->dwork.dec_items = reinterpret_cast<const int4*>(d);
+    ctx->dwork.dec_out = reinterpret_cast<const int32_t*>(d + n_items * sizeof(int4));
+    ctx->dwork.merges = reinterpret_cast<const int4*>(d + n_items * sizeof(int4) + out_words * sizeof(int32_t));
+    ctx->dwork.num_dec_items = static_cast<int32_t>(n_items);
+    ctx->dwork.num_merges = static_cast<int32_t>(n_merges);
+    ctx->dwork.num_slots = slots;
+    const int G = sh.hq / sh.hkv;
+    e = ctx->dec_acc_buf.reserve(static_cast<size_t>(slots > 0 ? slots : 1) * G * sh.d * sizeof(float), stream);
+    if (e != hipSuccess) return device_error("decode partial allocation", e);
+    e = ctx->dec_ml_buf.reserve(static_cast<size_t>(slots > 0 ? slots : 1) * G * sizeof(float2), stream);
+    if (e != hipSuccess) return device_error("decode partial allocation", e);
+    ctx->work_key = key;
+    return CA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +388,7 @@ ca_status ca_create(int device, ca_ctx** out) {
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     ca_ctx* ctx = new ca_ctx();
     ctx->device = device;
+    if (const char* env = std::getenv("CA_DECODE_SPLIT")) ctx->split_override = std::atoi(env);
     e = ctx->staging.init();
     if (e != hipSuccess) {
         ctx->staging.release();
@@ -305,6 +406,9 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->staging.release();
     ctx->plan_buf.release();
     ctx->partial_buf.release();
+    ctx->work_buf.release();
+    ctx->dec_acc_buf.release();
+    ctx->dec_ml_buf.release();
     delete ctx;
     return CA_OK;
 }
@@ -359,13 +463,30 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     st = upload_plan(ctx, plan, num_pool_pages, stream);
     if (st != CA_OK) return st;
 
-    const int nsplit = 8;
-    const size_t floats = ca::generic_partial_floats(plan->num_tokens, sh, nsplit);
-    hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
-    if (e != hipSuccess) return device_error("partials allocation", e);
-    e = ca::launch_attention_generic(ctx->dplan, sh, q, k_cache, v_cache, o, lse,
-                                     static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream);
-    if (e != hipSuccess) return device_error("attention launch", e);
+    const int G = sh.hq / sh.hkv;
+    const bool mfma_path = sh.dtype == CA_BF16 && G <= 16;
+    int32_t generic_row0 = 0;
+    if (mfma_path && plan->num_decodes > 0) {
+        st = prepare_decode_work(ctx, plan, sh, stream);
+        if (st != CA_OK) return st;
+        hipError_t e = ca::launch_decode(ctx->dplan, sh, ctx->dwork.dec_items, ctx->dwork.dec_out,
+                                         ctx->dwork.num_dec_items, ctx->dwork.merges,
+                                         ctx->dwork.num_merges, q, k_cache, v_cache,
+                                         static_cast<float*>(ctx->dec_acc_buf.ptr),
+                                         static_cast<float2*>(ctx->dec_ml_buf.ptr),
+                                         o, lse, stream);
+        if (e != hipSuccess) return device_error("decode attention launch", e);
+        generic_row0 = plan->qo_indptr[plan->num_decodes];
+    }
+    if (generic_row0 < plan->num_tokens) {
+        const int nsplit = 8;
+        const size_t floats = ca::generic_partial_floats(plan->num_tokens, sh, nsplit);
+        hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
+        if (e != hipSuccess) return device_error("partials allocation", e);
+        e = ca::launch_attention_generic(ctx->dplan, sh, generic_row0, q, k_cache, v_cache, o, lse,
+                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream);
+        if (e != hipSuccess) return device_error("attention launch", e);
+    }
     return CA_OK;
 }
 

@@ -1,0 +1,236 @@
+// attn_decode.hip -- split-KV paged attention for the decode rows of a mixed step (bf16, MFMA),
+// and the log-sum-exp merge of the splits.
+//
+// What it computes: pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文" --
+// a decode row is the query at position kv_len - 1; it attends to every key 0..kv_len-1 of its
+// request.  Decode is bound by reading the whole history K/V once (magicnetworld.com
+// "分块预填充与 Stall-free 调度", section 三: its arithmetic intensity is capped by the context
+// length), so the kernel is organised around HBM traffic:
+//   * one wavefront per work item (decode row, kv head, key range of a split); the G query heads
+//     sharing the kv head are the columns of one MFMA tile, so each K/V byte is read once for all
+//     of them;
+//   * every K and V fragment is a 16-byte load issued straight from HBM into registers, and the
+//     next 32-key block is requested before the current one is consumed (register double buffer),
+//     so each wave keeps two blocks (16 KB) in flight;
+//   * QK^T and PV run on MFMA only so that the vector ALUs stay free: at G = 8 the fp32 vector
+//     work of a VALU dot product would need most of the chip's non-packed vector rate just to keep
+//     up with 8 TB/s of bf16 K/V.
+// Splits shorter than the whole context write fp32 partials (unnormalised o, running max, sum);
+// a single-split row writes its normalised output directly.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "internal.h"
+#include "mfma.h"
+
+namespace ca {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int D>
+struct Block {
+    bf16x8 k0[D / 32];  // S^T tile 0 A fragments, one per 32-dim k step
+    bf16x8 k1[D / 32];  // S^T tile 1
+    bf16x8 v[D / 16];   // O^T A fragments, one per 16-dim output tile
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(Block<D>& b, const uint16_t* __restrict__ k_cache,
+                                           const uint16_t* __restrict__ v_cache,
+                                           const int32_t* __restrict__ pages, int np, int key0,
+                                           int g, int hkv, int c, int q) {
+    const int lp = key0 >> 4;
+    const int pa = pages[lp];
+    const int pb = (lp + 1 < np) ? pages[lp + 1] : pa;  // a missing second page is never used
+    // S^T rows: tile t row c holds block key 8 (c / 4) + 4 t + c % 4
+    const int kt0 = ((c >> 2) << 3) + (c & 3);
+    const int kt1 = kt0 + 4;
+    const int page0 = (kt0 >> 4) ? pb : pa;
+    const int page1 = (kt1 >> 4) ? pb : pa;
+    const uint16_t* kp0 = k_cache + ((static_cast<int64_t>(page0) * hkv + g) * 16 + (kt0 & 15)) * D + 8 * q;
+    const uint16_t* kp1 = k_cache + ((static_cast<int64_t>(page1) * hkv + g) * 16 + (kt1 & 15)) * D + 8 * q;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        b.k0[kk] = load_frag(kp0 + 32 * kk);
+        b.k1[kk] = load_frag(kp1 + 32 * kk);
+    }
+    // O^T A fragment: dim 16 mt + c, keys 8q .. 8q+7 = page (q / 2), slots 8 (q % 2) ..
+    const int pv = (q >> 1) ? pb : pa;
+    const uint16_t* vp = v_cache + ((static_cast<int64_t>(pv) * hkv + g) * D + c) * 16 + 8 * (q & 1);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) b.v[mt] = load_frag(vp + 16 * 16 * mt);
+}
+
+// item = {seq, kv head, key begin, key end}; out = partial slot (>= 0) or -1 for direct output
+template <int D>
+__global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(
+    DevPlan p, const int4* __restrict__ items, const int32_t* __restrict__ item_out, int num_items,
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
+    float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (item >= num_items) return;
+    const int4 it = items[item];
+    const int s = it.x, g = it.y, kb = it.z, ke = it.w;
+    const int G = hq / hkv;
+    const int c = lane & 15, q = lane >> 4;
+    const int row = p.qo_indptr[s];
+    const int32_t* pages = p.kv_page_indices + p.kv_page_indptr[s];
+    const int np = p.kv_page_indptr[s + 1] - p.kv_page_indptr[s];
+
+    // Q^T fragments: column c is q head g*G + c (zero beyond the group)
+    bf16x8 qf[D / 32];
+    {
+        const uint16_t* qp = qg + (static_cast<int64_t>(row) * hq + g * G + (c < G ? c : 0)) * D + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) qf[kk] = (c < G) ? load_frag(qp + 32 * kk) : zero_frag();
+    }
+
+    floatx4 acc[D / 16];
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.0f;
+
+    // One 32-key block: scores, online-softmax update, PV.  Lane group q holds the scores of
+    // keys key0 + 8q .. key0 + 8q + 7 of query column c.
+    auto consume = [&](const Block<D>& b, int key0) {
+        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            s0 = mfma16x16x32(b.k0[kk], qf[kk], s0);
+            s1 = mfma16x16x32(b.k1[kk], qf[kk], s1);
+        }
+        const int valid = ke - (key0 + 8 * q);  // keys of this lane inside the item
+        float sc[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = (i < valid) ? s0[i] * scale_log2 : -INFINITY;
+            sc[4 + i] = (4 + i < valid) ? s1[i] * scale_log2 : -INFINITY;
+        }
+        float bm = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sc[j]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float m_new = fmaxf(m, bm);  // finite: key0 < ke
+        const float alpha = exp2_fast(m - m_new);
+        float pr[8];
+        float ps = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pr[j] = exp2_fast(sc[j] - m_new);
+            ps += pr[j];
+        }
+        l = l * alpha + ps;
+        m = m_new;
+        const bf16x8 pf = pack_frag(pr);
+        // slots past the item's end may hold stale or non-finite bytes: zero them so that
+        // p = 0 cannot turn into 0 * NaN inside the MFMA
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            acc[mt] = mfma16x16x32(valid < 8 ? mask_frag(b.v[mt], valid) : b.v[mt], pf, acc[mt] * alpha);
+    };
+
+    // Register double buffer: the next block's loads are in flight while a block is consumed.
+    Block<D> ba, bb;
+    load_block<D>(ba, k_cache, v_cache, pages, np, kb, g, hkv, c, q);
+    for (int key0 = kb;;) {
+        if (key0 + 32 < ke) load_block<D>(bb, k_cache, v_cache, pages, np, key0 + 32, g, hkv, c, q);
+        consume(ba, key0);
+        key0 += 32;
+        if (key0 >= ke) break;
+        if (key0 + 32 < ke) load_block<D>(ba, k_cache, v_cache, pages, np, key0 + 32, g, hkv, c, q);
+        consume(bb, key0);
+        key0 += 32;
+        if (key0 >= ke) break;
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+    if (c >= G) return;
+    const int h = g * G + c;
+    const int out = item_out[item];
+    if (out < 0) {
+        const float inv = 1.0f / l;
+        uint16_t* op = o + (static_cast<int64_t>(row) * hq + h) * D + 4 * q;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            const uint32_t lo = f2bf(acc[mt][0] * inv) | (static_cast<uint32_t>(f2bf(acc[mt][1] * inv)) << 16);
+            const uint32_t hi = f2bf(acc[mt][2] * inv) | (static_cast<uint32_t>(f2bf(acc[mt][3] * inv)) << 16);
+            *reinterpret_cast<uint2*>(op + 16 * mt) = make_uint2(lo, hi);
+        }
+        if (lse && q == 0) lse[static_cast<int64_t>(row) * hq + h] = (m + __log2f(l)) * 0.69314718055994531f;
+    } else {
+        float* ap = part_acc + (static_cast<int64_t>(out) * G + c) * D + 4 * q;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            *reinterpret_cast<float4*>(ap + 16 * mt) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+        if (q == 0) part_ml[static_cast<int64_t>(out) * G + c] = make_float2(m, l);
+    }
+}
+
+// One block per (decode sequence, kv head) with more than one split; m is in log2 units.
+// merge = {seq, kv head, first partial slot, count}
+template <int D>
+__global__ void __launch_bounds__(256) merge_kernel(
+    DevPlan p, const int4* __restrict__ merges, const float* __restrict__ part_acc,
+    const float2* __restrict__ part_ml, int hq, int hkv, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
+    const int4 mg = merges[blockIdx.x];
+    const int s = mg.x, g = mg.y, first = mg.z, count = mg.w;
+    const int G = hq / hkv;
+    const int row = p.qo_indptr[s];
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int c = idx / D;
+        const int e = idx - c * D;
+        float mx = -INFINITY;
+        for (int k = 0; k < count; ++k) mx = fmaxf(mx, part_ml[static_cast<int64_t>(first + k) * G + c].x);
+        float L = 0.0f, a = 0.0f;
+        for (int k = 0; k < count; ++k) {
+            const float2 ml = part_ml[static_cast<int64_t>(first + k) * G + c];
+            const float w = exp2_fast(ml.x - mx);
+            L += w * ml.y;
+            a += w * part_acc[(static_cast<int64_t>(first + k) * G + c) * D + e];
+        }
+        const int h = g * G + c;
+        o[(static_cast<int64_t>(row) * hq + h) * D + e] = f2bf(a / L);
+        if (lse && e == 0) lse[static_cast<int64_t>(row) * hq + h] = (mx + __log2f(L)) * 0.69314718055994531f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
+                         const int32_t* item_out, int num_items, const int4* merges,
+                         int num_merges, const void* q, const void* k_cache, const void* v_cache,
+                         float* part_acc, float2* part_ml, void* o, float* lse,
+                         hipStream_t stream) {
+    if (num_items <= 0) return hipSuccess;
+    const float scale_log2 = sh.scale * 1.4426950408889634f;
+    const dim3 grid((num_items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
+    auto qq = static_cast<const uint16_t*>(q);
+    auto kc = static_cast<const uint16_t*>(k_cache);
+    auto vc = static_cast<const uint16_t*>(v_cache);
+    auto oo = static_cast<uint16_t*>(o);
+    if (sh.d == 128) {
+        hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, p, items, item_out,
+                           num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+        if (num_merges > 0)
+            hipLaunchKernelGGL(merge_kernel<128>, dim3(num_merges), dim3(256), 0, stream, p, merges,
+                               part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
+    } else {
+        hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p, items, item_out,
+                           num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+        if (num_merges > 0)
+            hipLaunchKernelGGL(merge_kernel<64>, dim3(num_merges), dim3(256), 0, stream, p, merges,
+                               part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ca

@@ -49,12 +49,12 @@ __device__ __forceinline__ int seq_of_row(const int32_t* qo_indptr, int num_seqs
 template <typename T>
 __global__ void __launch_bounds__(kWave) attn_generic_kernel(
     DevPlan p, const T* __restrict__ q, const T* __restrict__ k_cache,
-    const T* __restrict__ v_cache, int hq, int hkv, int d, float scale, int nsplit,
+    const T* __restrict__ v_cache, int hq, int hkv, int d, float scale, int nsplit, int row0,
     float* __restrict__ partial) {
     __shared__ float s_q[128];
     __shared__ float s_w[kWave];
 
-    const int t = blockIdx.x;
+    const int t = row0 + blockIdx.x;
     const int h = blockIdx.y;
     const int split = blockIdx.z;
     const int lane = threadIdx.x;
@@ -122,9 +122,9 @@ __global__ void __launch_bounds__(kWave) attn_generic_kernel(
 
 template <typename T>
 __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ partial, int hq,
-                                                    int d, int nsplit, T* __restrict__ o,
+                                                    int d, int nsplit, int row0, T* __restrict__ o,
                                                     float* __restrict__ lse) {
-    const int t = blockIdx.x;
+    const int t = row0 + blockIdx.x;
     const int h = blockIdx.y;
     const int e = threadIdx.x;
     const float* base = partial + (static_cast<int64_t>(t) * hq + h) * nsplit * (d + 2);
@@ -152,27 +152,27 @@ size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit) {
     return static_cast<size_t>(num_tokens) * sh.hq * nsplit * (sh.d + 2);
 }
 
-hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, const void* q,
+hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0, const void* q,
                                     const void* k_cache, const void* v_cache, void* o,
                                     float* lse, float* partial, int nsplit,
                                     hipStream_t stream) {
-    if (p.num_tokens <= 0) return hipSuccess;
-    dim3 grid(p.num_tokens, sh.hq, nsplit);
-    dim3 mgrid(p.num_tokens, sh.hq);
+    if (p.num_tokens - row0 <= 0) return hipSuccess;
+    dim3 grid(p.num_tokens - row0, sh.hq, nsplit);
+    dim3 mgrid(p.num_tokens - row0, sh.hq);
     if (sh.dtype == CA_FP32) {
         hipLaunchKernelGGL(attn_generic_kernel<float>, grid, dim3(kWave), 0, stream, p,
                            static_cast<const float*>(q), static_cast<const float*>(k_cache),
                            static_cast<const float*>(v_cache), sh.hq, sh.hkv, sh.d, sh.scale,
-                           nsplit, partial);
+                           nsplit, row0, partial);
         hipLaunchKernelGGL(merge_kernel<float>, mgrid, dim3(sh.d), 0, stream, partial, sh.hq, sh.d,
-                           nsplit, static_cast<float*>(o), lse);
+                           nsplit, row0, static_cast<float*>(o), lse);
     } else {
         hipLaunchKernelGGL(attn_generic_kernel<uint16_t>, grid, dim3(kWave), 0, stream, p,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                            static_cast<const uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, sh.scale,
-                           nsplit, partial);
+                           nsplit, row0, partial);
         hipLaunchKernelGGL(merge_kernel<uint16_t>, mgrid, dim3(sh.d), 0, stream, partial, sh.hq,
-                           sh.d, nsplit, static_cast<uint16_t*>(o), lse);
+                           sh.d, nsplit, row0, static_cast<uint16_t*>(o), lse);
     }
     return hipGetLastError();
 }

@@ -45,11 +45,22 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const void* q_i
 
 // Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
 // partial: fp32 workspace of num_tokens * hq * nsplit * (d + 2) floats.
-hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, const void* q,
+// Rows [row0, num_tokens) only; partial indices are relative to row 0 of the step.
+hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0, const void* q,
                                     const void* k_cache, const void* v_cache, void* o,
                                     float* lse, float* partial, int nsplit,
                                     hipStream_t stream);
 
 size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
+
+// MFMA split-KV decode (bf16, G <= 16).  items[i] = {seq, kv head, key begin, key end};
+// item_out[i] = partial slot or -1 (single split: the output is written directly);
+// merges[j] = {seq, kv head, first partial slot, count} for every multi-split (seq, kv head).
+// part_acc: [slots][G][d] fp32, part_ml: [slots][G] (running max in log2 units, sum).
+hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
+                         const int32_t* item_out, int num_items, const int4* merges,
+                         int num_merges, const void* q, const void* k_cache, const void* v_cache,
+                         float* part_acc, float2* part_ml, void* o, float* lse,
+                         hipStream_t stream);
 
 }  // namespace ca

@@ -1,0 +1,81 @@
+// mfma.h -- gfx950 bf16 MFMA fragments and wave helpers shared by the attention kernels.
+//
+// v_mfma_f32_16x16x32_bf16 (checked on the device): for lane l, with c = l % 16, q = l / 16,
+//   A (16 x 32): row c, k = 8q .. 8q+7      B (32 x 16): column c, k = 8q .. 8q+7
+//   C (16 x 16): column c, rows 4q .. 4q+3
+// The kernels compute S^T = K Q^T (A = 16 keys x 32 dims, B = Q^T) and O^T = V^T P^T
+// (A = 16 dims x 32 keys from a dimension-major V page, B = P^T).  Both A fragments are one
+// contiguous 16-byte load, and in both products the lane's C column is one query column, so
+// the running max / sum of a query column never leaves its lane group.
+//
+// Key order inside a 32-key block: the S^T tile t (t = 0, 1) row r holds key 8 (r / 4) + 4 t +
+// r % 4.  Lane group q then holds the scores of keys 8q .. 8q+7 (tile 0 gives 8q..8q+3, tile 1
+// gives 8q+4..8q+7), which is exactly the k range of its P^T fragment in O^T = V^T P^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ca {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global load of 8 bf16 as an MFMA fragment.
+__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 zero_frag() {
+    const uint4 v = make_uint4(0, 0, 0, 0);
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+// Zero the bf16 elements j of a fragment whose j >= valid (valid in [0, 8]).
+__device__ __forceinline__ bf16x8 mask_frag(bf16x8 f, int valid) {
+    if (valid >= 8) return f;
+    uint4 v;
+    __builtin_memcpy(&v, &f, sizeof(v));
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 2 * i;
+        uint32_t keep = (j < valid ? 0x0000ffffu : 0u) | (j + 1 < valid ? 0xffff0000u : 0u);
+        w[i] &= keep;
+    }
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+    __builtin_memcpy(&f, &v, sizeof(f));
+    return f;
+}
+
+// fp32 -> bf16 (round to nearest even) packed as a fragment of 8.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_frag(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f2bf(x[2 * i])) | (static_cast<uint32_t>(f2bf(x[2 * i + 1])) << 16);
+    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace ca
