@@ -53,6 +53,10 @@ class CaAttnDesc(ctypes.Structure):
                 ("rope_theta", ctypes.c_float)]
 
 
+class CaProfileRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float)]
+
+
 class CaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: status {status} ({status_string(status)}): {detail}")
@@ -79,8 +83,11 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.ca_mixed_attention.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
                                          vp, vp, vp, ctypes.c_int64, vp, vp, vp]
+        L.ca_profile_enable.argtypes = [vp, ctypes.c_int]
+        L.ca_profile_read.argtypes = [vp, ctypes.POINTER(CaProfileRecord), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32)]
         for fn in ("ca_create", "ca_destroy", "ca_plan_batch", "ca_append_kv_rope",
-                   "ca_mixed_attention"):
+                   "ca_mixed_attention", "ca_profile_enable", "ca_profile_read"):
             getattr(L, fn).restype = ctypes.c_int
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
@@ -144,6 +151,39 @@ class Plan:
                 "kv_page_indptr": self.kv_page_indptr[:ns + 1].copy(),
                 "kv_page_indices": self.kv_page_indices[:npg].copy(),
                 "kv_last_page_len": self.kv_last_page_len[:ns].copy()}
+
+
+class RequestBatch:
+    """A ca_request array built once; plan() re-plans it with one library call.
+
+    update(num_computed, num_prompt_left) refreshes the progress fields in place (block tables
+    are fixed at construction).
+    """
+
+    def __init__(self, num_computed, num_prompt_left, block_tables, token_budget: int,
+                 max_chunk: int, page_size: int, num_pool_pages: int):
+        n = len(num_computed)
+        self.n = n
+        self.tables = [np.ascontiguousarray(b, dtype=np.int32) for b in block_tables]
+        self.reqs = (CaRequest * max(n, 1))()
+        for i in range(n):
+            self.reqs[i].num_pages = int(self.tables[i].shape[0])
+            self.reqs[i].block_table = self.tables[i].ctypes.data_as(_i32p) if self.tables[i].size else None
+        self.update(num_computed, num_prompt_left)
+        self.prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), 0,
+                                int(num_pool_pages))
+        self.out = Plan(n, int(sum(t.shape[0] for t in self.tables)))
+
+    def update(self, num_computed, num_prompt_left):
+        for i in range(self.n):
+            self.reqs[i].num_computed = int(num_computed[i])
+            self.reqs[i].num_prompt_left = int(num_prompt_left[i])
+
+    def plan(self) -> "Plan":
+        st = lib().ca_plan_batch(self.reqs, self.n, ctypes.byref(self.prm), ctypes.byref(self.out.c))
+        self.out.status = st
+        _check(st, "ca_plan_batch")
+        return self.out
 
 
 def plan_batch(num_computed: Sequence[int], num_prompt_left: Sequence[int],
@@ -232,6 +272,16 @@ class Context:
             self.close()
         except Exception:
             pass
+
+    def profile_enable(self, enable: bool = True):
+        _check(lib().ca_profile_enable(self.h, 1 if enable else 0), "ca_profile_enable")
+
+    def profile_read(self, cap: int = 65536):
+        """[(kernel name, ms)] of the launches since the last read (waits for their events)."""
+        recs = (CaProfileRecord * max(cap, 1))()
+        n = ctypes.c_int32(0)
+        _check(lib().ca_profile_read(self.h, recs, cap, ctypes.byref(n)), "ca_profile_read")
+        return [(recs[i].kernel.decode(), float(recs[i].ms)) for i in range(n.value)]
 
     def append_kv_rope(self, desc: CaAttnDesc, plan: Plan, q_in, q_out, k_new, v_new, k_cache,
                        v_cache, num_pool_pages: int, stream=None):

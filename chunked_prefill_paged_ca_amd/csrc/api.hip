@@ -116,12 +116,14 @@ struct Staging {
 
 }  // namespace
 
-// Work lists of one attention call, built on the host from the plan (decode splits, merges).
+// Work lists of one attention call, built on the host from the plan: decode splits and their
+// merges, chunk workgroups and their merges.
 struct WorkKey {
     uint64_t generation = 0;
-    int32_t hq = 0, hkv = 0, d = 0, split = 0;
+    int32_t hq = 0, hkv = 0, d = 0, split = 0, csplit = 0;
     bool operator==(const WorkKey& o) const {
-        return generation == o.generation && hq == o.hq && hkv == o.hkv && d == o.d && split == o.split;
+        return generation == o.generation && hq == o.hq && hkv == o.hkv && d == o.d &&
+               split == o.split && csplit == o.csplit;
     }
 };
 
@@ -129,11 +131,69 @@ struct DevWork {
     const int4* dec_items = nullptr;
     const int32_t* dec_out = nullptr;
     const int4* merges = nullptr;
+    const int4* chunk_items = nullptr;   // two int4 per workgroup
+    const int4* chunk_groups = nullptr;  // two int4 per multi-split row block
     int32_t num_dec_items = 0, num_merges = 0, num_slots = 0;
+    int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0, rows_per_wave = 0;
+};
+
+// Event pairs around the library's own launches (ca_profile_enable).
+struct Profiler {
+    struct Rec {
+        const char* name;
+        hipEvent_t a, b;
+    };
+    bool on = false;
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void release() {
+        for (auto& r : pending) {
+            (void)hipEventDestroy(r.a);
+            (void)hipEventDestroy(r.b);
+        }
+        for (auto e : pool) (void)hipEventDestroy(e);
+        pending.clear();
+        pool.clear();
+    }
+};
+
+// Records one launch between two events when profiling is on.
+struct Timed {
+    Profiler& pf;
+    const char* name;
+    hipStream_t stream;
+    hipEvent_t a = nullptr;
+    Timed(Profiler& p, const char* n, hipStream_t s) : pf(p), name(n), stream(s) {
+        if (pf.on && pf.pending.size() < 65536) {
+            a = pf.get();
+            if (a && hipEventRecord(a, stream) != hipSuccess) { pf.pool.push_back(a); a = nullptr; }
+        }
+    }
+    ~Timed() {
+        if (!a) return;
+        hipEvent_t b = pf.get();
+        if (b && hipEventRecord(b, stream) == hipSuccess) {
+            pf.pending.push_back({name, a, b});
+        } else {
+            pf.pool.push_back(a);
+            if (b) pf.pool.push_back(b);
+        }
+    }
 };
 
 struct ca_ctx {
     int device = 0;
+    Profiler prof;
     Staging staging;
     DevBuf plan_buf;        // int32: qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices
     uint64_t plan_generation = 0;
@@ -144,7 +204,10 @@ struct ca_ctx {
     DevWork dwork{};
     DevBuf dec_acc_buf;     // fp32 [slots][G][d]
     DevBuf dec_ml_buf;      // float2 [slots][G]
-    int32_t split_override = 0;  // CA_DECODE_SPLIT (keys per decode split), 0 = automatic
+    DevBuf chk_acc_buf;     // fp32 [slots][cols][d]
+    DevBuf chk_ml_buf;      // float2 [slots][cols]
+    int32_t split_override = 0;   // CA_DECODE_SPLIT (keys per decode split), 0 = automatic
+    int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
 };
 
 namespace {
@@ -314,11 +377,73 @@ int32_t decode_split_keys(const ca_plan* plan, const Shape& sh, int32_t override
     return static_cast<int32_t>(L);
 }
 
-// Build (or reuse) the decode work list of this plan and shape and copy it to the device.
-ca_status prepare_decode_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh,
-                              hipStream_t stream) {
-    WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d, decode_split_keys(plan, sh, ctx->split_override)};
+// Keys per chunk split: a row block whose visible keys exceed this is cut into several
+// workgroups (merged afterwards) so that a step with few chunk rows still covers the CUs.
+int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t rows_per_block,
+                         int32_t override_keys) {
+    if (override_keys > 0) {
+        int32_t longest = 0;
+        for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+            if (kv_len > longest) longest = kv_len;
+        }
+        int32_t L = override_keys > (longest + 63) / 64 ? override_keys : (longest + 63) / 64;
+        return ((L + 31) / 32) * 32;
+    }
+    int64_t work = 0;  // sum over row blocks of visible keys (x kv heads)
+    for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+        const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        for (int32_t rb = 0; rb < q_len; rb += rows_per_block) {
+            const int32_t rows = (q_len - rb < rows_per_block) ? q_len - rb : rows_per_block;
+            work += static_cast<int64_t>(kv_len - q_len + rb + rows) * sh.hkv;
+        }
+    }
+    const int64_t target = 1024;  // workgroups (one per CU at a time; several rounds)
+    int64_t L = (work + target - 1) / target;
+    if (L < 512) L = 512;
+    // the split merge handles at most 64 splits of one row block
+    int32_t longest = 0;
+    for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        if (kv_len > longest) longest = kv_len;
+    }
+    if (L * 64 < longest) L = (longest + 63) / 64;
+    L = ((L + 31) / 32) * 32;
+    return static_cast<int32_t>(L);
+}
+
+// Reorder workgroup records so that consecutive records (same sequence and kv head, hence the
+// same K/V pages) are dispatched to the same XCD: workgroups go round-robin over the 8 XCDs, so
+// record i is placed at grid slot (i % per) * 8 + i / per.  Returns the padded grid size; pad
+// slots are marked with seq = -1.
+template <int N>
+int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
+    const int32_t n = static_cast<int32_t>(in.size()) / N;
+    const int32_t per = (n + 7) / 8;
+    const int32_t grid = per * 8;
+    out.assign(static_cast<size_t>(grid) * N, make_int4(-1, 0, 0, 0));
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t slot = (i % per) * 8 + i / per;
+        for (int k = 0; k < N; ++k) out[static_cast<size_t>(slot) * N + k] = in[static_cast<size_t>(i) * N + k];
+    }
+    return grid;
+}
+
+// Build (or reuse) the work lists of this plan and shape and copy them to the device.
+ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStream_t stream) {
+    const int G = sh.hq / sh.hkv;
+    const int32_t rows_per_wave = 64 / G;
+    const int32_t rows_per_block = rows_per_wave * 4;
+    WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
+                decode_split_keys(plan, sh, ctx->split_override),
+                chunk_split_keys(plan, sh, rows_per_block, ctx->csplit_override)};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
+
+    // decode: one wave per (row, kv head, split of L keys)
     const int32_t L = key.split;
     std::vector<int4> items;
     std::vector<int32_t> outs;
@@ -342,9 +467,45 @@ ca_status prepare_decode_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh,
             }
         }
     }
+
+    // chunks: one workgroup per (sequence, kv head, block of rows, split of Lc keys)
+    const int32_t Lc = key.csplit;
+    std::vector<int4> citems, groups;
+    int32_t cslots = 0;
+    for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+        const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        for (int32_t g = 0; g < sh.hkv; ++g) {
+            for (int32_t rb = 0; rb < q_len; rb += rows_per_block) {
+                const int32_t rows = (q_len - rb < rows_per_block) ? q_len - rb : rows_per_block;
+                const int32_t key_end = kv_len - q_len + rb + rows;  // last row's position + 1
+                const int32_t nsplit = (key_end + Lc - 1) / Lc;
+                if (nsplit == 1) {
+                    citems.push_back(make_int4(s, g, rb, -1));
+                    citems.push_back(make_int4(0, key_end, 0, 0));
+                    continue;
+                }
+                groups.push_back(make_int4(s, g, rb, cslots));
+                groups.push_back(make_int4(nsplit, 0, 0, 0));
+                for (int32_t i = 0; i < nsplit; ++i) {
+                    const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
+                    citems.push_back(make_int4(s, g, rb, cslots++));
+                    citems.push_back(make_int4(b, e, 0, 0));
+                }
+            }
+        }
+    }
+    std::vector<int4> cgrid;
+    const int32_t n_citems = citems.empty() ? 0 : xcd_order<2>(citems, cgrid);
+
     const size_t n_items = items.size(), n_merges = merges.size();
     const size_t out_words = (n_items + 3) / 4 * 4;
-    const size_t bytes = n_items * sizeof(int4) + out_words * sizeof(int32_t) + n_merges * sizeof(int4) + 16;
+    const size_t off_out = n_items * sizeof(int4);
+    const size_t off_merge = off_out + out_words * sizeof(int32_t);
+    const size_t off_citem = off_merge + n_merges * sizeof(int4);
+    const size_t off_group = off_citem + cgrid.size() * sizeof(int4);
+    const size_t bytes = off_group + groups.size() * sizeof(int4) + 16;
     hipError_t e = ctx->work_buf.reserve(bytes, stream);
     if (e != hipSuccess) return device_error("work list allocation", e);
     int slot = 0;
@@ -352,22 +513,33 @@ ca_status prepare_decode_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh,
     if (e != hipSuccess) return device_error("staging allocation", e);
     char* h = static_cast<char*>(ctx->staging.host[slot]);
     std::memcpy(h, items.data(), n_items * sizeof(int4));
-    std::memcpy(h + n_items * sizeof(int4), outs.data(), n_items * sizeof(int32_t));
-    std::memcpy(h + n_items * sizeof(int4) + out_words * sizeof(int32_t), merges.data(), n_merges * sizeof(int4));
+    std::memcpy(h + off_out, outs.data(), n_items * sizeof(int32_t));
+    std::memcpy(h + off_merge, merges.data(), n_merges * sizeof(int4));
+    std::memcpy(h + off_citem, cgrid.data(), cgrid.size() * sizeof(int4));
+    std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
     e = ctx->staging.copy(slot, ctx->work_buf.ptr, bytes, stream);
     if (e != hipSuccess) return device_error("work list copy", e);
     const char* d = static_cast<const char*>(ctx->work_buf.ptr);
-    ctx->dwork.dec_items = reinterpret_cast<const int4*>(d);
-    ctx->dwork.dec_out = reinterpret_cast<const int32_t*>(d + n_items * sizeof(int4));
-    ctx->dwork.merges = reinterpret_cast<const int4*>(d + n_items * sizeof(int4) + out_words * sizeof(int32_t));
-    ctx->dwork.num_dec_items = static_cast<int32_t>(n_items);
-    ctx->dwork.num_merges = static_cast<int32_t>(n_merges);
-    ctx->dwork.num_slots = slots;
-    const int G = sh.hq / sh.hkv;
-    e = ctx->dec_acc_buf.reserve(static_cast<size_t>(slots > 0 ? slots : 1) * G * sh.d * sizeof(float), stream);
-    if (e != hipSuccess) return device_error("decode partial allocation", e);
-    e = ctx->dec_ml_buf.reserve(static_cast<size_t>(slots > 0 ? slots : 1) * G * sizeof(float2), stream);
-    if (e != hipSuccess) return device_error("decode partial allocation", e);
+    DevWork& w = ctx->dwork;
+    w.dec_items = reinterpret_cast<const int4*>(d);
+    w.dec_out = reinterpret_cast<const int32_t*>(d + off_out);
+    w.merges = reinterpret_cast<const int4*>(d + off_merge);
+    w.chunk_items = reinterpret_cast<const int4*>(d + off_citem);
+    w.chunk_groups = reinterpret_cast<const int4*>(d + off_group);
+    w.num_dec_items = static_cast<int32_t>(n_items);
+    w.num_merges = static_cast<int32_t>(n_merges);
+    w.num_slots = slots;
+    w.num_chunk_items = n_citems;
+    w.num_chunk_groups = static_cast<int32_t>(groups.size() / 2);
+    w.num_chunk_slots = cslots;
+    w.rows_per_wave = rows_per_wave;
+    const size_t dslots = static_cast<size_t>(slots > 0 ? slots : 1);
+    e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
+    if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
+    const size_t cslots_sz = static_cast<size_t>(cslots > 0 ? cslots : 1) * ca::chunk_cols_per_block();
+    if (e == hipSuccess) e = ctx->chk_acc_buf.reserve(cslots_sz * sh.d * sizeof(float), stream);
+    if (e == hipSuccess) e = ctx->chk_ml_buf.reserve(cslots_sz * sizeof(float2), stream);
+    if (e != hipSuccess) return device_error("partial allocation", e);
     ctx->work_key = key;
     return CA_OK;
 }
@@ -389,6 +561,7 @@ ca_status ca_create(int device, ca_ctx** out) {
     ca_ctx* ctx = new ca_ctx();
     ctx->device = device;
     if (const char* env = std::getenv("CA_DECODE_SPLIT")) ctx->split_override = std::atoi(env);
+    if (const char* env = std::getenv("CA_CHUNK_SPLIT")) ctx->csplit_override = std::atoi(env);
     e = ctx->staging.init();
     if (e != hipSuccess) {
         ctx->staging.release();
@@ -409,6 +582,9 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->work_buf.release();
     ctx->dec_acc_buf.release();
     ctx->dec_ml_buf.release();
+    ctx->chk_acc_buf.release();
+    ctx->chk_ml_buf.release();
+    ctx->prof.release();
     delete ctx;
     return CA_OK;
 }
@@ -435,8 +611,11 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     st = upload_plan(ctx, plan, num_pool_pages, stream);
     if (st != CA_OK) return st;
-    hipError_t e = ca::launch_append_rope(ctx->dplan, sh, q_in, q_out, k_new, v_new, k_cache,
-                                          v_cache, stream);
+    hipError_t e;
+    {
+        Timed t(ctx->prof, "append_rope", stream);
+        e = ca::launch_append_rope(ctx->dplan, sh, q_in, q_out, k_new, v_new, k_cache, v_cache, stream);
+    }
     if (e != hipSuccess) return device_error("append_rope launch", e);
     return CA_OK;
 }
@@ -464,30 +643,81 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     if (st != CA_OK) return st;
 
     const int G = sh.hq / sh.hkv;
-    const bool mfma_path = sh.dtype == CA_BF16 && G <= 16;
-    int32_t generic_row0 = 0;
-    if (mfma_path && plan->num_decodes > 0) {
-        st = prepare_decode_work(ctx, plan, sh, stream);
+    if (sh.dtype == CA_BF16 && G <= 16) {
+        st = prepare_work(ctx, plan, sh, stream);
         if (st != CA_OK) return st;
-        hipError_t e = ca::launch_decode(ctx->dplan, sh, ctx->dwork.dec_items, ctx->dwork.dec_out,
-                                         ctx->dwork.num_dec_items, ctx->dwork.merges,
-                                         ctx->dwork.num_merges, q, k_cache, v_cache,
-                                         static_cast<float*>(ctx->dec_acc_buf.ptr),
-                                         static_cast<float2*>(ctx->dec_ml_buf.ptr),
-                                         o, lse, stream);
-        if (e != hipSuccess) return device_error("decode attention launch", e);
-        generic_row0 = plan->qo_indptr[plan->num_decodes];
-    }
-    if (generic_row0 < plan->num_tokens) {
-        const int nsplit = 8;
-        const size_t floats = ca::generic_partial_floats(plan->num_tokens, sh, nsplit);
-        hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
-        if (e != hipSuccess) return device_error("partials allocation", e);
-        e = ca::launch_attention_generic(ctx->dplan, sh, generic_row0, q, k_cache, v_cache, o, lse,
-                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream);
+        const DevWork& w = ctx->dwork;
+        float* cacc = static_cast<float*>(ctx->chk_acc_buf.ptr);
+        float2* cml = static_cast<float2*>(ctx->chk_ml_buf.ptr);
+        float* dacc = static_cast<float*>(ctx->dec_acc_buf.ptr);
+        float2* dml = static_cast<float2*>(ctx->dec_ml_buf.ptr);
+        hipError_t e = hipSuccess;
+        // chunk rows first: their workgroups are the long ones, decode splits fill in behind
+        if (w.num_chunk_items > 0) {
+            Timed t(ctx->prof, "chunk", stream);
+            e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, w.rows_per_wave, q,
+                                 k_cache, v_cache, cacc, cml, o, lse, stream);
+        }
+        if (e == hipSuccess && w.num_dec_items > 0) {
+            Timed t(ctx->prof, "decode", stream);
+            e = ca::launch_decode(ctx->dplan, sh, w.dec_items, w.dec_out, w.num_dec_items, q, k_cache,
+                                  v_cache, dacc, dml, o, lse, stream);
+        }
+        if (e == hipSuccess && w.num_chunk_groups > 0) {
+            Timed t(ctx->prof, "chunk_merge", stream);
+            e = ca::launch_chunk_merge(ctx->dplan, sh, w.chunk_groups, w.num_chunk_groups,
+                                       w.rows_per_wave, cacc, cml, o, lse, stream);
+        }
+        if (e == hipSuccess && w.num_merges > 0) {
+            Timed t(ctx->prof, "decode_merge", stream);
+            e = ca::launch_decode_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, o, lse, stream);
+        }
         if (e != hipSuccess) return device_error("attention launch", e);
+        return CA_OK;
     }
+    // fp32 storage, or groups wider than one MFMA tile: the plain kernel serves every row
+    const int nsplit = 8;
+    const size_t floats = ca::generic_partial_floats(plan->num_tokens, sh, nsplit);
+    hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
+    if (e != hipSuccess) return device_error("partials allocation", e);
+    {
+        Timed t(ctx->prof, "generic", stream);
+        e = ca::launch_attention_generic(ctx->dplan, sh, 0, q, k_cache, v_cache, o, lse,
+                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream);
+    }
+    if (e != hipSuccess) return device_error("attention launch", e);
     return CA_OK;
+}
+
+ca_status ca_profile_enable(ca_ctx* ctx, int enable) {
+    ca::clear_error();
+    if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
+    ctx->prof.on = enable != 0;
+    return CA_OK;
+}
+
+ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int32_t* count) {
+    ca::clear_error();
+    if (!ctx || !count || (cap > 0 && !out) || cap < 0) { ca::set_error("ca_profile_read: bad arguments"); return CA_ERR_INVALID_ARG; }
+    DeviceGuard g(ctx->device);
+    int32_t n = 0;
+    ca_status st = CA_OK;
+    for (auto& r : ctx->prof.pending) {
+        if (n < cap) {
+            float ms = 0.0f;
+            hipError_t e = hipEventSynchronize(r.b);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+            if (e != hipSuccess && st == CA_OK) st = device_error("ca_profile_read", e);
+            out[n].kernel = r.name;
+            out[n].ms = ms;
+            ++n;
+        }
+        ctx->prof.pool.push_back(r.a);
+        ctx->prof.pool.push_back(r.b);
+    }
+    ctx->prof.pending.clear();
+    *count = n;
+    return st;
 }
 
 const char* ca_status_string(ca_status s) {

@@ -174,41 +174,59 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(
     }
 }
 
-// One block per (decode sequence, kv head) with more than one split; m is in log2 units.
-// merge = {seq, kv head, first partial slot, count}
+// One wavefront per (multi-split decode sequence, kv head, q head of the group): lane k reads
+// split k's (max, sum), the wave reduces the global max and the weighted sum, then every lane
+// accumulates its output dimensions over the splits (independent loads, unrolled).  m is in
+// log2 units.  merge = {seq, kv head, first partial slot, count}
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(
-    DevPlan p, const int4* __restrict__ merges, const float* __restrict__ part_acc,
+    DevPlan p, const int4* __restrict__ merges, int num_merges, const float* __restrict__ part_acc,
     const float2* __restrict__ part_ml, int hq, int hkv, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-    const int4 mg = merges[blockIdx.x];
-    const int s = mg.x, g = mg.y, first = mg.z, count = mg.w;
     const int G = hq / hkv;
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wid >= num_merges * G) return;
+    const int4 mg = merges[wid / G];
+    const int c = wid - (wid / G) * G;
+    const int s = mg.x, g = mg.y, first = mg.z, count = mg.w;
     const int row = p.qo_indptr[s];
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int c = idx / D;
-        const int e = idx - c * D;
-        float mx = -INFINITY;
-        for (int k = 0; k < count; ++k) mx = fmaxf(mx, part_ml[static_cast<int64_t>(first + k) * G + c].x);
-        float L = 0.0f, a = 0.0f;
-        for (int k = 0; k < count; ++k) {
-            const float2 ml = part_ml[static_cast<int64_t>(first + k) * G + c];
-            const float w = exp2_fast(ml.x - mx);
-            L += w * ml.y;
-            a += w * part_acc[(static_cast<int64_t>(first + k) * G + c) * D + e];
+    float mx = -INFINITY;
+    for (int k = lane; k < count; k += 64) mx = fmaxf(mx, part_ml[static_cast<int64_t>(first + k) * G + c].x);
+#pragma unroll
+    for (int o_ = 32; o_ >= 1; o_ >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o_, 64));
+    float L = 0.0f;
+    float a[D / 64] = {};
+    for (int k0 = 0; k0 < count; k0 += 64) {
+        float wk = 0.0f;
+        if (k0 + lane < count) {
+            const float2 ml = part_ml[static_cast<int64_t>(first + k0 + lane) * G + c];
+            wk = exp2_fast(ml.x - mx);
+            L += wk * ml.y;
         }
-        const int h = g * G + c;
-        o[(static_cast<int64_t>(row) * hq + h) * D + e] = f2bf(a / L);
-        if (lse && e == 0) lse[static_cast<int64_t>(row) * hq + h] = (mx + __log2f(L)) * 0.69314718055994531f;
+        const int n = count - k0 < 64 ? count - k0 : 64;
+        const float* base = part_acc + (static_cast<int64_t>(first + k0) * G + c) * D + lane;
+#pragma unroll 8
+        for (int k = 0; k < n; ++k) {
+            const float wgt = __shfl(wk, k, 64);
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[static_cast<int64_t>(k) * G * D + 64 * e];
+        }
     }
+#pragma unroll
+    for (int o_ = 32; o_ >= 1; o_ >>= 1) L += __shfl_xor(L, o_, 64);
+    const int h = g * G + c;
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) o[(static_cast<int64_t>(row) * hq + h) * D + lane + 64 * e] = f2bf(a[e] * inv);
+    if (lse && lane == 0) lse[static_cast<int64_t>(row) * hq + h] = (mx + __log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* item_out, int num_items, const int4* merges,
-                         int num_merges, const void* q, const void* k_cache, const void* v_cache,
-                         float* part_acc, float2* part_ml, void* o, float* lse,
+                         const int32_t* item_out, int num_items, const void* q, const void* k_cache,
+                         const void* v_cache, float* part_acc, float2* part_ml, void* o, float* lse,
                          hipStream_t stream) {
     if (num_items <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
@@ -217,19 +235,27 @@ hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
     auto kc = static_cast<const uint16_t*>(k_cache);
     auto vc = static_cast<const uint16_t*>(v_cache);
     auto oo = static_cast<uint16_t*>(o);
-    if (sh.d == 128) {
+    if (sh.d == 128)
         hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, p, items, item_out,
                            num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-        if (num_merges > 0)
-            hipLaunchKernelGGL(merge_kernel<128>, dim3(num_merges), dim3(256), 0, stream, p, merges,
-                               part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
-    } else {
+    else
         hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p, items, item_out,
                            num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-        if (num_merges > 0)
-            hipLaunchKernelGGL(merge_kernel<64>, dim3(num_merges), dim3(256), 0, stream, p, merges,
-                               part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
-    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DevPlan& p, const Shape& sh, const int4* merges,
+                               int num_merges, const float* part_acc, const float2* part_ml,
+                               void* o, float* lse, hipStream_t stream) {
+    if (num_merges <= 0) return hipSuccess;
+    auto oo = static_cast<uint16_t*>(o);
+    const dim3 grid((num_merges * (sh.hq / sh.hkv) + 3) / 4);
+    if (sh.d == 128)
+        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, p, merges, num_merges,
+                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
+    else
+        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, p, merges, num_merges,
+                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
     return hipGetLastError();
 }
 

@@ -54,13 +54,29 @@ hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0,
 size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
 
 // MFMA split-KV decode (bf16, G <= 16).  items[i] = {seq, kv head, key begin, key end};
-// item_out[i] = partial slot or -1 (single split: the output is written directly);
-// merges[j] = {seq, kv head, first partial slot, count} for every multi-split (seq, kv head).
+// item_out[i] = partial slot or -1 (single split: the output is written directly).
 // part_acc: [slots][G][d] fp32, part_ml: [slots][G] (running max in log2 units, sum).
 hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* item_out, int num_items, const int4* merges,
-                         int num_merges, const void* q, const void* k_cache, const void* v_cache,
-                         float* part_acc, float2* part_ml, void* o, float* lse,
+                         const int32_t* item_out, int num_items, const void* q, const void* k_cache,
+                         const void* v_cache, float* part_acc, float2* part_ml, void* o, float* lse,
                          hipStream_t stream);
+// merges[j] = {seq, kv head, first partial slot, count} for every multi-split (seq, kv head).
+hipError_t launch_decode_merge(const DevPlan& p, const Shape& sh, const int4* merges,
+                               int num_merges, const float* part_acc, const float2* part_ml,
+                               void* o, float* lse, hipStream_t stream);
 
+}  // namespace ca
+
+namespace ca {
+// MFMA prefill-chunk attention (bf16, G <= 16).  items: two int4 per workgroup,
+// {seq, kv head, first row, partial slot or -1}, {key begin, key end, 0, 0} (seq -1: padding);
+// groups: two int4 per multi-split row block, {seq, kv head, first row, first slot}, {splits}.
+// Partials: [slot][chunk_cols_per_block()][d] fp32 and [slot][cols] (max in log2 units, sum).
+hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
+                        int rows_per_wave, const void* q, const void* k_cache, const void* v_cache,
+                        float* part_acc, float2* part_ml, void* o, float* lse, hipStream_t stream);
+hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* groups, int num_groups,
+                              int rows_per_wave, const float* part_acc, const float2* part_ml,
+                              void* o, float* lse, hipStream_t stream);
+int chunk_cols_per_block();
 }  // namespace ca

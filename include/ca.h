@@ -157,6 +157,23 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
                              const void* q, const void* k_cache, const void* v_cache,
                              int64_t num_pool_pages, void* o, float* lse, void* hip_stream);
 
+/*
+ * Kernel timing (the tracing layer).  When enabled, every kernel the library enqueues is
+ * bracketed by two HIP events recorded on the call's stream, so the figures are device time of
+ * that launch alone.  ca_profile_read waits for the recorded events, copies up to `cap` records
+ * (oldest first), sets *count to the number copied and forgets every record read or not.
+ * Names are static strings: "append_rope", "chunk", "chunk_merge", "decode", "decode_merge" and
+ * "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between
+ * reads; later ones are not recorded.
+ */
+typedef struct {
+    const char* kernel;
+    float ms;
+} ca_profile_record;
+
+ca_status ca_profile_enable(ca_ctx* ctx, int enable);
+ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int32_t* count);
+
 const char* ca_status_string(ca_status s);
 /* Detail message of the calling thread's last failed call ("" if none). */
 const char* ca_last_error(void);

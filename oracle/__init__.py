@@ -175,6 +175,17 @@ class Session:
             self.k[r] = hk.astype(np.float64)
             self.v[r] = hv.astype(np.float64)
 
+    def fork(self) -> "Session":
+        """An independent copy of the session's progress and cache (arrays are never mutated in
+        place by step(), so the per-request arrays can be shared)."""
+        other = Session.__new__(Session)
+        other.wl = self.wl
+        other.num_computed = self.num_computed.copy()
+        other.num_prompt_left = self.num_prompt_left.copy()
+        other.k = dict(self.k)
+        other.v = dict(self.v)
+        return other
+
     def plan(self) -> Dict:
         wl = self.wl
         return plan(self.num_computed, self.num_prompt_left, wl.block_tables, wl.token_budget,

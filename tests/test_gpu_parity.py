@@ -241,3 +241,26 @@ def test_empty_step_is_noop(env):
     ctx.append_kv_rope(desc, plan, x, x, x[:, :2], x[:, :2], kc, vc, 8)
     ctx.mixed_attention(desc, plan, x, kc, vc, 8, x)
     torch.cuda.synchronize()
+
+
+def test_profile_records_every_kernel(env):
+    """The timing layer records one event pair per library launch, with positive durations."""
+    import torch
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, make_config
+    from tests import harness as H
+    ctx, _ = env
+    wl = make_config(2)
+    kc, vc = H.alloc_pool(wl, fill=0.0)
+    plan = H.lib_plan(wl, wl.num_computed, wl.num_prompt_left)
+    q, k, v = StreamCursor(wl).take(plan.arrays()["req_ids"], np.diff(plan.arrays()["qo_indptr"]))
+    ctx.profile_read()
+    ctx.profile_enable(True)
+    H.gpu_step(ctx, wl, plan, q, k, v, kc, vc)
+    torch.cuda.synchronize()
+    ctx.profile_enable(False)
+    recs = ctx.profile_read()
+    names = [n for n, _ in recs]
+    _log(f"[profile] {recs}")
+    assert names[0] == "append_rope" and "decode" in names and "chunk" in names
+    assert all(ms > 0 for _, ms in recs)
+    assert ctx.profile_read() == []
