@@ -389,7 +389,8 @@ int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t rows_per_
             if (kv_len > longest) longest = kv_len;
         }
         int32_t L = override_keys > (longest + 63) / 64 ? override_keys : (longest + 63) / 64;
-        return ((L + 31) / 32) * 32;
+        L = ((L + 31) / 32) * 32;
+        return L < ca::chunk_max_split_keys() ? L : ca::chunk_max_split_keys() / 32 * 32;
     }
     int64_t work = 0;  // sum over row blocks of visible keys (x kv heads)
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
@@ -413,7 +414,8 @@ int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t rows_per_
     }
     if (L * 64 < longest) L = (longest + 63) / 64;
     L = ((L + 31) / 32) * 32;
-    return static_cast<int32_t>(L);
+    const int64_t cap = ca::chunk_max_split_keys() / 32 * 32;
+    return static_cast<int32_t>(L < cap ? L : cap);
 }
 
 // Reorder workgroup records so that consecutive records (same sequence and kv head, hence the

@@ -32,18 +32,16 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTiles = 4;  // 16-column MFMA tiles per wave -> 64 columns
+constexpr int kMaxItemPages = 2048;  // page ids of one workgroup's key range kept in LDS
 
 // 16-byte unit swizzle of K row `key` (block key 0..31): spreads the 16 rows an S^T fragment
 // reads (keys 8a + 4t + b, a, b in 0..3) over 16 distinct units.
 __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
 
 // One stage = K block (32 keys x D, 16-byte units swizzled per key) then V block
-// (2 pages x [d][16 slots]); two stages.
-template <int D>
-struct ChunkSmem {
-    uint16_t blk[2][64 * D];
-};
-
+// (2 pages x [d][16 slots]) = 64 D halves.  The two stages are separate __shared__ objects so
+// the compiler can tell that the DMA filling one never aliases reads of the other (with one
+// array indexed at run time it waits for every DMA before any LDS read).
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     bf16x8 r;
@@ -52,20 +50,16 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
 }
 
 
-// Copy one 32-key block straight from HBM into LDS stage `buf` (16-byte DMA per lane, no
+// Copy one 32-key block straight from HBM into LDS stage `stage` (16-byte DMA per lane, no
 // registers).  The stage holds 8D 16-byte units: K units first (key-major, D/8 per key), then
 // the two V pages.  Wave w, instruction u fills the contiguous units (w*U + u)*64 + lane; the
 // lane picks the global unit that belongs there, which applies the K swizzle on the load side.
 template <int D>
-__device__ __forceinline__ void dma_block(ChunkSmem<D>& sm, int buf, const uint16_t* __restrict__ k_cache,
-                                          const uint16_t* __restrict__ v_cache,
-                                          const int32_t* __restrict__ pages, int np, int key0,
+__device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __restrict__ k_cache,
+                                          const uint16_t* __restrict__ v_cache, int pa, int pb,
                                           int g, int hkv, int w, int lane) {
     constexpr int U = 8 * D / 256;  // instructions per wave
     constexpr int KUNITS = 32 * D / 8;
-    const int lp = key0 >> 4;
-    const int pa = pages[lp];
-    const int pb = (lp + 1 < np) ? pages[lp + 1] : pa;  // a missing page is masked, never used
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int first = (w * U + u) * 64;
@@ -83,7 +77,7 @@ __device__ __forceinline__ void dma_block(ChunkSmem<D>& sm, int buf, const uint1
             const int off = (y >= 2 * D) ? y - 2 * D : y;
             src = v_cache + (static_cast<int64_t>(page) * hkv + g) * 16 * D + 8 * off;
         }
-        __builtin_amdgcn_global_load_lds(src, &sm.blk[buf][8 * first], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
     }
 }
 
@@ -96,7 +90,9 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-    __shared__ ChunkSmem<D> sm;
+    __shared__ __attribute__((aligned(16))) uint16_t stage0[64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t stage1[64 * D];
+    __shared__ int s_pages[kMaxItemPages];  // the item's page ids, so a block's ids are an LDS read
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
@@ -113,21 +109,34 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
     const int q0 = p.qo_indptr[s];
     const int q_len = p.qo_indptr[s + 1] - q0;
     const int pos0 = kv_len - q_len;  // position of the chunk's first row
+    // page ids of the item's key range [kb, ke) plus the page after it (clamped to the sequence)
+    const int lp0 = kb >> 4;
+    const int nlp = min(((ke + 31) >> 4) - lp0, np - lp0);  // <= kMaxItemPages (host-checked)
+    for (int i = tid; i < nlp; i += 64 * kWaves) s_pages[i] = pages[lp0 + i];
+    auto page_pair = [&](int key0, int* pa, int* pb) {
+        const int lp = (key0 >> 4) - lp0;
+        *pa = s_pages[lp];
+        *pb = (lp0 + lp + 1 < np) ? s_pages[lp + 1] : *pa;  // a missing page is masked, never used
+    };
 
     // columns of this wave: tile nt, column c -> (row, head) = (cw / G, cw % G), cw = 16 nt + c
     bf16x8 qf[kTiles][D / 32];
-    int pos[kTiles];
+    int lim[kTiles];     // last key this column may see inside the item (-1: padding column)
+    int wmin = 0x7fffffff;  // smallest lim over the wave's real columns
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
         const int cw = 16 * nt + c;
         const int r = cw / G, j = cw - (cw / G) * G;
         const int row = rb + w * rows_per_wave + r;
         const bool ok = r < rows_per_wave && row < q_len;
-        pos[nt] = ok ? pos0 + row : -1;  // -1: every key masked (padding column)
+        lim[nt] = ok ? min(pos0 + row, ke - 1) : -1;
+        if (ok) wmin = min(wmin, lim[nt]);
         const uint16_t* qp = qg + (static_cast<int64_t>(q0 + (ok ? row : 0)) * hq + g * G + (ok ? j : 0)) * D + 8 * q;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) qf[nt][kk] = ok ? load_frag(qp + 32 * kk) : zero_frag();
     }
+#pragma unroll
+    for (int o_ = 32; o_ >= 1; o_ >>= 1) wmin = min(wmin, __shfl_xor(wmin, o_, 64));
 
     floatx4 acc[kTiles][D / 16];
     float m[kTiles], l[kTiles];
@@ -139,15 +148,9 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
         for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    dma_block<D>(sm, 0, k_cache, v_cache, pages, np, kb, g, hkv, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int buf = 0;
-    for (int key0 = kb; key0 < ke; key0 += 32) {
-        const bool more = key0 + 32 < ke;
-        if (more) dma_block<D>(sm, buf ^ 1, k_cache, v_cache, pages, np, key0 + 32, g, hkv, w, lane);
-
-        // S^T for each column tile; K fragments are read once and reused by all 4 tiles
+    // One 32-key block held in LDS stage `stg`.  Blocks wholly inside every column's visible
+    // range (the common case) skip the causal mask; the mask test is wave-uniform.
+    auto consume = [&](const uint16_t* stg, int key0) {
         floatx4 st[kTiles][2];
 #pragma unroll
         for (int nt = 0; nt < kTiles; ++nt) st[nt][0] = st[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -157,57 +160,89 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
                 const int phys = (4 * kk + q) ^ (kswz(key) & (D / 8 - 1));
-                const bf16x8 kf = lds_frag(&sm.blk[buf][key * D + 8 * phys]);
+                const bf16x8 kf = lds_frag(stg + key * D + 8 * phys);
 #pragma unroll
                 for (int nt = 0; nt < kTiles; ++nt) st[nt][t] = mfma16x16x32(kf, qf[nt][kk], st[nt][t]);
             }
         }
-        // online softmax per column; lane group q holds keys key0 + 8q + (0..7)
+        const bool full = key0 + 31 <= wmin;
         bf16x8 pf[kTiles];
 #pragma unroll
         for (int nt = 0; nt < kTiles; ++nt) {
-            const int lim = pos[nt] < ke - 1 ? pos[nt] : ke - 1;  // last visible key
-            const int valid = lim - (key0 + 8 * q) + 1;
             float sc[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sc[i] = (i < valid) ? st[nt][0][i] * scale_log2 : -INFINITY;
-                sc[4 + i] = (4 + i < valid) ? st[nt][1][i] * scale_log2 : -INFINITY;
+                sc[i] = st[nt][0][i];
+                sc[4 + i] = st[nt][1][i];
+            }
+            if (!full) {
+                const int valid = lim[nt] - (key0 + 8 * q) + 1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sc[j] = (j < valid) ? sc[j] : -INFINITY;
             }
             float bm = sc[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sc[j]);
             bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
             bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            const float m_new = fmaxf(m[nt], bm);
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;  // column with no key yet
-            const float alpha = exp2_fast(m[nt] - m_use);
+            bm *= scale_log2;
+            const bool grow = bm > m[nt] + kRescaleSlack;
+            if (__any(grow)) {
+                const float alpha = grow ? exp2_fast(m[nt] - bm) : 1.0f;
+                l[nt] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] *= alpha;
+                m[nt] = grow ? bm : m[nt];
+            }
+            const float m_use = (m[nt] == -INFINITY) ? 0.0f : m[nt];  // column with no key yet
             float pr[8];
-            float ps = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pr[j] = exp2_fast(sc[j] - m_use);
-                ps += pr[j];
+                pr[j] = exp2_fast(__builtin_fmaf(sc[j], scale_log2, -m_use));
+                l[nt] += pr[j];
             }
-            l[nt] = l[nt] * alpha + ps;
-            m[nt] = m_new;
             pf[nt] = pack_frag(pr);
-#pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] *= alpha;
         }
-        // O^T += V^T P^T; V fragments are read once and reused by all 4 tiles
-        const int vvalid = kv_len - (key0 + 8 * q);  // slots past the sequence end are zeroed
+        // O^T += V^T P^T; V fragments are read once and reused by all 4 tiles.  Slots past the
+        // sequence end are zeroed (a stale or NaN slot must not meet p = 0).
+        const bool vtail = key0 + 32 > kv_len;
+        const int vvalid = kv_len - (key0 + 8 * q);
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
-            bf16x8 vf = lds_frag(&sm.blk[buf][32 * D + (q >> 1) * 16 * D + (16 * mt + c) * 16 + 8 * (q & 1)]);
-            if (vvalid < 8) vf = mask_frag(vf, vvalid);
+            bf16x8 vf = lds_frag(stg + 32 * D + (q >> 1) * 16 * D + (16 * mt + c) * 16 + 8 * (q & 1));
+            if (vtail) vf = mask_frag(vf, vvalid);
 #pragma unroll
             for (int nt = 0; nt < kTiles; ++nt) acc[nt][mt] = mfma16x16x32(vf, pf[nt], acc[nt][mt]);
         }
-        // the DMA into the other stage must have landed before anyone reads it
+    };
+
+    // Two LDS stages, loop unrolled by two so each half names its stage at compile time: the
+    // DMA for block i+1 (into one stage) runs while block i is consumed from the other; one
+    // wait + barrier per block makes the DMA visible and frees the consumed stage.
+    const int nblk = (ke - kb + 31) >> 5;
+    __syncthreads();  // page ids in LDS
+    int pa, pb;
+    page_pair(kb, &pa, &pb);
+    dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int bi = 0; bi < nblk; bi += 2) {
+        const int key0 = kb + 32 * bi;
+        if (bi + 1 < nblk) {
+            page_pair(key0 + 32, &pa, &pb);
+            dma_block<D>(stage1, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+        }
+        consume(stage0, key0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        buf ^= 1;
+        if (bi + 1 >= nblk) break;
+        if (bi + 2 < nblk) {
+            page_pair(key0 + 64, &pa, &pb);
+            dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+        }
+        consume(stage1, key0 + 32);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
 #pragma unroll
@@ -293,6 +328,7 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(
 }  // namespace
 
 int chunk_cols_per_block() { return 64 * kWaves; }
+int chunk_max_split_keys() { return 16 * (kMaxItemPages - 2); }
 
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
                         int rows_per_wave, const void* q, const void* k_cache, const void* v_cache,

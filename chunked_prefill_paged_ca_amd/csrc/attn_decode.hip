@@ -39,12 +39,8 @@ struct Block {
 
 template <int D>
 __device__ __forceinline__ void load_block(Block<D>& b, const uint16_t* __restrict__ k_cache,
-                                           const uint16_t* __restrict__ v_cache,
-                                           const int32_t* __restrict__ pages, int np, int key0,
+                                           const uint16_t* __restrict__ v_cache, int pa, int pb,
                                            int g, int hkv, int c, int q) {
-    const int lp = key0 >> 4;
-    const int pa = pages[lp];
-    const int pb = (lp + 1 < np) ? pages[lp + 1] : pa;  // a missing second page is never used
     // S^T rows: tile t row c holds block key 8 (c / 4) + 4 t + c % 4
     const int kt0 = ((c >> 2) << 3) + (c & 3);
     const int kt1 = kt0 + 4;
@@ -66,14 +62,17 @@ __device__ __forceinline__ void load_block(Block<D>& b, const uint16_t* __restri
 
 // item = {seq, kv head, key begin, key end}; out = partial slot (>= 0) or -1 for direct output
 template <int D>
-__global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(
+__global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
     DevPlan p, const int4* __restrict__ items, const int32_t* __restrict__ item_out, int num_items,
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    // wave-uniform item index: everything derived from it (page ids included) lives in scalar
+    // registers and is read with scalar loads, which do not share the vector-load counter the
+    // K/V prefetch relies on
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     if (item >= num_items) return;
     const int4 it = items[item];
     const int s = it.x, g = it.y, kb = it.z, ke = it.w;
@@ -97,7 +96,8 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(
     float m = -INFINITY, l = 0.0f;
 
     // One 32-key block: scores, online-softmax update, PV.  Lane group q holds the scores of
-    // keys key0 + 8q .. key0 + 8q + 7 of query column c.
+    // keys key0 + 8q .. key0 + 8q + 7 of query column c.  Only an item's last block can run past
+    // its end, so the masks are taken on that block alone (the test is wave-uniform).
     auto consume = [&](const Block<D>& b, int key0) {
         floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -105,49 +105,84 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) decode_kernel(
             s0 = mfma16x16x32(b.k0[kk], qf[kk], s0);
             s1 = mfma16x16x32(b.k1[kk], qf[kk], s1);
         }
+        const bool full = key0 + 32 <= ke;
         const int valid = ke - (key0 + 8 * q);  // keys of this lane inside the item
         float sc[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sc[i] = (i < valid) ? s0[i] * scale_log2 : -INFINITY;
-            sc[4 + i] = (4 + i < valid) ? s1[i] * scale_log2 : -INFINITY;
+            sc[i] = s0[i];
+            sc[4 + i] = s1[i];
+        }
+        if (!full) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sc[j] = (j < valid) ? sc[j] : -INFINITY;
         }
         float bm = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sc[j]);
         bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float m_new = fmaxf(m, bm);  // finite: key0 < ke
-        const float alpha = exp2_fast(m - m_new);
+        bm *= scale_log2;  // finite: key0 < ke
+        const bool grow = bm > m + kRescaleSlack;
+        if (__any(grow)) {
+            const float m_new = grow ? bm : m;
+            const float alpha = exp2_fast(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+            m = m_new;
+        }
         float pr[8];
-        float ps = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            pr[j] = exp2_fast(sc[j] - m_new);
-            ps += pr[j];
+            pr[j] = exp2_fast(__builtin_fmaf(sc[j], scale_log2, -m));
+            l += pr[j];
         }
-        l = l * alpha + ps;
-        m = m_new;
         const bf16x8 pf = pack_frag(pr);
         // slots past the item's end may hold stale or non-finite bytes: zero them so that
         // p = 0 cannot turn into 0 * NaN inside the MFMA
+        if (full) {
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-            acc[mt] = mfma16x16x32(valid < 8 ? mask_frag(b.v[mt], valid) : b.v[mt], pf, acc[mt] * alpha);
+            for (int mt = 0; mt < D / 16; ++mt) acc[mt] = mfma16x16x32(b.v[mt], pf, acc[mt]);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) acc[mt] = mfma16x16x32(mask_frag(b.v[mt], valid), pf, acc[mt]);
+        }
+    };
+
+    // Page ids of a 32-key block (two pages; a page past the sequence end is replaced by the
+    // first one and never used).  They are scalar loads, fetched one block ahead of the K/V
+    // loads that need them.
+    auto pages_of = [&](int key0, int& pa, int& pb) {
+        const int lp = key0 >> 4;
+        pa = pages[lp];
+        pb = (lp + 1 < np) ? pages[lp + 1] : pa;
     };
 
     // Register double buffer: the next block's loads are in flight while a block is consumed.
+    // Inside the loop every prefetch is unconditional (the last block or two are peeled off
+    // below), so the compiler's load counter waits only for the block being consumed.
+    const int nblk = (ke - kb + 31) >> 5;
     Block<D> ba, bb;
-    load_block<D>(ba, k_cache, v_cache, pages, np, kb, g, hkv, c, q);
-    for (int key0 = kb;;) {
-        if (key0 + 32 < ke) load_block<D>(bb, k_cache, v_cache, pages, np, key0 + 32, g, hkv, c, q);
-        consume(ba, key0);
-        key0 += 32;
-        if (key0 >= ke) break;
-        if (key0 + 32 < ke) load_block<D>(ba, k_cache, v_cache, pages, np, key0 + 32, g, hkv, c, q);
-        consume(bb, key0);
-        key0 += 32;
-        if (key0 >= ke) break;
+    int pa, pb;
+    pages_of(kb, pa, pb);
+    load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, c, q);
+    if (nblk > 1) pages_of(kb + 32, pa, pb);
+    int bi = 0;
+    for (; bi + 2 < nblk; bi += 2) {
+        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, c, q);  // block bi + 1
+        pages_of(kb + 32 * (bi + 2), pa, pb);
+        consume(ba, kb + 32 * bi);
+        load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, c, q);  // block bi + 2
+        if (bi + 3 < nblk) pages_of(kb + 32 * (bi + 3), pa, pb);
+        consume(bb, kb + 32 * (bi + 1));
+    }
+    if (bi + 1 < nblk) {
+        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, c, q);
+        consume(ba, kb + 32 * bi);
+        consume(bb, kb + 32 * (bi + 1));
+    } else {
+        consume(ba, kb + 32 * bi);
     }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);

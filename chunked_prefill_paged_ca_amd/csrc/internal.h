@@ -79,4 +79,6 @@ hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* gro
                               int rows_per_wave, const float* part_acc, const float2* part_ml,
                               void* o, float* lse, hipStream_t stream);
 int chunk_cols_per_block();
+// Longest key range one chunk workgroup may cover (its page ids are staged in LDS).
+int chunk_max_split_keys();
 }  // namespace ca

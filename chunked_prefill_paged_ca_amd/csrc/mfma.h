@@ -58,23 +58,26 @@ __device__ __forceinline__ bf16x8 mask_frag(bf16x8 f, int valid) {
     return f;
 }
 
-// fp32 -> bf16 (round to nearest even) packed as a fragment of 8.
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    const __bf16 b = static_cast<__bf16>(f);
+    uint16_t u;
+    __builtin_memcpy(&u, &b, sizeof(u));
+    return u;
 }
 
 __device__ __forceinline__ bf16x8 pack_frag(const float* x) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w[i] = static_cast<uint32_t>(f2bf(x[2 * i])) | (static_cast<uint32_t>(f2bf(x[2 * i + 1])) << 16);
-    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
     bf16x8 r;
-    __builtin_memcpy(&r, &v, sizeof(r));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(x[i]);
     return r;
 }
+
+// Lazy rescaling threshold of the online softmax, in log2 units: the running reference max of a
+// query column only moves when a block's max exceeds it by more than this, so p = 2^(s - m)
+// stays below 2^8 (exact enough in bf16, far from fp32 overflow) and the accumulator rescale
+// is skipped for almost every block after the first.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
