@@ -134,7 +134,7 @@ struct DevWork {
     const int4* chunk_items = nullptr;   // two int4 per workgroup
     const int4* chunk_groups = nullptr;  // two int4 per multi-split row block
     int32_t num_dec_items = 0, num_merges = 0, num_slots = 0;
-    int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0, rows_per_wave = 0;
+    int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0;
 };
 
 // Event pairs around the library's own launches (ca_profile_enable).
@@ -379,8 +379,9 @@ int32_t decode_split_keys(const ca_plan* plan, const Shape& sh, int32_t override
 
 // Keys per chunk split: a row block whose visible keys exceed this is cut into several
 // workgroups (merged afterwards) so that a step with few chunk rows still covers the CUs.
-int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t rows_per_block,
-                         int32_t override_keys) {
+int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t override_keys) {
+    const int32_t G = sh.hq / sh.hkv;
+    const int32_t cols_per_block = ca::chunk_cols_per_block();
     if (override_keys > 0) {
         int32_t longest = 0;
         for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
@@ -392,14 +393,15 @@ int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t rows_per_
         L = ((L + 31) / 32) * 32;
         return L < ca::chunk_max_split_keys() ? L : ca::chunk_max_split_keys() / 32 * 32;
     }
-    int64_t work = 0;  // sum over row blocks of visible keys (x kv heads)
+    int64_t work = 0;  // sum over column blocks of visible keys (x kv heads)
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
         const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
         const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
         const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
-        for (int32_t rb = 0; rb < q_len; rb += rows_per_block) {
-            const int32_t rows = (q_len - rb < rows_per_block) ? q_len - rb : rows_per_block;
-            work += static_cast<int64_t>(kv_len - q_len + rb + rows) * sh.hkv;
+        const int32_t ncols = q_len * G;
+        for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+            const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+            work += static_cast<int64_t>(kv_len - q_len + last / G + 1) * sh.hkv;
         }
     }
     const int64_t target = 1024;  // workgroups (one per CU at a time; several rounds)
@@ -438,11 +440,9 @@ int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
 // Build (or reuse) the work lists of this plan and shape and copy them to the device.
 ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStream_t stream) {
     const int G = sh.hq / sh.hkv;
-    const int32_t rows_per_wave = 64 / G;
-    const int32_t rows_per_block = rows_per_wave * 4;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
                 decode_split_keys(plan, sh, ctx->split_override),
-                chunk_split_keys(plan, sh, rows_per_block, ctx->csplit_override)};
+                chunk_split_keys(plan, sh, ctx->csplit_override)};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
 
     // decode: one wave per (row, kv head, split of L keys)
@@ -470,29 +470,32 @@ ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStr
         }
     }
 
-    // chunks: one workgroup per (sequence, kv head, block of rows, split of Lc keys)
+    // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys); a
+    // column is one (row, q head) pair, numbered row * G + head
     const int32_t Lc = key.csplit;
+    const int32_t cols_per_block = ca::chunk_cols_per_block();
     std::vector<int4> citems, groups;
     int32_t cslots = 0;
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
         const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
         const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
         const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        const int32_t ncols = q_len * G;
         for (int32_t g = 0; g < sh.hkv; ++g) {
-            for (int32_t rb = 0; rb < q_len; rb += rows_per_block) {
-                const int32_t rows = (q_len - rb < rows_per_block) ? q_len - rb : rows_per_block;
-                const int32_t key_end = kv_len - q_len + rb + rows;  // last row's position + 1
+            for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+                const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+                const int32_t key_end = kv_len - q_len + last / G + 1;  // last row's position + 1
                 const int32_t nsplit = (key_end + Lc - 1) / Lc;
                 if (nsplit == 1) {
-                    citems.push_back(make_int4(s, g, rb, -1));
+                    citems.push_back(make_int4(s, g, cb, -1));
                     citems.push_back(make_int4(0, key_end, 0, 0));
                     continue;
                 }
-                groups.push_back(make_int4(s, g, rb, cslots));
+                groups.push_back(make_int4(s, g, cb, cslots));
                 groups.push_back(make_int4(nsplit, 0, 0, 0));
                 for (int32_t i = 0; i < nsplit; ++i) {
                     const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
-                    citems.push_back(make_int4(s, g, rb, cslots++));
+                    citems.push_back(make_int4(s, g, cb, cslots++));
                     citems.push_back(make_int4(b, e, 0, 0));
                 }
             }
@@ -534,7 +537,6 @@ ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStr
     w.num_chunk_items = n_citems;
     w.num_chunk_groups = static_cast<int32_t>(groups.size() / 2);
     w.num_chunk_slots = cslots;
-    w.rows_per_wave = rows_per_wave;
     const size_t dslots = static_cast<size_t>(slots > 0 ? slots : 1);
     e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
     if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
@@ -657,8 +659,8 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         // chunk rows first: their workgroups are the long ones, decode splits fill in behind
         if (w.num_chunk_items > 0) {
             Timed t(ctx->prof, "chunk", stream);
-            e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, w.rows_per_wave, q,
-                                 k_cache, v_cache, cacc, cml, o, lse, stream);
+            e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, q, k_cache,
+                                 v_cache, cacc, cml, o, lse, stream);
         }
         if (e == hipSuccess && w.num_dec_items > 0) {
             Timed t(ctx->prof, "decode", stream);
@@ -667,8 +669,8 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         }
         if (e == hipSuccess && w.num_chunk_groups > 0) {
             Timed t(ctx->prof, "chunk_merge", stream);
-            e = ca::launch_chunk_merge(ctx->dplan, sh, w.chunk_groups, w.num_chunk_groups,
-                                       w.rows_per_wave, cacc, cml, o, lse, stream);
+            e = ca::launch_chunk_merge(ctx->dplan, sh, w.chunk_groups, w.num_chunk_groups, cacc, cml,
+                                       o, lse, stream);
         }
         if (e == hipSuccess && w.num_merges > 0) {
             Timed t(ctx->prof, "decode_merge", stream);

@@ -9,16 +9,18 @@
 // reads are whole 4 KB (page, kv head) runs, coalesced, and shared by every query column of the
 // workgroup through LDS.
 //
-// Work item = (sequence, kv head, block of rows, key range).  A workgroup is 4 wavefronts; each
-// owns 64 query columns, a column being one (row, q head) pair of the kv head's group, so one K/V
-// tile in LDS serves 4 x 64 columns.  Per 32-key block (two pages): the workgroup copies the two
-// K pages and two V pages (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no
-// registers), issued for the next block before the current one is consumed; each wave then runs
-// S^T = K Q^T and O^T = V^T P^T on
+// Work item = (sequence, kv head, block of 256 query columns, key range).  A query column is one
+// (row, q head) pair of the kv head's group, numbered row * G + head, so any group size packs the
+// MFMA tiles without padding.  A workgroup is 8 wavefronts of 32 columns (two waves per SIMD:
+// one wave's softmax overlaps the other's MFMAs), and one K/V tile in LDS serves all 256
+// columns.  Per 32-key block (two pages): the workgroup copies the two K pages and two V pages
+// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), issued for the
+// next block before the current one is consumed; each wave then runs S^T = K Q^T and
+// O^T = V^T P^T on
 // v_mfma_f32_16x16x32_bf16 with an online softmax per column.  K rows in LDS are XOR-swizzled
 // in 16-byte units so that the 16 keys an MFMA fragment reads fall on distinct banks.
 // Only blocks that cross a row's diagonal need the mask; keys past a column's position get
-// weight 0 and slots past the sequence end are zeroed before they reach the MFMA.
+// weight 0, and V slots past the sequence end are zeroed in LDS before they reach the MFMA.
 
 #include <hip/hip_runtime.h>
 
@@ -30,8 +32,9 @@
 namespace ca {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kTiles = 4;  // 16-column MFMA tiles per wave -> 64 columns
+constexpr int kWaves = 8;
+constexpr int kTiles = 2;  // 16-column MFMA tiles per wave -> 32 columns
+constexpr int kCols = 16 * kTiles * kWaves;  // 256 columns per workgroup
 constexpr int kMaxItemPages = 2048;  // page ids of one workgroup's key range kept in LDS
 
 // 16-byte unit swizzle of K row `key` (block key 0..31): spreads the 16 rows an S^T fragment
@@ -42,6 +45,7 @@ __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) &
 // (2 pages x [d][16 slots]) = 64 D halves.  The two stages are separate __shared__ objects so
 // the compiler can tell that the DMA filling one never aliases reads of the other (with one
 // array indexed at run time it waits for every DMA before any LDS read).
+
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     bf16x8 r;
@@ -49,43 +53,46 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
     return r;
 }
 
-
 // Copy one 32-key block straight from HBM into LDS stage `stage` (16-byte DMA per lane, no
 // registers).  The stage holds 8D 16-byte units: K units first (key-major, D/8 per key), then
-// the two V pages.  Wave w, instruction u fills the contiguous units (w*U + u)*64 + lane; the
-// lane picks the global unit that belongs there, which applies the K swizzle on the load side.
+// the two V pages.  Wave w's instruction u fills the contiguous units (w*U + u)*64 + lane; the
+// first half of the waves fetch K (and apply the K swizzle on the load side), the rest V.
 template <int D>
 __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __restrict__ k_cache,
                                           const uint16_t* __restrict__ v_cache, int pa, int pb,
                                           int g, int hkv, int w, int lane) {
-    constexpr int U = 8 * D / 256;  // instructions per wave
+    constexpr int U = 8 * D / (64 * kWaves);  // instructions per wave
     constexpr int KUNITS = 32 * D / 8;
+    if (w < kWaves / 2) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int first = (w * U + u) * 64;
-        const int x = first + lane;
-        const uint16_t* src;
-        if (x < KUNITS) {
+        for (int u = 0; u < U; ++u) {
+            const int first = (w * U + u) * 64;
+            const int x = first + lane;
             const int key = x / (D / 8);
             const int phys = x - key * (D / 8);
             const int unit = phys ^ (kswz(key) & (D / 8 - 1));
             const int page = (key >> 4) ? pb : pa;
-            src = k_cache + ((static_cast<int64_t>(page) * hkv + g) * 16 + (key & 15)) * D + 8 * unit;
-        } else {
-            const int y = x - KUNITS;
+            const uint16_t* src = k_cache + ((static_cast<int64_t>(page) * hkv + g) * 16 + (key & 15)) * D + 8 * unit;
+            __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int first = (w * U + u) * 64;
+            const int y = first - KUNITS + lane;
             const int page = (y >= 2 * D) ? pb : pa;
             const int off = (y >= 2 * D) ? y - 2 * D : y;
-            src = v_cache + (static_cast<int64_t>(page) * hkv + g) * 16 * D + 8 * off;
+            const uint16_t* src = v_cache + (static_cast<int64_t>(page) * hkv + g) * 16 * D + 8 * off;
+            __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
     }
 }
 
-// items: two int4 per item: {seq, kv head, first row of the block, partial slot or -1},
-//                           {key begin, key end, 0, 0}
+// items: two int4 per item: {seq, kv head, first column (row * G + head), partial slot or -1},
+//                           {key begin, key end, 0, 0}   (seq -1: grid padding)
 template <int D>
-__global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
-    DevPlan p, const int4* __restrict__ items, int rows_per_wave,
+__global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
+    DevPlan p, const int4* __restrict__ items,
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
@@ -94,11 +101,12 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t stage1[64 * D];
     __shared__ int s_pages[kMaxItemPages];  // the item's page ids, so a block's ids are an LDS read
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, q = lane >> 4;
     const int4 it0 = items[2 * blockIdx.x];
     const int4 it1 = items[2 * blockIdx.x + 1];
-    const int s = it0.x, g = it0.y, rb = it0.z, slot = it0.w;
+    const int s = it0.x, g = it0.y, cb = it0.z, slot = it0.w;
     const int kb = it1.x, ke = it1.y;
     if (s < 0) return;  // grid padding (uniform across the workgroup)
     const int G = hq / hkv;
@@ -109,6 +117,7 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
     const int q0 = p.qo_indptr[s];
     const int q_len = p.qo_indptr[s + 1] - q0;
     const int pos0 = kv_len - q_len;  // position of the chunk's first row
+    const int ncols = q_len * G;
     // page ids of the item's key range [kb, ke) plus the page after it (clamped to the sequence)
     const int lp0 = kb >> 4;
     const int nlp = min(((ke + 31) >> 4) - lp0, np - lp0);  // <= kMaxItemPages (host-checked)
@@ -119,19 +128,19 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
         *pb = (lp0 + lp + 1 < np) ? s_pages[lp + 1] : *pa;  // a missing page is masked, never used
     };
 
-    // columns of this wave: tile nt, column c -> (row, head) = (cw / G, cw % G), cw = 16 nt + c
+    // this wave's columns: tile nt, lane column c -> column cb + 32 w + 16 nt + c
     bf16x8 qf[kTiles][D / 32];
-    int lim[kTiles];     // last key this column may see inside the item (-1: padding column)
+    int lim[kTiles];        // last key this column may see inside the item (-1: past the chunk)
     int wmin = 0x7fffffff;  // smallest lim over the wave's real columns
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
-        const int cw = 16 * nt + c;
-        const int r = cw / G, j = cw - (cw / G) * G;
-        const int row = rb + w * rows_per_wave + r;
-        const bool ok = r < rows_per_wave && row < q_len;
+        const int col = cb + 32 * w + 16 * nt + c;
+        const bool ok = col < ncols;
+        const int row = ok ? col / G : 0;
+        const int j = ok ? col - row * G : 0;
         lim[nt] = ok ? min(pos0 + row, ke - 1) : -1;
         if (ok) wmin = min(wmin, lim[nt]);
-        const uint16_t* qp = qg + (static_cast<int64_t>(q0 + (ok ? row : 0)) * hq + g * G + (ok ? j : 0)) * D + 8 * q;
+        const uint16_t* qp = qg + (static_cast<int64_t>(q0 + row) * hq + g * G + j) * D + 8 * q;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) qf[nt][kk] = ok ? load_frag(qp + 32 * kk) : zero_frag();
     }
@@ -178,11 +187,11 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
             if (!full) {
                 const int valid = lim[nt] - (key0 + 8 * q) + 1;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sc[j] = (j < valid) ? sc[j] : -INFINITY;
+                for (int jj = 0; jj < 8; ++jj) sc[jj] = (jj < valid) ? sc[jj] : -INFINITY;
             }
             float bm = sc[0];
 #pragma unroll
-            for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sc[j]);
+            for (int jj = 1; jj < 8; ++jj) bm = fmaxf(bm, sc[jj]);
             bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
             bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
             bm *= scale_log2;
@@ -197,23 +206,31 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
             const float m_use = (m[nt] == -INFINITY) ? 0.0f : m[nt];  // column with no key yet
             float pr[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pr[j] = exp2_fast(__builtin_fmaf(sc[j], scale_log2, -m_use));
-                l[nt] += pr[j];
+            for (int jj = 0; jj < 8; ++jj) {
+                pr[jj] = exp2_fast(__builtin_fmaf(sc[jj], scale_log2, -m_use));
+                l[nt] += pr[jj];
             }
             pf[nt] = pack_frag(pr);
         }
-        // O^T += V^T P^T; V fragments are read once and reused by all 4 tiles.  Slots past the
-        // sequence end are zeroed (a stale or NaN slot must not meet p = 0).
-        const bool vtail = key0 + 32 > kv_len;
-        const int vvalid = kv_len - (key0 + 8 * q);
+        // O^T += V^T P^T; V fragments are read once and reused by both tiles
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
-            bf16x8 vf = lds_frag(stg + 32 * D + (q >> 1) * 16 * D + (16 * mt + c) * 16 + 8 * (q & 1));
-            if (vtail) vf = mask_frag(vf, vvalid);
+            const bf16x8 vf = lds_frag(stg + 32 * D + (q >> 1) * 16 * D + (16 * mt + c) * 16 + 8 * (q & 1));
 #pragma unroll
             for (int nt = 0; nt < kTiles; ++nt) acc[nt][mt] = mfma16x16x32(vf, pf[nt], acc[nt][mt]);
         }
+    };
+    // The block holding the sequence's last key may carry stale (even non-finite) bytes in the
+    // slots after it; they get p = 0, and 0 * NaN must not reach the accumulator, so those V
+    // slots are zeroed in LDS once the block has landed (a wave-uniform, once-per-item branch).
+    auto zero_v_tail = [&](uint16_t* stg, int key0) {
+        if (key0 + 32 <= kv_len) return;
+        const int first_bad = kv_len - key0;  // block slots [first_bad, 32) are past the end
+        for (int i = tid; i < 2 * D * 16; i += 64 * kWaves) {
+            const int slot = 16 * (i / (D * 16)) + (i & 15);
+            if (slot >= first_bad) stg[32 * D + i] = 0;
+        }
+        __syncthreads();
     };
 
     // Two LDS stages, loop unrolled by two so each half names its stage at compile time: the
@@ -228,6 +245,7 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
     __syncthreads();
     for (int bi = 0; bi < nblk; bi += 2) {
         const int key0 = kb + 32 * bi;
+        zero_v_tail(stage0, key0);
         if (bi + 1 < nblk) {
             page_pair(key0 + 32, &pa, &pb);
             dma_block<D>(stage1, k_cache, v_cache, pa, pb, g, hkv, w, lane);
@@ -236,6 +254,7 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (bi + 1 >= nblk) break;
+        zero_v_tail(stage1, key0 + 32);
         if (bi + 2 < nblk) {
             page_pair(key0 + 64, &pa, &pb);
             dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
@@ -250,12 +269,11 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
         float lt = l[nt];
         lt += __shfl_xor(lt, 16, 64);
         lt += __shfl_xor(lt, 32, 64);
-        const int cw = 16 * nt + c;
-        const int r = cw / G, j = cw - (cw / G) * G;
-        const int row = rb + w * rows_per_wave + r;
-        if (!(r < rows_per_wave && row < q_len)) continue;
-        const int h = g * G + j;
-        const int64_t orow = static_cast<int64_t>(q0 + row) * hq + h;
+        const int wc = 32 * w + 16 * nt + c;  // column within the workgroup
+        const int col = cb + wc;
+        if (col >= ncols) continue;
+        const int row = col / G, j = col - (col / G) * G;
+        const int64_t orow = static_cast<int64_t>(q0 + row) * hq + g * G + j;
         if (slot < 0) {
             const float inv = 1.0f / lt;
             uint16_t* op = o + orow * D + 4 * q;
@@ -267,42 +285,40 @@ __global__ void __launch_bounds__(64 * kWaves) chunk_kernel(
             }
             if (lse && q == 0) lse[orow] = (m[nt] + __log2f(lt)) * 0.69314718055994531f;
         } else {
-            const int64_t col = static_cast<int64_t>(slot) * (64 * kWaves) + 64 * w + cw;
-            float* ap = part_acc + col * D + 4 * q;
+            const int64_t pc = static_cast<int64_t>(slot) * kCols + wc;
+            float* ap = part_acc + pc * D + 4 * q;
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt)
                 *reinterpret_cast<float4*>(ap + 16 * mt) = make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
-            if (q == 0) part_ml[col] = make_float2(m[nt], lt);
+            if (q == 0) part_ml[pc] = make_float2(m[nt], lt);
         }
     }
 }
 
-// One wavefront per (row block, column): combine the column's key splits.  A split that saw
-// no key of the column has l = 0 and is skipped.  groups: two int4 per row block,
-// {seq, kv head, first row of the block, first slot}, {number of splits, 0, 0, 0}.
+// One wavefront per (column block, column): combine the column's key splits.  A split that saw
+// no key of the column has l = 0 and is skipped.  groups: two int4 per column block,
+// {seq, kv head, first column, first slot}, {number of splits (<= 64), 0, 0, 0}.
 template <int D>
 __global__ void __launch_bounds__(256) chunk_merge_kernel(
-    DevPlan p, const int4* __restrict__ groups, int num_groups, int rows_per_wave,
-    const float* __restrict__ part_acc, const float2* __restrict__ part_ml, int hq, int hkv,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
-    constexpr int COLS = 64 * kWaves;
+    DevPlan p, const int4* __restrict__ groups, int num_groups, const float* __restrict__ part_acc,
+    const float2* __restrict__ part_ml, int hq, int hkv, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= num_groups * COLS) return;
-    const int grp = wid / COLS, col = wid - grp * COLS;
+    if (wid >= num_groups * kCols) return;
+    const int grp = wid / kCols, wc = wid - grp * kCols;
     const int4 g0 = groups[2 * grp];
     const int nsplit = groups[2 * grp + 1].x;
-    const int s = g0.x, g = g0.y, rb = g0.z, first = g0.w;
+    const int s = g0.x, g = g0.y, cb = g0.z, first = g0.w;
     const int G = hq / hkv;
     const int q0 = p.qo_indptr[s];
     const int q_len = p.qo_indptr[s + 1] - q0;
     const int lane = threadIdx.x & 63;
-    const int w = col >> 6, cw = col & 63;
-    const int r = cw / G, j = cw - (cw / G) * G;
-    const int row = rb + w * rows_per_wave + r;
-    if (!(r < rows_per_wave && row < q_len)) return;
-    // lane k holds split k's (max, sum); splits never exceed 64 here (checked on the host)
+    const int col = cb + wc;
+    if (col >= q_len * G) return;
+    const int row = col / G, j = col - (col / G) * G;
+    // lane k holds split k's (max, sum)
     float2 ml = make_float2(-INFINITY, 0.0f);
-    if (lane < nsplit) ml = part_ml[static_cast<int64_t>(first + lane) * COLS + col];
+    if (lane < nsplit) ml = part_ml[static_cast<int64_t>(first + lane) * kCols + wc];
     float mx = ml.y > 0.0f ? ml.x : -INFINITY;
 #pragma unroll
     for (int o_ = 32; o_ >= 1; o_ >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o_, 64));
@@ -311,12 +327,12 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(
 #pragma unroll
     for (int o_ = 32; o_ >= 1; o_ >>= 1) L += __shfl_xor(L, o_, 64);
     float a[D / 64] = {};
-    const float* base = part_acc + (static_cast<int64_t>(first) * COLS + col) * D + lane;
+    const float* base = part_acc + (static_cast<int64_t>(first) * kCols + wc) * D + lane;
 #pragma unroll 4
     for (int k = 0; k < nsplit; ++k) {
         const float wgt = __shfl(wk, k, 64);
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[static_cast<int64_t>(k) * COLS * D + 64 * e];
+        for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[static_cast<int64_t>(k) * kCols * D + 64 * e];
     }
     const int64_t orow = static_cast<int64_t>(q0 + row) * hq + g * G + j;
     const float inv = 1.0f / L;
@@ -327,12 +343,12 @@ __global__ void __launch_bounds__(256) chunk_merge_kernel(
 
 }  // namespace
 
-int chunk_cols_per_block() { return 64 * kWaves; }
+int chunk_cols_per_block() { return kCols; }
 int chunk_max_split_keys() { return 16 * (kMaxItemPages - 2); }
 
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
-                        int rows_per_wave, const void* q, const void* k_cache, const void* v_cache,
-                        float* part_acc, float2* part_ml, void* o, float* lse, hipStream_t stream) {
+                        const void* q, const void* k_cache, const void* v_cache, float* part_acc,
+                        float2* part_ml, void* o, float* lse, hipStream_t stream) {
     if (num_items <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
     auto qq = static_cast<const uint16_t*>(q);
@@ -341,25 +357,25 @@ hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, in
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
         hipLaunchKernelGGL(chunk_kernel<128>, dim3(num_items), dim3(64 * kWaves), 0, stream, p, items,
-                           rows_per_wave, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+                           qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
     else
         hipLaunchKernelGGL(chunk_kernel<64>, dim3(num_items), dim3(64 * kWaves), 0, stream, p, items,
-                           rows_per_wave, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+                           qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* groups, int num_groups,
-                              int rows_per_wave, const float* part_acc, const float2* part_ml,
-                              void* o, float* lse, hipStream_t stream) {
+                              const float* part_acc, const float2* part_ml, void* o, float* lse,
+                              hipStream_t stream) {
     if (num_groups <= 0) return hipSuccess;
     auto oo = static_cast<uint16_t*>(o);
-    const dim3 grid((num_groups * 64 * kWaves + 3) / 4);
+    const dim3 grid((num_groups * kCols + 3) / 4);
     if (sh.d == 128)
         hipLaunchKernelGGL(chunk_merge_kernel<128>, grid, dim3(256), 0, stream, p, groups, num_groups,
-                           rows_per_wave, part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
+                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
     else
         hipLaunchKernelGGL(chunk_merge_kernel<64>, grid, dim3(256), 0, stream, p, groups, num_groups,
-                           rows_per_wave, part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
+                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
     return hipGetLastError();
 }
 

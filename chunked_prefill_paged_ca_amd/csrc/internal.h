@@ -68,16 +68,18 @@ hipError_t launch_decode_merge(const DevPlan& p, const Shape& sh, const int4* me
 }  // namespace ca
 
 namespace ca {
-// MFMA prefill-chunk attention (bf16, G <= 16).  items: two int4 per workgroup,
-// {seq, kv head, first row, partial slot or -1}, {key begin, key end, 0, 0} (seq -1: padding);
-// groups: two int4 per multi-split row block, {seq, kv head, first row, first slot}, {splits}.
-// Partials: [slot][chunk_cols_per_block()][d] fp32 and [slot][cols] (max in log2 units, sum).
+// MFMA prefill-chunk attention (bf16, G <= 16).  A query column is one (row, q head) pair of a kv
+// head's group, numbered row * G + head.  items: two int4 per workgroup,
+// {seq, kv head, first column, partial slot or -1}, {key begin, key end, 0, 0} (seq -1: padding);
+// groups: two int4 per multi-split column block, {seq, kv head, first column, first slot},
+// {splits}.  Partials: [slot][chunk_cols_per_block()][d] fp32 and [slot][cols] (max in log2
+// units, sum).
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
-                        int rows_per_wave, const void* q, const void* k_cache, const void* v_cache,
-                        float* part_acc, float2* part_ml, void* o, float* lse, hipStream_t stream);
+                        const void* q, const void* k_cache, const void* v_cache, float* part_acc,
+                        float2* part_ml, void* o, float* lse, hipStream_t stream);
 hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* groups, int num_groups,
-                              int rows_per_wave, const float* part_acc, const float2* part_ml,
-                              void* o, float* lse, hipStream_t stream);
+                              const float* part_acc, const float2* part_ml, void* o, float* lse,
+                              hipStream_t stream);
 int chunk_cols_per_block();
 // Longest key range one chunk workgroup may cover (its page ids are staged in LDS).
 int chunk_max_split_keys();
