@@ -14,8 +14,8 @@
 // MFMA tiles without padding.  A workgroup is 8 wavefronts of 32 columns (two waves per SIMD:
 // one wave's softmax overlaps the other's MFMAs), and one K/V tile in LDS serves all 256
 // columns.  Per 32-key block (two pages): the workgroup copies the two K pages and two V pages
-// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), issued for the
-// next block before the current one is consumed; each wave then runs S^T = K Q^T and
+// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), kept three blocks
+// ahead of the block being consumed (four LDS stages); each wave then runs S^T = K Q^T and
 // O^T = V^T P^T on
 // v_mfma_f32_16x16x32_bf16 with an online softmax per column.  K rows in LDS are XOR-swizzled
 // in 16-byte units so that the 16 keys an MFMA fragment reads fall on distinct banks.
@@ -99,6 +99,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
     float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t stage0[64 * D];
     __shared__ __attribute__((aligned(16))) uint16_t stage1[64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t stage2[64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t stage3[64 * D];
     __shared__ int s_pages[kMaxItemPages];  // the item's page ids, so a block's ids are an LDS read
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -189,14 +191,18 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) sc[jj] = (jj < valid) ? sc[jj] : -INFINITY;
             }
-            float bm = sc[0];
+            // Each lane checks its own 8 scores against the column's reference max; only when
+            // some score of the wave exceeds it by more than the slack (the first block, and
+            // rarely after) is the column max formed across the 4 lane groups and the
+            // accumulator rescaled.  The common path needs no cross-lane traffic.
+            float lmax = sc[0];
 #pragma unroll
-            for (int jj = 1; jj < 8; ++jj) bm = fmaxf(bm, sc[jj]);
-            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            bm *= scale_log2;
-            const bool grow = bm > m[nt] + kRescaleSlack;
-            if (__any(grow)) {
+            for (int jj = 1; jj < 8; ++jj) lmax = fmaxf(lmax, sc[jj]);
+            lmax *= scale_log2;
+            if (__any(lmax > m[nt] + kRescaleSlack)) {
+                float bm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                const bool grow = bm > m[nt] + kRescaleSlack;
                 const float alpha = grow ? exp2_fast(m[nt] - bm) : 1.0f;
                 l[nt] *= alpha;
 #pragma unroll
@@ -233,35 +239,58 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
         __syncthreads();
     };
 
-    // Two LDS stages, loop unrolled by two so each half names its stage at compile time: the
-    // DMA for block i+1 (into one stage) runs while block i is consumed from the other; one
-    // wait + barrier per block makes the DMA visible and frees the consumed stage.
+    // Four LDS stages, loop unrolled by four so each step names its stages at compile time:
+    // blocks i+1 .. i+3 are in flight (DMA) while block i is consumed, which covers an L2/MALL
+    // or HBM round trip with three blocks of MFMA work.  Each step waits only for its own block
+    // (the DMA count of the blocks issued after it may stay outstanding), and one barrier both
+    // publishes that block and frees the stage the step is about to refill.
+    constexpr int U = 8 * D / (64 * kWaves);  // DMA instructions per wave per block
     const int nblk = (ke - kb + 31) >> 5;
     __syncthreads();  // page ids in LDS
     int pa, pb;
     page_pair(kb, &pa, &pb);
     dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int bi = 0; bi < nblk; bi += 2) {
+    if (nblk > 1) {
+        page_pair(kb + 32, &pa, &pb);
+        dma_block<D>(stage1, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+    }
+    if (nblk > 2) {
+        page_pair(kb + 64, &pa, &pb);
+        dma_block<D>(stage2, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+    }
+    // Wait until at most `later` blocks' DMAs of this wave are still outstanding, then an
+    // execution barrier.  __syncthreads() would also be a release fence, which makes the
+    // compiler drain every outstanding DMA first; here visibility is already explicit: the
+    // step's own DMA is waited for above, and every LDS read of the stage about to be refilled
+    // has returned (its MFMA consumed it) before a wave can reach the barrier.  The signal
+    // fence keeps the compiler from moving LDS accesses across it.
+    auto wait_block = [&](int later) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt((2 * U) | (0x7 << 4) | (0xf << 8));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(U | (0x7 << 4) | (0xf << 8));
+        else __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto step = [&](uint16_t* cur, uint16_t* refill, int bi) {
         const int key0 = kb + 32 * bi;
-        zero_v_tail(stage0, key0);
-        if (bi + 1 < nblk) {
-            page_pair(key0 + 32, &pa, &pb);
-            dma_block<D>(stage1, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+        const int issued_after = min(2, nblk - 1 - bi);  // blocks bi+1, bi+2 already requested
+        wait_block(issued_after);
+        zero_v_tail(cur, key0);
+        if (bi + 3 < nblk) {
+            page_pair(key0 + 96, &pa, &pb);
+            dma_block<D>(refill, k_cache, v_cache, pa, pb, g, hkv, w, lane);
         }
-        consume(stage0, key0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        consume(cur, key0);
+    };
+    for (int bi = 0; bi < nblk; bi += 4) {
+        step(stage0, stage3, bi);
         if (bi + 1 >= nblk) break;
-        zero_v_tail(stage1, key0 + 32);
-        if (bi + 2 < nblk) {
-            page_pair(key0 + 64, &pa, &pb);
-            dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-        }
-        consume(stage1, key0 + 32);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        step(stage1, stage0, bi + 1);
+        if (bi + 2 >= nblk) break;
+        step(stage2, stage1, bi + 2);
+        if (bi + 3 >= nblk) break;
+        step(stage3, stage2, bi + 3);
     }
 
 #pragma unroll
