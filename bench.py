@@ -122,7 +122,7 @@ def main():
     kern_ms = {k: float(np.mean(v)) for k, v in per.items()}
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
-    attn_ms = sum(kern_ms.get(k, 0.0) for k in ("chunk", "decode", "chunk_merge", "decode_merge", "generic"))
+    attn_ms = sum(kern_ms.get(k, 0.0) for k in ("chunk", "decode", "merge", "generic"))
 
     # dominant kernel: the decode split-KV kernel (HBM-bound); the chunk kernel is MFMA-bound
     dec_ms = kern_ms.get("decode", kern_ms.get("generic", float("nan")))

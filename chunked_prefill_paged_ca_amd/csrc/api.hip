@@ -195,12 +195,10 @@ struct ca_ctx {
     int device = 0;
     Profiler prof;
     Staging staging;
-    DevBuf plan_buf;        // int32: qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices
-    uint64_t plan_generation = 0;
+    DevBuf meta_buf;        // one upload per step: plan metadata, then the work lists
     DevPlan dplan{};
     DevBuf partial_buf;     // fp32 split-KV partials of the generic path
-    DevBuf work_buf;        // decode items | item outputs | merges
-    WorkKey work_key{};
+    WorkKey work_key{};     // what meta_buf holds (generation 0: nothing)
     DevWork dwork{};
     DevBuf dec_acc_buf;     // fp32 [slots][G][d]
     DevBuf dec_ml_buf;      // float2 [slots][G]
@@ -323,41 +321,6 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
     return CA_OK;
 }
 
-// Copy the plan's metadata to the device unless this generation is already there.
-ca_status upload_plan(ca_ctx* ctx, const ca_plan* plan, int64_t pool, hipStream_t stream) {
-    if (plan->generation != 0 && plan->generation == ctx->plan_generation) return CA_OK;
-    ca_status st = validate_plan_arrays(plan, pool);
-    if (st != CA_OK) return st;
-    const int32_t ns = plan->num_seqs;
-    const size_t n_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages;
-    const size_t bytes = n_ints * sizeof(int32_t);
-    hipError_t e = ctx->plan_buf.reserve(bytes, stream);
-    if (e != hipSuccess) return device_error("plan metadata allocation", e);
-    int slot = 0;
-    e = ctx->staging.acquire(bytes, &slot);
-    if (e != hipSuccess) return device_error("staging allocation", e);
-    int32_t* h = static_cast<int32_t*>(ctx->staging.host[slot]);
-    std::memcpy(h, plan->qo_indptr, sizeof(int32_t) * (ns + 1));
-    std::memcpy(h + (ns + 1), plan->kv_page_indptr, sizeof(int32_t) * (ns + 1));
-    std::memcpy(h + 2 * (ns + 1), plan->kv_last_page_len, sizeof(int32_t) * ns);
-    if (plan->num_pages)
-        std::memcpy(h + 2 * (ns + 1) + ns, plan->kv_page_indices, sizeof(int32_t) * plan->num_pages);
-    e = ctx->staging.copy(slot, ctx->plan_buf.ptr, bytes, stream);
-    if (e != hipSuccess) return device_error("plan metadata copy", e);
-    const int32_t* d = static_cast<const int32_t*>(ctx->plan_buf.ptr);
-    ctx->dplan.qo_indptr = d;
-    ctx->dplan.kv_page_indptr = d + (ns + 1);
-    ctx->dplan.kv_last_page_len = d + 2 * (ns + 1);
-    ctx->dplan.kv_page_indices = d + 2 * (ns + 1) + ns;
-    ctx->dplan.num_seqs = ns;
-    ctx->dplan.num_decodes = plan->num_decodes;
-    ctx->dplan.num_tokens = plan->num_tokens;
-    ctx->dplan.num_pages = plan->num_pages;
-    ctx->dplan.page_size = plan->page_size;
-    ctx->plan_generation = plan->generation;
-    return CA_OK;
-}
-
 // Keys per decode split: enough work items to cover every CU several times over, in whole
 // 32-key blocks, and long enough that the partial (G x (d + 2) floats) stays a few percent of
 // the K/V bytes the split reads.
@@ -437,96 +400,128 @@ int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
     return grid;
 }
 
-// Build (or reuse) the work lists of this plan and shape and copy them to the device.
-ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStream_t stream) {
+// Make the plan's metadata and, for the MFMA path, its work lists resident on the device.
+// Everything goes in ONE host->device copy (pinned staging, async on the caller's stream):
+//   [qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices | row_seq | pad to 16 B]
+//   [decode items | item outputs | decode merges | chunk items | chunk merges]
+// keyed by (plan generation, shape, split sizes), so the append and the attention of one step
+// share it and a repeated call with the same plan uploads nothing.
+ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
+                  hipStream_t stream) {
     const int G = sh.hq / sh.hkv;
+    const bool mfma = sh.dtype == CA_BF16 && G <= 16;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
-                decode_split_keys(plan, sh, ctx->split_override),
-                chunk_split_keys(plan, sh, ctx->csplit_override)};
+                mfma ? decode_split_keys(plan, sh, ctx->split_override) : -1,
+                mfma ? chunk_split_keys(plan, sh, ctx->csplit_override) : -1};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
+    ca_status st = validate_plan_arrays(plan, pool);
+    if (st != CA_OK) return st;
 
-    // decode: one wave per (row, kv head, split of L keys)
-    const int32_t L = key.split;
-    std::vector<int4> items;
+    std::vector<int4> items, merges, citems, groups;
     std::vector<int32_t> outs;
-    std::vector<int4> merges;
-    int32_t slots = 0;
-    for (int32_t s = 0; s < plan->num_decodes; ++s) {
-        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
-        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
-        const int32_t nsplit = (kv_len + L - 1) / L;
-        for (int32_t g = 0; g < sh.hkv; ++g) {
-            if (nsplit == 1) {
-                items.push_back(make_int4(s, g, 0, kv_len));
-                outs.push_back(-1);
-                continue;
-            }
-            merges.push_back(make_int4(s, g, slots, nsplit));
-            for (int32_t i = 0; i < nsplit; ++i) {
-                const int32_t b = i * L, e = (b + L < kv_len) ? b + L : kv_len;
-                items.push_back(make_int4(s, g, b, e));
-                outs.push_back(slots++);
-            }
-        }
-    }
-
-    // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys); a
-    // column is one (row, q head) pair, numbered row * G + head
-    const int32_t Lc = key.csplit;
-    const int32_t cols_per_block = ca::chunk_cols_per_block();
-    std::vector<int4> citems, groups;
-    int32_t cslots = 0;
-    for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
-        const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
-        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
-        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
-        const int32_t ncols = q_len * G;
-        for (int32_t g = 0; g < sh.hkv; ++g) {
-            for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
-                const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
-                const int32_t key_end = kv_len - q_len + last / G + 1;  // last row's position + 1
-                const int32_t nsplit = (key_end + Lc - 1) / Lc;
+    int32_t slots = 0, cslots = 0;
+    if (mfma) {
+        // decode: one wave per (row, kv head, split of L keys)
+        const int32_t L = key.split;
+        for (int32_t s = 0; s < plan->num_decodes; ++s) {
+            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+            const int32_t nsplit = (kv_len + L - 1) / L;
+            for (int32_t g = 0; g < sh.hkv; ++g) {
                 if (nsplit == 1) {
-                    citems.push_back(make_int4(s, g, cb, -1));
-                    citems.push_back(make_int4(0, key_end, 0, 0));
+                    items.push_back(make_int4(s, g, 0, kv_len));
+                    outs.push_back(-1);
                     continue;
                 }
-                groups.push_back(make_int4(s, g, cb, cslots));
-                groups.push_back(make_int4(nsplit, 0, 0, 0));
+                merges.push_back(make_int4(s, g, slots, nsplit));
                 for (int32_t i = 0; i < nsplit; ++i) {
-                    const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
-                    citems.push_back(make_int4(s, g, cb, cslots++));
-                    citems.push_back(make_int4(b, e, 0, 0));
+                    const int32_t b = i * L, e = (b + L < kv_len) ? b + L : kv_len;
+                    items.push_back(make_int4(s, g, b, e));
+                    outs.push_back(slots++);
                 }
             }
         }
+        // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys);
+        // a column is one (row, q head) pair, numbered row * G + head
+        const int32_t Lc = key.csplit;
+        const int32_t cols_per_block = ca::chunk_cols_per_block();
+        std::vector<int4> clist;
+        for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+            const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+            const int32_t ncols = q_len * G;
+            for (int32_t g = 0; g < sh.hkv; ++g) {
+                for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+                    const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+                    const int32_t key_end = kv_len - q_len + last / G + 1;  // last row's position + 1
+                    const int32_t nsplit = (key_end + Lc - 1) / Lc;
+                    if (nsplit == 1) {
+                        clist.push_back(make_int4(s, g, cb, -1));
+                        clist.push_back(make_int4(0, key_end, 0, 0));
+                        continue;
+                    }
+                    groups.push_back(make_int4(s, g, cb, cslots));
+                    groups.push_back(make_int4(nsplit, 0, 0, 0));
+                    for (int32_t i = 0; i < nsplit; ++i) {
+                        const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
+                        clist.push_back(make_int4(s, g, cb, cslots++));
+                        clist.push_back(make_int4(b, e, 0, 0));
+                    }
+                }
+            }
+        }
+        if (!clist.empty()) xcd_order<2>(clist, citems);
     }
-    std::vector<int4> cgrid;
-    const int32_t n_citems = citems.empty() ? 0 : xcd_order<2>(citems, cgrid);
 
+    const int32_t ns = plan->num_seqs;
+    const int32_t T = plan->num_tokens;
+    const size_t plan_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages + T;
+    const size_t off_items = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
     const size_t n_items = items.size(), n_merges = merges.size();
     const size_t out_words = (n_items + 3) / 4 * 4;
-    const size_t off_out = n_items * sizeof(int4);
+    const size_t off_out = off_items + n_items * sizeof(int4);
     const size_t off_merge = off_out + out_words * sizeof(int32_t);
     const size_t off_citem = off_merge + n_merges * sizeof(int4);
-    const size_t off_group = off_citem + cgrid.size() * sizeof(int4);
+    const size_t off_group = off_citem + citems.size() * sizeof(int4);
     const size_t bytes = off_group + groups.size() * sizeof(int4) + 16;
-    hipError_t e = ctx->work_buf.reserve(bytes, stream);
-    if (e != hipSuccess) return device_error("work list allocation", e);
+    hipError_t e = ctx->meta_buf.reserve(bytes, stream);
+    if (e != hipSuccess) return device_error("metadata allocation", e);
     int slot = 0;
     e = ctx->staging.acquire(bytes, &slot);
     if (e != hipSuccess) return device_error("staging allocation", e);
     char* h = static_cast<char*>(ctx->staging.host[slot]);
-    std::memcpy(h, items.data(), n_items * sizeof(int4));
+    int32_t* hp = reinterpret_cast<int32_t*>(h);
+    std::memcpy(hp, plan->qo_indptr, sizeof(int32_t) * (ns + 1));
+    std::memcpy(hp + (ns + 1), plan->kv_page_indptr, sizeof(int32_t) * (ns + 1));
+    std::memcpy(hp + 2 * (ns + 1), plan->kv_last_page_len, sizeof(int32_t) * ns);
+    if (plan->num_pages)
+        std::memcpy(hp + 2 * (ns + 1) + ns, plan->kv_page_indices, sizeof(int32_t) * plan->num_pages);
+    int32_t* hrow = hp + 2 * (ns + 1) + ns + plan->num_pages;
+    for (int32_t s = 0; s < ns; ++s)
+        for (int32_t t = plan->qo_indptr[s]; t < plan->qo_indptr[s + 1]; ++t) hrow[t] = s;
+    std::memcpy(h + off_items, items.data(), n_items * sizeof(int4));
     std::memcpy(h + off_out, outs.data(), n_items * sizeof(int32_t));
     std::memcpy(h + off_merge, merges.data(), n_merges * sizeof(int4));
-    std::memcpy(h + off_citem, cgrid.data(), cgrid.size() * sizeof(int4));
+    std::memcpy(h + off_citem, citems.data(), citems.size() * sizeof(int4));
     std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
-    e = ctx->staging.copy(slot, ctx->work_buf.ptr, bytes, stream);
-    if (e != hipSuccess) return device_error("work list copy", e);
-    const char* d = static_cast<const char*>(ctx->work_buf.ptr);
+    e = ctx->staging.copy(slot, ctx->meta_buf.ptr, bytes, stream);
+    if (e != hipSuccess) return device_error("metadata copy", e);
+
+    const char* d = static_cast<const char*>(ctx->meta_buf.ptr);
+    const int32_t* dp = reinterpret_cast<const int32_t*>(d);
+    ctx->dplan.qo_indptr = dp;
+    ctx->dplan.kv_page_indptr = dp + (ns + 1);
+    ctx->dplan.kv_last_page_len = dp + 2 * (ns + 1);
+    ctx->dplan.kv_page_indices = dp + 2 * (ns + 1) + ns;
+    ctx->dplan.row_seq = dp + 2 * (ns + 1) + ns + plan->num_pages;
+    ctx->dplan.num_seqs = ns;
+    ctx->dplan.num_decodes = plan->num_decodes;
+    ctx->dplan.num_tokens = plan->num_tokens;
+    ctx->dplan.num_pages = plan->num_pages;
+    ctx->dplan.page_size = plan->page_size;
     DevWork& w = ctx->dwork;
-    w.dec_items = reinterpret_cast<const int4*>(d);
+    w.dec_items = reinterpret_cast<const int4*>(d + off_items);
     w.dec_out = reinterpret_cast<const int32_t*>(d + off_out);
     w.merges = reinterpret_cast<const int4*>(d + off_merge);
     w.chunk_items = reinterpret_cast<const int4*>(d + off_citem);
@@ -534,16 +529,18 @@ ca_status prepare_work(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, hipStr
     w.num_dec_items = static_cast<int32_t>(n_items);
     w.num_merges = static_cast<int32_t>(n_merges);
     w.num_slots = slots;
-    w.num_chunk_items = n_citems;
+    w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
     w.num_chunk_groups = static_cast<int32_t>(groups.size() / 2);
     w.num_chunk_slots = cslots;
-    const size_t dslots = static_cast<size_t>(slots > 0 ? slots : 1);
-    e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
-    if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
-    const size_t cslots_sz = static_cast<size_t>(cslots > 0 ? cslots : 1) * ca::chunk_cols_per_block();
-    if (e == hipSuccess) e = ctx->chk_acc_buf.reserve(cslots_sz * sh.d * sizeof(float), stream);
-    if (e == hipSuccess) e = ctx->chk_ml_buf.reserve(cslots_sz * sizeof(float2), stream);
-    if (e != hipSuccess) return device_error("partial allocation", e);
+    if (mfma) {
+        const size_t dslots = static_cast<size_t>(slots > 0 ? slots : 1);
+        e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
+        if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
+        const size_t cslots_sz = static_cast<size_t>(cslots > 0 ? cslots : 1) * ca::chunk_cols_per_block();
+        if (e == hipSuccess) e = ctx->chk_acc_buf.reserve(cslots_sz * sh.d * sizeof(float), stream);
+        if (e == hipSuccess) e = ctx->chk_ml_buf.reserve(cslots_sz * sizeof(float2), stream);
+        if (e != hipSuccess) return device_error("partial allocation", e);
+    }
     ctx->work_key = key;
     return CA_OK;
 }
@@ -581,9 +578,8 @@ ca_status ca_destroy(ca_ctx* ctx) {
     if (!ctx) return CA_OK;
     DeviceGuard g(ctx->device);
     ctx->staging.release();
-    ctx->plan_buf.release();
+    ctx->meta_buf.release();
     ctx->partial_buf.release();
-    ctx->work_buf.release();
     ctx->dec_acc_buf.release();
     ctx->dec_ml_buf.release();
     ctx->chk_acc_buf.release();
@@ -613,7 +609,7 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    st = upload_plan(ctx, plan, num_pool_pages, stream);
+    st = prepare(ctx, plan, sh, num_pool_pages, stream);
     if (st != CA_OK) return st;
     hipError_t e;
     {
@@ -643,20 +639,21 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    st = upload_plan(ctx, plan, num_pool_pages, stream);
+    st = prepare(ctx, plan, sh, num_pool_pages, stream);
     if (st != CA_OK) return st;
 
     const int G = sh.hq / sh.hkv;
     if (sh.dtype == CA_BF16 && G <= 16) {
-        st = prepare_work(ctx, plan, sh, stream);
-        if (st != CA_OK) return st;
         const DevWork& w = ctx->dwork;
         float* cacc = static_cast<float*>(ctx->chk_acc_buf.ptr);
         float2* cml = static_cast<float2*>(ctx->chk_ml_buf.ptr);
         float* dacc = static_cast<float*>(ctx->dec_acc_buf.ptr);
         float2* dml = static_cast<float2*>(ctx->dec_ml_buf.ptr);
         hipError_t e = hipSuccess;
-        // chunk rows first: their workgroups are the long ones, decode splits fill in behind
+        // Chunk workgroups first (the long ones), then the decode splits.  Running them on two
+        // streams was measured and rejected: decode waves occupy every CU, the chunk
+        // workgroups (8 waves, 72 KB of LDS) only start where a CU drains completely, and the
+        // fork/join events stalled the host between steps.
         if (w.num_chunk_items > 0) {
             Timed t(ctx->prof, "chunk", stream);
             e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, q, k_cache,
@@ -667,14 +664,10 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
             e = ca::launch_decode(ctx->dplan, sh, w.dec_items, w.dec_out, w.num_dec_items, q, k_cache,
                                   v_cache, dacc, dml, o, lse, stream);
         }
-        if (e == hipSuccess && w.num_chunk_groups > 0) {
-            Timed t(ctx->prof, "chunk_merge", stream);
-            e = ca::launch_chunk_merge(ctx->dplan, sh, w.chunk_groups, w.num_chunk_groups, cacc, cml,
-                                       o, lse, stream);
-        }
-        if (e == hipSuccess && w.num_merges > 0) {
-            Timed t(ctx->prof, "decode_merge", stream);
-            e = ca::launch_decode_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, o, lse, stream);
+        if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
+            Timed t(ctx->prof, "merge", stream);
+            e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
+                                 w.num_chunk_groups, cacc, cml, o, lse, stream);
         }
         if (e != hipSuccess) return device_error("attention launch", e);
         return CA_OK;

@@ -17,16 +17,6 @@
 namespace ca {
 namespace {
 
-// Sequence of flat row t: largest s with qo_indptr[s] <= t (binary search over num_seqs + 1).
-__device__ __forceinline__ int seq_of_row(const int32_t* qo_indptr, int num_seqs, int t) {
-    int lo = 0, hi = num_seqs;  // invariant: qo_indptr[lo] <= t < qo_indptr[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (qo_indptr[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 template <typename T>
 __global__ void __launch_bounds__(256) append_rope_kernel(
     DevPlan p, const T* q_in, T* q_out, const T* __restrict__ k_new,
@@ -37,7 +27,7 @@ __global__ void __launch_bounds__(256) append_rope_kernel(
     __shared__ double s_sin[64];
     const int t = blockIdx.x;
     const int P = p.page_size;
-    const int s = seq_of_row(p.qo_indptr, p.num_seqs, t);
+    const int s = p.row_seq[t];
     const int np = p.kv_page_indptr[s + 1] - p.kv_page_indptr[s];
     const int kv_len = (np - 1) * P + p.kv_last_page_len[s];
     const int q_len = p.qo_indptr[s + 1] - p.qo_indptr[s];

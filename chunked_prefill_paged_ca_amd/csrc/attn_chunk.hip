@@ -1,5 +1,5 @@
 // attn_chunk.hip -- causal paged attention for the prefill-chunk rows of a mixed step (bf16,
-// MFMA, K/V pages staged in LDS), plus the merge of key splits.
+// MFMA, K/V pages staged in LDS).  The merge of key splits is in merge.hip.
 //
 // What it computes: pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文" --
 // the chunk's query at absolute position p attends to keys 0..p of its request: the history pages
@@ -324,52 +324,6 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
     }
 }
 
-// One wavefront per (column block, column): combine the column's key splits.  A split that saw
-// no key of the column has l = 0 and is skipped.  groups: two int4 per column block,
-// {seq, kv head, first column, first slot}, {number of splits (<= 64), 0, 0, 0}.
-template <int D>
-__global__ void __launch_bounds__(256) chunk_merge_kernel(
-    DevPlan p, const int4* __restrict__ groups, int num_groups, const float* __restrict__ part_acc,
-    const float2* __restrict__ part_ml, int hq, int hkv, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= num_groups * kCols) return;
-    const int grp = wid / kCols, wc = wid - grp * kCols;
-    const int4 g0 = groups[2 * grp];
-    const int nsplit = groups[2 * grp + 1].x;
-    const int s = g0.x, g = g0.y, cb = g0.z, first = g0.w;
-    const int G = hq / hkv;
-    const int q0 = p.qo_indptr[s];
-    const int q_len = p.qo_indptr[s + 1] - q0;
-    const int lane = threadIdx.x & 63;
-    const int col = cb + wc;
-    if (col >= q_len * G) return;
-    const int row = col / G, j = col - (col / G) * G;
-    // lane k holds split k's (max, sum)
-    float2 ml = make_float2(-INFINITY, 0.0f);
-    if (lane < nsplit) ml = part_ml[static_cast<int64_t>(first + lane) * kCols + wc];
-    float mx = ml.y > 0.0f ? ml.x : -INFINITY;
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o_, 64));
-    const float wk = ml.y > 0.0f ? exp2_fast(ml.x - mx) : 0.0f;
-    float L = wk * ml.y;
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) L += __shfl_xor(L, o_, 64);
-    float a[D / 64] = {};
-    const float* base = part_acc + (static_cast<int64_t>(first) * kCols + wc) * D + lane;
-#pragma unroll 4
-    for (int k = 0; k < nsplit; ++k) {
-        const float wgt = __shfl(wk, k, 64);
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[static_cast<int64_t>(k) * kCols * D + 64 * e];
-    }
-    const int64_t orow = static_cast<int64_t>(q0 + row) * hq + g * G + j;
-    const float inv = 1.0f / L;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[orow * D + lane + 64 * e] = f2bf(a[e] * inv);
-    if (lse && lane == 0) lse[orow] = (mx + __log2f(L)) * 0.69314718055994531f;
-}
-
 }  // namespace
 
 int chunk_cols_per_block() { return kCols; }
@@ -390,21 +344,6 @@ hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, in
     else
         hipLaunchKernelGGL(chunk_kernel<64>, dim3(num_items), dim3(64 * kWaves), 0, stream, p, items,
                            qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-    return hipGetLastError();
-}
-
-hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* groups, int num_groups,
-                              const float* part_acc, const float2* part_ml, void* o, float* lse,
-                              hipStream_t stream) {
-    if (num_groups <= 0) return hipSuccess;
-    auto oo = static_cast<uint16_t*>(o);
-    const dim3 grid((num_groups * kCols + 3) / 4);
-    if (sh.d == 128)
-        hipLaunchKernelGGL(chunk_merge_kernel<128>, grid, dim3(256), 0, stream, p, groups, num_groups,
-                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
-    else
-        hipLaunchKernelGGL(chunk_merge_kernel<64>, grid, dim3(256), 0, stream, p, groups, num_groups,
-                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
     return hipGetLastError();
 }
 

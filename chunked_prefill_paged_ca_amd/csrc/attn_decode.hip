@@ -1,5 +1,5 @@
-// attn_decode.hip -- split-KV paged attention for the decode rows of a mixed step (bf16, MFMA),
-// and the log-sum-exp merge of the splits.
+// attn_decode.hip -- split-KV paged attention for the decode rows of a mixed step (bf16, MFMA).
+// The log-sum-exp merge of the splits is in merge.hip.
 //
 // What it computes: pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文" --
 // a decode row is the query at position kv_len - 1; it attends to every key 0..kv_len-1 of its
@@ -209,54 +209,6 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
     }
 }
 
-// One wavefront per (multi-split decode sequence, kv head, q head of the group): lane k reads
-// split k's (max, sum), the wave reduces the global max and the weighted sum, then every lane
-// accumulates its output dimensions over the splits (independent loads, unrolled).  m is in
-// log2 units.  merge = {seq, kv head, first partial slot, count}
-template <int D>
-__global__ void __launch_bounds__(256) merge_kernel(
-    DevPlan p, const int4* __restrict__ merges, int num_merges, const float* __restrict__ part_acc,
-    const float2* __restrict__ part_ml, int hq, int hkv, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
-    const int G = hq / hkv;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (wid >= num_merges * G) return;
-    const int4 mg = merges[wid / G];
-    const int c = wid - (wid / G) * G;
-    const int s = mg.x, g = mg.y, first = mg.z, count = mg.w;
-    const int row = p.qo_indptr[s];
-    float mx = -INFINITY;
-    for (int k = lane; k < count; k += 64) mx = fmaxf(mx, part_ml[static_cast<int64_t>(first + k) * G + c].x);
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o_, 64));
-    float L = 0.0f;
-    float a[D / 64] = {};
-    for (int k0 = 0; k0 < count; k0 += 64) {
-        float wk = 0.0f;
-        if (k0 + lane < count) {
-            const float2 ml = part_ml[static_cast<int64_t>(first + k0 + lane) * G + c];
-            wk = exp2_fast(ml.x - mx);
-            L += wk * ml.y;
-        }
-        const int n = count - k0 < 64 ? count - k0 : 64;
-        const float* base = part_acc + (static_cast<int64_t>(first + k0) * G + c) * D + lane;
-#pragma unroll 8
-        for (int k = 0; k < n; ++k) {
-            const float wgt = __shfl(wk, k, 64);
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[static_cast<int64_t>(k) * G * D + 64 * e];
-        }
-    }
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) L += __shfl_xor(L, o_, 64);
-    const int h = g * G + c;
-    const float inv = 1.0f / L;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[(static_cast<int64_t>(row) * hq + h) * D + lane + 64 * e] = f2bf(a[e] * inv);
-    if (lse && lane == 0) lse[static_cast<int64_t>(row) * hq + h] = (mx + __log2f(L)) * 0.69314718055994531f;
-}
-
 }  // namespace
 
 hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
@@ -276,21 +228,6 @@ hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
     else
         hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p, items, item_out,
                            num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_merge(const DevPlan& p, const Shape& sh, const int4* merges,
-                               int num_merges, const float* part_acc, const float2* part_ml,
-                               void* o, float* lse, hipStream_t stream) {
-    if (num_merges <= 0) return hipSuccess;
-    auto oo = static_cast<uint16_t*>(o);
-    const dim3 grid((num_merges * (sh.hq / sh.hkv) + 3) / 4);
-    if (sh.d == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, p, merges, num_merges,
-                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
-    else
-        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, p, merges, num_merges,
-                           part_acc, part_ml, sh.hq, sh.hkv, oo, lse);
     return hipGetLastError();
 }
 

@@ -36,15 +36,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ int seq_of_row(const int32_t* qo_indptr, int num_seqs, int t) {
-    int lo = 0, hi = num_seqs;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (qo_indptr[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 // partial layout: [row][q head][split][d + 2] with (acc[0..d), m, l)
 template <typename T>
 __global__ void __launch_bounds__(kWave) attn_generic_kernel(
@@ -61,7 +52,7 @@ __global__ void __launch_bounds__(kWave) attn_generic_kernel(
     const int P = p.page_size;
     const int g = h / (hq / hkv);
 
-    const int s = seq_of_row(p.qo_indptr, p.num_seqs, t);
+    const int s = p.row_seq[t];
     const int page0 = p.kv_page_indptr[s];
     const int np = p.kv_page_indptr[s + 1] - page0;
     const int kv_len = (np - 1) * P + p.kv_last_page_len[s];

@@ -24,6 +24,7 @@ struct DevPlan {
     const int32_t* kv_page_indptr;
     const int32_t* kv_page_indices;
     const int32_t* kv_last_page_len;
+    const int32_t* row_seq;  // [num_tokens] sequence of each flat row (qo_indptr expanded)
     int32_t num_seqs;
     int32_t num_decodes;
     int32_t num_tokens;
@@ -60,10 +61,6 @@ hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
                          const int32_t* item_out, int num_items, const void* q, const void* k_cache,
                          const void* v_cache, float* part_acc, float2* part_ml, void* o, float* lse,
                          hipStream_t stream);
-// merges[j] = {seq, kv head, first partial slot, count} for every multi-split (seq, kv head).
-hipError_t launch_decode_merge(const DevPlan& p, const Shape& sh, const int4* merges,
-                               int num_merges, const float* part_acc, const float2* part_ml,
-                               void* o, float* lse, hipStream_t stream);
 
 }  // namespace ca
 
@@ -77,10 +74,16 @@ namespace ca {
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
                         const void* q, const void* k_cache, const void* v_cache, float* part_acc,
                         float2* part_ml, void* o, float* lse, hipStream_t stream);
-hipError_t launch_chunk_merge(const DevPlan& p, const Shape& sh, const int4* groups, int num_groups,
-                              const float* part_acc, const float2* part_ml, void* o, float* lse,
-                              hipStream_t stream);
 int chunk_cols_per_block();
+
+// One launch combining every split: decode merges[j] = {seq, kv head, first slot, count}
+// (partials [slot][G][d]); chunk groups: two int4 {seq, kv head, first column, first slot},
+// {splits, 0, 0, 0} (partials [slot][chunk_cols_per_block()][d]).  Running maxima are in log2
+// units.  One wavefront per output (row, q head).
+hipError_t launch_merge(const DevPlan& p, const Shape& sh, const int4* dec_merges, int num_dec,
+                        const float* dec_acc, const float2* dec_ml, const int4* chunk_groups,
+                        int num_chunk, const float* chunk_acc, const float2* chunk_ml, void* o,
+                        float* lse, hipStream_t stream);
 // Longest key range one chunk workgroup may cover (its page ids are staged in LDS).
 int chunk_max_split_keys();
 }  // namespace ca

@@ -162,8 +162,8 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
  * bracketed by two HIP events recorded on the call's stream, so the figures are device time of
  * that launch alone.  ca_profile_read waits for the recorded events, copies up to `cap` records
  * (oldest first), sets *count to the number copied and forgets every record read or not.
- * Names are static strings: "append_rope", "chunk", "chunk_merge", "decode", "decode_merge" and
- * "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between
+ * Names are static strings: "append_rope", "chunk", "decode", "merge" (both kinds of split
+ * merge in one launch) and "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between
  * reads; later ones are not recorded.
  */
 typedef struct {
