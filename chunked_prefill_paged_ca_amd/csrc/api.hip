@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -58,58 +59,96 @@ struct DevBuf {
     }
 };
 
-// Ring of pinned host staging slots.  A slot is reused only after the copy that read it has
-// completed (its event), so the host never overwrites bytes an async copy still needs.
+// Copies the staged metadata into device memory.  The staging slots are pinned, device-mapped,
+// coherent host memory, so a kernel can read them directly: the upload then runs on the compute
+// queue in stream order, with no copy-engine hand-off between it and the kernels that read it.
+__global__ void __launch_bounds__(256) upload_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] = src[i];
+}
+
+// Ring of pinned host staging slots.  A slot is reused only after the upload that read it has
+// completed, so the host never overwrites bytes the device still needs.  Completion is tracked
+// per group of kGroup consecutive slots with one event recorded after the group's last upload:
+// an event is a marker in the stream that delays the next kernel by a few microseconds, so one
+// per group rather than one per step.  Before the first slot of a group is refilled, the
+// group's event (recorded a full ring earlier) is waited for.
 struct Staging {
-    static constexpr int kSlots = 4;
+    static constexpr int kSlots = 8;
+    static constexpr int kGroup = 4;
     void* host[kSlots] = {};
+    void* dev[kSlots] = {};  // the same memory as the device addresses it
     size_t cap[kSlots] = {};
-    hipEvent_t ev[kSlots] = {};
-    bool pending[kSlots] = {};
+    hipEvent_t ev[kSlots / kGroup] = {};
+    bool pending[kSlots / kGroup] = {};
     int next = 0;
 
     hipError_t init() {
-        for (int i = 0; i < kSlots; ++i) {
+        for (int i = 0; i < kSlots / kGroup; ++i) {
             hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
     hipError_t acquire(size_t bytes, int* slot) {
-        int i = next;
+        const int i = next;
         next = (next + 1) % kSlots;
-        if (pending[i]) {
-            hipError_t e = hipEventSynchronize(ev[i]);
+        const int g = i / kGroup;
+        if (i % kGroup == 0 && pending[g]) {
+            hipError_t e = hipEventSynchronize(ev[g]);
             if (e != hipSuccess) return e;
-            pending[i] = false;
+            pending[g] = false;
         }
         if (cap[i] < bytes) {
             if (host[i]) (void)hipHostFree(host[i]);
             host[i] = nullptr;
+            dev[i] = nullptr;
             cap[i] = 0;
-            size_t want = bytes + bytes / 4 + 4096;
-            hipError_t e = hipHostMalloc(&host[i], want, hipHostMallocDefault);
+            size_t want = (bytes + bytes / 4 + 4096 + 15) / 16 * 16;
+            hipError_t e = hipHostMalloc(&host[i], want, hipHostMallocMapped | hipHostMallocCoherent);
             if (e != hipSuccess) { host[i] = nullptr; return e; }
+            e = hipHostGetDevicePointer(&dev[i], host[i], 0);
+            if (e != hipSuccess) {
+                (void)hipHostFree(host[i]);
+                host[i] = nullptr;
+                dev[i] = nullptr;
+                return e;
+            }
             cap[i] = want;
         }
         *slot = i;
         return hipSuccess;
     }
-    hipError_t copy(int slot, void* dst, size_t bytes, hipStream_t stream) {
-        hipError_t e = hipMemcpyAsync(dst, host[slot], bytes, hipMemcpyHostToDevice, stream);
+    // bytes: a multiple of 16 within the slot's capacity
+    hipError_t upload(int slot, void* dst, size_t bytes, hipStream_t stream,
+                      const ca::LaunchEvents& timing) {
+        const int64_t n = static_cast<int64_t>(bytes / 16);
+        const int64_t blocks = (n + 255) / 256;
+        const dim3 grid(static_cast<unsigned>(blocks < 256 ? (blocks > 0 ? blocks : 1) : 256));
+        hipExtLaunchKernelGGL(upload_kernel, grid, dim3(256), 0, stream, timing.start, timing.stop, 0,
+                              static_cast<const uint4*>(dev[slot]), static_cast<uint4*>(dst), n);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = hipEventRecord(ev[slot], stream);
-        if (e != hipSuccess) return e;
-        pending[slot] = true;
+        if (slot % kGroup == kGroup - 1) {
+            e = hipEventRecord(ev[slot / kGroup], stream);
+            if (e != hipSuccess) return e;
+            pending[slot / kGroup] = true;
+        }
         return hipSuccess;
     }
     void release() {
+        for (int g = 0; g < kSlots / kGroup; ++g) {
+            if (pending[g]) (void)hipEventSynchronize(ev[g]);
+            if (ev[g]) (void)hipEventDestroy(ev[g]);
+            ev[g] = nullptr;
+            pending[g] = false;
+        }
         for (int i = 0; i < kSlots; ++i) {
-            if (pending[i]) (void)hipEventSynchronize(ev[i]);
             if (host[i]) (void)hipHostFree(host[i]);
-            if (ev[i]) (void)hipEventDestroy(ev[i]);
             host[i] = nullptr;
-            ev[i] = nullptr;
+            dev[i] = nullptr;
         }
     }
 };
@@ -117,23 +156,25 @@ struct Staging {
 }  // namespace
 
 // Work lists of one attention call, built on the host from the plan: decode splits and their
-// merges, chunk workgroups and their merges.
+// merges, chunk workgroups and their merges (split = decode shares, csplit = keys per chunk
+// split).
 struct WorkKey {
     uint64_t generation = 0;
     int32_t hq = 0, hkv = 0, d = 0, split = 0, csplit = 0;
+    double theta = 0.0;
     bool operator==(const WorkKey& o) const {
         return generation == o.generation && hq == o.hq && hkv == o.hkv && d == o.d &&
-               split == o.split && csplit == o.csplit;
+               split == o.split && csplit == o.csplit && theta == o.theta;
     }
 };
 
 struct DevWork {
-    const int4* dec_items = nullptr;
-    const int32_t* dec_out = nullptr;
+    const int4* dec_items = nullptr;          // two int4 per decode item
+    const int32_t* dec_wave_items = nullptr;  // [num_dec_waves + 1] first item of each wave
     const int4* merges = nullptr;
     const int4* chunk_items = nullptr;   // two int4 per workgroup
     const int4* chunk_groups = nullptr;  // two int4 per multi-split row block
-    int32_t num_dec_items = 0, num_merges = 0, num_slots = 0;
+    int32_t num_dec_items = 0, num_dec_waves = 0, num_merges = 0, num_slots = 0;
     int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0;
 };
 
@@ -167,26 +208,35 @@ struct Profiler {
     }
 };
 
-// Records one launch between two events when profiling is on.
+// Timing of one library call when profiling is on: a start/stop event pair handed to the
+// launcher, which attaches it to the call's kernels (LaunchEvents).  commit() after a successful
+// launch files the record; otherwise the events go back to the pool unrecorded.
 struct Timed {
     Profiler& pf;
     const char* name;
-    hipStream_t stream;
-    hipEvent_t a = nullptr;
-    Timed(Profiler& p, const char* n, hipStream_t s) : pf(p), name(n), stream(s) {
+    ca::LaunchEvents ev{};
+    bool committed = false;
+    Timed(Profiler& p, const char* n) : pf(p), name(n) {
         if (pf.on && pf.pending.size() < 65536) {
-            a = pf.get();
-            if (a && hipEventRecord(a, stream) != hipSuccess) { pf.pool.push_back(a); a = nullptr; }
+            ev.start = pf.get();
+            ev.stop = pf.get();
+            if (!ev.start || !ev.stop) {
+                if (ev.start) pf.pool.push_back(ev.start);
+                if (ev.stop) pf.pool.push_back(ev.stop);
+                ev = ca::LaunchEvents{};
+            }
+        }
+    }
+    void commit() {
+        if (ev.start) {
+            pf.pending.push_back({name, ev.start, ev.stop});
+            committed = true;
         }
     }
     ~Timed() {
-        if (!a) return;
-        hipEvent_t b = pf.get();
-        if (b && hipEventRecord(b, stream) == hipSuccess) {
-            pf.pending.push_back({name, a, b});
-        } else {
-            pf.pool.push_back(a);
-            if (b) pf.pool.push_back(b);
+        if (ev.start && !committed) {
+            pf.pool.push_back(ev.start);
+            pf.pool.push_back(ev.stop);
         }
     }
 };
@@ -197,6 +247,7 @@ struct ca_ctx {
     Staging staging;
     DevBuf meta_buf;        // one upload per step: plan metadata, then the work lists
     DevPlan dplan{};
+    const double* inv_freq = nullptr;  // [d / 2] rotary inverse frequencies, in meta_buf
     DevBuf partial_buf;     // fp32 split-KV partials of the generic path
     WorkKey work_key{};     // what meta_buf holds (generation 0: nothing)
     DevWork dwork{};
@@ -204,7 +255,9 @@ struct ca_ctx {
     DevBuf dec_ml_buf;      // float2 [slots][G]
     DevBuf chk_acc_buf;     // fp32 [slots][cols][d]
     DevBuf chk_ml_buf;      // float2 [slots][cols]
-    int32_t split_override = 0;   // CA_DECODE_SPLIT (keys per decode split), 0 = automatic
+    int32_t num_cus = 0;
+    int32_t dec_waves_per_cu[2] = {0, 0};  // d = 64, d = 128 (queried on first use)
+    int32_t dec_waves_override = 0;  // CA_DECODE_WAVES (decode shares), 0 = automatic
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
 };
 
@@ -228,6 +281,12 @@ struct DeviceGuard {
         if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
     }
 };
+
+bool aligned16(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
+    return true;
+}
 
 ca_status check_plan(const ca_plan* plan) {
     if (!plan) { ca::set_error("null plan"); return CA_ERR_INVALID_ARG; }
@@ -321,23 +380,24 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
     return CA_OK;
 }
 
-// Keys per decode split: enough work items to cover every CU several times over, in whole
-// 32-key blocks, and long enough that the partial (G x (d + 2) floats) stays a few percent of
-// the K/V bytes the split reads.
-int32_t decode_split_keys(const ca_plan* plan, const Shape& sh, int32_t override_keys) {
-    if (override_keys > 0) return ((override_keys + 31) / 32) * 32;
-    int64_t total = 0;
+// Number of decode shares: the 32-key blocks of every (decode row, kv head), laid end to end, are
+// cut into this many equal runs, one per decode wavefront the device holds at once, so a single
+// round of waves streams the whole decode K/V with no tail.
+int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh) {
+    int64_t blocks = 0;
     for (int32_t s = 0; s < plan->num_decodes; ++s) {
         const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
-        total += static_cast<int64_t>(np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        blocks += (kv_len + 31) / 32;
     }
-    total *= sh.hkv;
-    const int64_t target_items = 6144;
-    int64_t L = (total + target_items - 1) / target_items;
-    L = ((L + 31) / 32) * 32;
-    if (L < 256) L = 256;
-    if (L > 4096) L = 4096;
-    return static_cast<int32_t>(L);
+    blocks *= sh.hkv;
+    int64_t W = ctx->dec_waves_override;
+    if (W <= 0) {
+        int32_t& per_cu = ctx->dec_waves_per_cu[sh.d == 128 ? 1 : 0];
+        if (per_cu == 0) per_cu = ca::decode_waves_per_cu(sh.d);
+        W = static_cast<int64_t>(ctx->num_cus) * per_cu;
+    }
+    return static_cast<int32_t>(W < blocks ? W : blocks);
 }
 
 // Keys per chunk split: a row block whose visible keys exceed this is cut into several
@@ -401,9 +461,10 @@ int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
 }
 
 // Make the plan's metadata and, for the MFMA path, its work lists resident on the device.
-// Everything goes in ONE host->device copy (pinned staging, async on the caller's stream):
-//   [qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices | row_seq | pad to 16 B]
-//   [decode items | item outputs | decode merges | chunk items | chunk merges]
+// Everything goes in ONE upload (pinned staging, copied by a kernel on the caller's stream):
+//   [qo_indptr | kv_page_indptr | kv_last_page_len | kv_page_indices | row_seq | row_pos |
+//    row_page | pad to 16 B][rotary inverse frequencies, fp64]
+//   [decode items | first item of each decode wave | decode merges | chunk items | chunk merges]
 // keyed by (plan generation, shape, split sizes), so the append and the attention of one step
 // share it and a repeated call with the same plan uploads nothing.
 ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
@@ -411,36 +472,59 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     const int G = sh.hq / sh.hkv;
     const bool mfma = sh.dtype == CA_BF16 && G <= 16;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
-                mfma ? decode_split_keys(plan, sh, ctx->split_override) : -1,
-                mfma ? chunk_split_keys(plan, sh, ctx->csplit_override) : -1};
+                mfma ? decode_shares(ctx, plan, sh) : -1,
+                mfma ? chunk_split_keys(plan, sh, ctx->csplit_override) : -1, sh.theta};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
     ca_status st = validate_plan_arrays(plan, pool);
     if (st != CA_OK) return st;
 
     std::vector<int4> items, merges, citems, groups;
-    std::vector<int32_t> outs;
+    std::vector<int32_t> wave_items;
     int32_t slots = 0, cslots = 0;
     if (mfma) {
-        // decode: one wave per (row, kv head, split of L keys)
-        const int32_t L = key.split;
+        // decode: share w holds blocks [B w / W, B (w + 1) / W) of the B blocks of all
+        // (decode row, kv head) pairs in order; each pair's run inside a share is one item, and
+        // a pair cut over several shares gets one partial slot per piece and a merge
+        const int32_t W = key.split;
+        const int64_t B = [&] {
+            int64_t b = 0;
+            for (int32_t s = 0; s < plan->num_decodes; ++s) {
+                const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+                b += ((np - 1) * plan->page_size + plan->kv_last_page_len[s] + 31) / 32;
+            }
+            return b * sh.hkv;
+        }();
+        auto bound = [&](int64_t k) { return B * k / W; };
+        wave_items.assign(static_cast<size_t>(W) + 1, 0);
+        int64_t off = 0;
+        int32_t w = 0;
         for (int32_t s = 0; s < plan->num_decodes; ++s) {
-            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            const int32_t p0 = plan->kv_page_indptr[s];
+            const int32_t np = plan->kv_page_indptr[s + 1] - p0;
             const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
-            const int32_t nsplit = (kv_len + L - 1) / L;
+            const int64_t nb = (kv_len + 31) / 32;
+            const int32_t row = plan->qo_indptr[s];
             for (int32_t g = 0; g < sh.hkv; ++g) {
-                if (nsplit == 1) {
-                    items.push_back(make_int4(s, g, 0, kv_len));
-                    outs.push_back(-1);
-                    continue;
+                const int64_t end = off + nb;
+                const size_t first = items.size() / 2;
+                for (int64_t lo = off; lo < end;) {
+                    while (bound(w + 1) <= lo) wave_items[++w] = static_cast<int32_t>(items.size() / 2);
+                    const int64_t hi = end < bound(w + 1) ? end : bound(w + 1);
+                    const int32_t kb = static_cast<int32_t>(32 * (lo - off));
+                    const int32_t ke = static_cast<int32_t>(32 * (hi - off) < kv_len ? 32 * (hi - off) : kv_len);
+                    items.push_back(make_int4(g, kb, ke, -1));
+                    items.push_back(make_int4(row, p0, np, 0));
+                    lo = hi;
                 }
-                merges.push_back(make_int4(s, g, slots, nsplit));
-                for (int32_t i = 0; i < nsplit; ++i) {
-                    const int32_t b = i * L, e = (b + L < kv_len) ? b + L : kv_len;
-                    items.push_back(make_int4(s, g, b, e));
-                    outs.push_back(slots++);
+                const int32_t pieces = static_cast<int32_t>(items.size() / 2 - first);
+                if (pieces > 1) {
+                    merges.push_back(make_int4(row, g, slots, pieces));
+                    for (int32_t i = 0; i < pieces; ++i) items[2 * (first + i)].w = slots++;
                 }
+                off = end;
             }
         }
+        while (w < W) wave_items[++w] = static_cast<int32_t>(items.size() / 2);
         // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys);
         // a column is one (row, q head) pair, numbered row * G + head
         const int32_t Lc = key.csplit;
@@ -462,7 +546,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
                         continue;
                     }
                     groups.push_back(make_int4(s, g, cb, cslots));
-                    groups.push_back(make_int4(nsplit, 0, 0, 0));
+                    groups.push_back(make_int4(nsplit, plan->qo_indptr[s], q_len, 0));
                     for (int32_t i = 0; i < nsplit; ++i) {
                         const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
                         clist.push_back(make_int4(s, g, cb, cslots++));
@@ -476,15 +560,16 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
 
     const int32_t ns = plan->num_seqs;
     const int32_t T = plan->num_tokens;
-    const size_t plan_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages + T;
-    const size_t off_items = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
-    const size_t n_items = items.size(), n_merges = merges.size();
-    const size_t out_words = (n_items + 3) / 4 * 4;
-    const size_t off_out = off_items + n_items * sizeof(int4);
-    const size_t off_merge = off_out + out_words * sizeof(int32_t);
+    const size_t plan_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages + 3 * static_cast<size_t>(T);
+    const size_t off_freq = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
+    const size_t off_items = off_freq + (static_cast<size_t>(sh.d / 2) * sizeof(double) + 15) / 16 * 16;
+    const size_t n_items = items.size() / 2, n_merges = merges.size();
+    const size_t wave_words = (wave_items.size() + 3) / 4 * 4;
+    const size_t off_out = off_items + items.size() * sizeof(int4);
+    const size_t off_merge = off_out + wave_words * sizeof(int32_t);
     const size_t off_citem = off_merge + n_merges * sizeof(int4);
     const size_t off_group = off_citem + citems.size() * sizeof(int4);
-    const size_t bytes = off_group + groups.size() * sizeof(int4) + 16;
+    const size_t bytes = (off_group + groups.size() * sizeof(int4) + 16 + 15) / 16 * 16;
     hipError_t e = ctx->meta_buf.reserve(bytes, stream);
     if (e != hipSuccess) return device_error("metadata allocation", e);
     int slot = 0;
@@ -497,16 +582,36 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     std::memcpy(hp + 2 * (ns + 1), plan->kv_last_page_len, sizeof(int32_t) * ns);
     if (plan->num_pages)
         std::memcpy(hp + 2 * (ns + 1) + ns, plan->kv_page_indices, sizeof(int32_t) * plan->num_pages);
+    // per row: its sequence, absolute position and destination page (the slot is pos % P)
     int32_t* hrow = hp + 2 * (ns + 1) + ns + plan->num_pages;
-    for (int32_t s = 0; s < ns; ++s)
-        for (int32_t t = plan->qo_indptr[s]; t < plan->qo_indptr[s + 1]; ++t) hrow[t] = s;
-    std::memcpy(h + off_items, items.data(), n_items * sizeof(int4));
-    std::memcpy(h + off_out, outs.data(), n_items * sizeof(int32_t));
+    int32_t* hpos = hrow + T;
+    int32_t* hpage = hpos + T;
+    for (int32_t s = 0; s < ns; ++s) {
+        const int32_t q0 = plan->qo_indptr[s], q_len = plan->qo_indptr[s + 1] - q0;
+        const int32_t p0 = plan->kv_page_indptr[s];
+        const int32_t kv_len = (plan->kv_page_indptr[s + 1] - p0 - 1) * plan->page_size + plan->kv_last_page_len[s];
+        for (int32_t i = 0; i < q_len; ++i) {
+            const int32_t pos = kv_len - q_len + i;
+            hrow[q0 + i] = s;
+            hpos[q0 + i] = pos;
+            hpage[q0 + i] = plan->kv_page_indices[p0 + pos / plan->page_size];
+        }
+    }
+    // rotary inverse frequencies theta^(-2i/d), fp64
+    double* hfreq = reinterpret_cast<double*>(h + off_freq);
+    for (int32_t i = 0; i < sh.d / 2; ++i)
+        hfreq[i] = std::pow(sh.theta, -2.0 * static_cast<double>(i) / static_cast<double>(sh.d));
+    std::memcpy(h + off_items, items.data(), items.size() * sizeof(int4));
+    std::memcpy(h + off_out, wave_items.data(), wave_items.size() * sizeof(int32_t));
     std::memcpy(h + off_merge, merges.data(), n_merges * sizeof(int4));
     std::memcpy(h + off_citem, citems.data(), citems.size() * sizeof(int4));
     std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
-    e = ctx->staging.copy(slot, ctx->meta_buf.ptr, bytes, stream);
-    if (e != hipSuccess) return device_error("metadata copy", e);
+    {
+        Timed t(ctx->prof, "upload");
+        e = ctx->staging.upload(slot, ctx->meta_buf.ptr, bytes, stream, t.ev);
+        if (e == hipSuccess) t.commit();
+    }
+    if (e != hipSuccess) return device_error("metadata upload", e);
 
     const char* d = static_cast<const char*>(ctx->meta_buf.ptr);
     const int32_t* dp = reinterpret_cast<const int32_t*>(d);
@@ -515,6 +620,9 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     ctx->dplan.kv_last_page_len = dp + 2 * (ns + 1);
     ctx->dplan.kv_page_indices = dp + 2 * (ns + 1) + ns;
     ctx->dplan.row_seq = dp + 2 * (ns + 1) + ns + plan->num_pages;
+    ctx->dplan.row_pos = ctx->dplan.row_seq + T;
+    ctx->dplan.row_page = ctx->dplan.row_pos + T;
+    ctx->inv_freq = reinterpret_cast<const double*>(d + off_freq);
     ctx->dplan.num_seqs = ns;
     ctx->dplan.num_decodes = plan->num_decodes;
     ctx->dplan.num_tokens = plan->num_tokens;
@@ -522,11 +630,12 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     ctx->dplan.page_size = plan->page_size;
     DevWork& w = ctx->dwork;
     w.dec_items = reinterpret_cast<const int4*>(d + off_items);
-    w.dec_out = reinterpret_cast<const int32_t*>(d + off_out);
+    w.dec_wave_items = reinterpret_cast<const int32_t*>(d + off_out);
     w.merges = reinterpret_cast<const int4*>(d + off_merge);
     w.chunk_items = reinterpret_cast<const int4*>(d + off_citem);
     w.chunk_groups = reinterpret_cast<const int4*>(d + off_group);
     w.num_dec_items = static_cast<int32_t>(n_items);
+    w.num_dec_waves = wave_items.empty() ? 0 : static_cast<int32_t>(wave_items.size()) - 1;
     w.num_merges = static_cast<int32_t>(n_merges);
     w.num_slots = slots;
     w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
@@ -561,7 +670,12 @@ ca_status ca_create(int device, ca_ctx** out) {
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     ca_ctx* ctx = new ca_ctx();
     ctx->device = device;
-    if (const char* env = std::getenv("CA_DECODE_SPLIT")) ctx->split_override = std::atoi(env);
+    if (const char* env = std::getenv("CA_DECODE_WAVES")) ctx->dec_waves_override = std::atoi(env);
+    e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess || ctx->num_cus <= 0) {
+        delete ctx;
+        return device_error("hipDeviceGetAttribute(multiprocessor count)", e != hipSuccess ? e : hipErrorInvalidValue);
+    }
     if (const char* env = std::getenv("CA_CHUNK_SPLIT")) ctx->csplit_override = std::atoi(env);
     e = ctx->staging.init();
     if (e != hipSuccess) {
@@ -606,6 +720,10 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
         ca::set_error("ca_append_kv_rope: null buffer");
         return CA_ERR_INVALID_ARG;
     }
+    if (!aligned16({q_in, q_out, k_new, v_new, k_cache, v_cache})) {
+        ca::set_error("ca_append_kv_rope: device buffers must be 16-byte aligned");
+        return CA_ERR_INVALID_ARG;
+    }
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -613,8 +731,10 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
     if (st != CA_OK) return st;
     hipError_t e;
     {
-        Timed t(ctx->prof, "append_rope", stream);
-        e = ca::launch_append_rope(ctx->dplan, sh, q_in, q_out, k_new, v_new, k_cache, v_cache, stream);
+        Timed t(ctx->prof, "append_rope");
+        e = ca::launch_append_rope(ctx->dplan, sh, ctx->inv_freq, q_in, q_out, k_new, v_new, k_cache,
+                                   v_cache, stream, t.ev);
+        if (e == hipSuccess) t.commit();
     }
     if (e != hipSuccess) return device_error("append_rope launch", e);
     return CA_OK;
@@ -636,6 +756,10 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         ca::set_error("ca_mixed_attention: null buffer");
         return CA_ERR_INVALID_ARG;
     }
+    if (!aligned16({q, k_cache, v_cache, o}) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) {
+        ca::set_error("ca_mixed_attention: device buffers must be 16-byte aligned (lse 4-byte)");
+        return CA_ERR_INVALID_ARG;
+    }
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -655,19 +779,22 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         // workgroups (8 waves, 72 KB of LDS) only start where a CU drains completely, and the
         // fork/join events stalled the host between steps.
         if (w.num_chunk_items > 0) {
-            Timed t(ctx->prof, "chunk", stream);
+            Timed t(ctx->prof, "chunk");
             e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, q, k_cache,
-                                 v_cache, cacc, cml, o, lse, stream);
+                                 v_cache, cacc, cml, o, lse, stream, t.ev);
+            if (e == hipSuccess) t.commit();
         }
-        if (e == hipSuccess && w.num_dec_items > 0) {
-            Timed t(ctx->prof, "decode", stream);
-            e = ca::launch_decode(ctx->dplan, sh, w.dec_items, w.dec_out, w.num_dec_items, q, k_cache,
-                                  v_cache, dacc, dml, o, lse, stream);
+        if (e == hipSuccess && w.num_dec_waves > 0) {
+            Timed t(ctx->prof, "decode");
+            e = ca::launch_decode(ctx->dplan, sh, w.dec_items, w.dec_wave_items, w.num_dec_waves, q,
+                                  k_cache, v_cache, dacc, dml, o, lse, stream, t.ev);
+            if (e == hipSuccess) t.commit();
         }
         if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
-            Timed t(ctx->prof, "merge", stream);
+            Timed t(ctx->prof, "merge");
             e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
-                                 w.num_chunk_groups, cacc, cml, o, lse, stream);
+                                 w.num_chunk_groups, cacc, cml, o, lse, stream, t.ev);
+            if (e == hipSuccess) t.commit();
         }
         if (e != hipSuccess) return device_error("attention launch", e);
         return CA_OK;
@@ -678,9 +805,11 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
     if (e != hipSuccess) return device_error("partials allocation", e);
     {
-        Timed t(ctx->prof, "generic", stream);
+        Timed t(ctx->prof, "generic");
         e = ca::launch_attention_generic(ctx->dplan, sh, 0, q, k_cache, v_cache, o, lse,
-                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream);
+                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream,
+                                         t.ev);
+        if (e == hipSuccess) t.commit();
     }
     if (e != hipSuccess) return device_error("attention launch", e);
     return CA_OK;

@@ -4,10 +4,16 @@
 // carries its absolute position (positions are never restarted per chunk) and its K/V goes into
 // the paged cache, in its request's logical page p / P, slot p % P, before attention reads it.
 //
-// One workgroup per token.  The pair angles p * theta^(-2i/d) are formed in fp64 once per token
-// (d/2 of them, shared by every head) and kept in LDS; each rotated element is computed in fp64
-// and rounded once to the storage type.  Work per token is tiny and the kernel is bound by the
-// bytes it moves (read q, k, v; write q', the K row and the V column of one slot).
+// One workgroup per token.  The work per token is a few KB, so the kernel is bound by latency,
+// and it is laid out to pay one memory round trip, not a chain of them:
+//   * the token's position and destination page come from per-row arrays the host fills with
+//     the plan (no sequence -> indptr -> page-id chain), and the inverse frequencies
+//     theta^(-2i/d) are a host-computed fp64 table;
+//   * every q/k/v load is a 16-byte vector load, all issued before the first store (a thread
+//     writes back exactly the elements it read, so q_out may alias q_in), and unconditional so
+//     that they are in flight together;
+//   * the d/2 pair angles are formed in fp64 once per token, shared through LDS, and each
+//     rotated element is computed in fp64 and rounded once to the storage type.
 
 #include <hip/hip_runtime.h>
 
@@ -17,87 +23,154 @@
 namespace ca {
 namespace {
 
+constexpr int kThreads = 256;
+constexpr int kUnits = 4;  // q/k vector units per thread per pass
+
 template <typename T>
-__global__ void __launch_bounds__(256) append_rope_kernel(
-    DevPlan p, const T* q_in, T* q_out, const T* __restrict__ k_new,
-    const T* __restrict__ v_new, T* __restrict__ k_cache, T* __restrict__ v_cache, int hq, int hkv,
-    int d, double theta) {
+struct Vec {
+    static constexpr int N = 16 / sizeof(T);
+    T e[N];
+};
+
+template <typename T>
+__device__ __forceinline__ Vec<T> load16(const T* p) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    Vec<T> v;
+    __builtin_memcpy(&v, &raw, sizeof(v));
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const Vec<T>& v) {
+    uint4 raw;
+    __builtin_memcpy(&raw, &v, sizeof(raw));
+    *reinterpret_cast<uint4*>(p) = raw;
+}
+
+template <typename T>
+__device__ __forceinline__ double widen(T x);
+template <>
+__device__ __forceinline__ double widen<float>(float x) { return static_cast<double>(x); }
+template <>
+__device__ __forceinline__ double widen<uint16_t>(uint16_t x) { return static_cast<double>(bf16_bits_to_float(x)); }
+
+template <typename T>
+__device__ __forceinline__ T narrow(double x);
+template <>
+__device__ __forceinline__ float narrow<float>(double x) { return static_cast<float>(x); }
+template <>
+__device__ __forceinline__ uint16_t narrow<uint16_t>(double x) { return double_to_bf16_bits(x); }
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) append_rope_kernel(
+    const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_page,
+    const double* __restrict__ inv_freq, const T* q_in, T* q_out, const T* __restrict__ k_new,
+    const T* __restrict__ v_new, T* __restrict__ k_cache, T* __restrict__ v_cache, int hq,
+    int hkv, int d, int P) {
 #pragma clang fp contract(off)
+    constexpr int N = Vec<T>::N;
     __shared__ double s_cos[64];
     __shared__ double s_sin[64];
     const int t = blockIdx.x;
-    const int P = p.page_size;
-    const int s = p.row_seq[t];
-    const int np = p.kv_page_indptr[s + 1] - p.kv_page_indptr[s];
-    const int kv_len = (np - 1) * P + p.kv_last_page_len[s];
-    const int q_len = p.qo_indptr[s + 1] - p.qo_indptr[s];
-    const int pos = kv_len - q_len + (t - p.qo_indptr[s]);
-    const int page = p.kv_page_indices[p.kv_page_indptr[s] + pos / P];
-    const int slot = pos % P;
+    const int tid = threadIdx.x;
     const int half = d >> 1;
+    const int per_head = half / N;  // vector units per head (each covers N pairs)
+    const int units = (hq + hkv) * per_head;
+    const int v_units = hkv * d / N;
+    const int pos = row_pos[t];
+    const int page = row_page[t];
+    const int slot = pos % P;
 
-    for (int i = threadIdx.x; i < half; i += blockDim.x) {
-        const double inv_freq = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(d));
-        const double angle = static_cast<double>(pos) * inv_freq;
+    // Loads are unconditional (indices clamped into range; only the stores are predicated), so
+    // they are all in flight together instead of each waiting at the end of its own branch.
+    // The frequency load is issued first: waiting for it does not wait for the q/k/v loads.
+    const double freq = inv_freq[tid < half ? tid : half - 1];
+    Vec<T> vv = load16(v_new + static_cast<int64_t>(t) * hkv * d + (tid < v_units ? tid : v_units - 1) * N);
+
+    Vec<T> a[kUnits], b[kUnits];
+    int i0[kUnits];
+    auto load_pass = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < kUnits; ++j) {
+            const int u0 = base + tid + j * kThreads;
+            const int u = u0 < units ? u0 : units - 1;
+            const int h = u / per_head;
+            i0[j] = (u - h * per_head) * N;
+            const T* src = h < hq ? q_in + (static_cast<int64_t>(t) * hq + h) * d
+                                  : k_new + (static_cast<int64_t>(t) * hkv + (h - hq)) * d;
+            a[j] = load16(src + i0[j]);
+            b[j] = load16(src + i0[j] + half);
+        }
+    };
+    auto rotate_pass = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < kUnits; ++j) {
+            const int u = base + tid + j * kThreads;
+            // skip a unit slot no lane of this wave uses (wave-uniform test)
+            if (__builtin_amdgcn_readfirstlane(base + j * kThreads + (tid & ~63)) >= units) continue;
+            Vec<T> ra, rb;
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                const double x = widen<T>(a[j].e[e]), y = widen<T>(b[j].e[e]);
+                const double c = s_cos[i0[j] + e], s = s_sin[i0[j] + e];
+                ra.e[e] = narrow<T>(x * c - y * s);
+                rb.e[e] = narrow<T>(y * c + x * s);
+            }
+            if (u < units) {
+                const int h = u / per_head;
+                T* dst = h < hq ? q_out + (static_cast<int64_t>(t) * hq + h) * d
+                                : k_cache + ((static_cast<int64_t>(page) * hkv + (h - hq)) * P + slot) * d;
+                store16(dst + i0[j], ra);
+                store16(dst + i0[j] + half, rb);
+            }
+        }
+    };
+
+    load_pass(0);
+    if (tid < half) {
         double sn, cs;
-        sincos(angle, &sn, &cs);
-        s_cos[i] = cs;
-        s_sin[i] = sn;
+        sincos(static_cast<double>(pos) * freq, &sn, &cs);
+        s_cos[tid] = cs;
+        s_sin[tid] = sn;
     }
     __syncthreads();
-
-    // Rotate every (head, pair) of q and k.  Each thread reads both members of its pair before
-    // writing them, so q_out may alias q_in.
-    const int pairs = (hq + hkv) * half;
-    for (int idx = threadIdx.x; idx < pairs; idx += blockDim.x) {
-        const int h = idx / half;
-        const int i = idx - h * half;
-        const T* src;
-        T* dst;
-        if (h < hq) {
-            src = q_in + (static_cast<int64_t>(t) * hq + h) * d;
-            dst = q_out + (static_cast<int64_t>(t) * hq + h) * d;
-        } else {
-            const int g = h - hq;
-            src = k_new + (static_cast<int64_t>(t) * hkv + g) * d;
-            dst = k_cache + ((static_cast<int64_t>(page) * hkv + g) * P + slot) * d;
-        }
-        const double a = static_cast<double>(Storage<T>::load(src + i));
-        const double b = static_cast<double>(Storage<T>::load(src + i + half));
-        const double c = s_cos[i], sn = s_sin[i];
-        Storage<T>::store_from_double(dst + i, a * c - b * sn);
-        Storage<T>::store_from_double(dst + i + half, b * c + a * sn);
+    rotate_pass(0);
+    for (int base = kThreads * kUnits; base < units; base += kThreads * kUnits) {
+        load_pass(base);
+        rotate_pass(base);
     }
 
-    // V is copied unrotated into the dimension-major page: element e of slot goes to [e][slot].
-    const int vn = hkv * d;
-    for (int idx = threadIdx.x; idx < vn; idx += blockDim.x) {
-        const int g = idx / d;
-        const int e = idx - g * d;
-        v_cache[((static_cast<int64_t>(page) * hkv + g) * d + e) * P + slot] =
-            v_new[(static_cast<int64_t>(t) * hkv + g) * d + e];
+    // V goes unrotated into the dimension-major page: element e of the slot lands at [e][slot]
+    for (int vu = tid; vu < v_units; vu += kThreads) {
+        if (vu != tid) vv = load16(v_new + static_cast<int64_t>(t) * hkv * d + vu * N);
+        const int g = (vu * N) / d;
+        const int e0 = vu * N - g * d;
+        T* vp = v_cache + ((static_cast<int64_t>(page) * hkv + g) * d + e0) * P + slot;
+#pragma unroll
+        for (int e = 0; e < N; ++e) vp[static_cast<int64_t>(e) * P] = vv.e[e];
     }
 }
 
 }  // namespace
 
-hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const void* q_in, void* q_out,
-                              const void* k_new, const void* v_new, void* k_cache,
-                              void* v_cache, hipStream_t stream) {
+hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
+                              const void* q_in, void* q_out, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, hipStream_t stream,
+                              const LaunchEvents& ev) {
     if (p.num_tokens <= 0) return hipSuccess;
-    dim3 grid(p.num_tokens), block(256);
+    const dim3 grid(p.num_tokens), block(kThreads);
     if (sh.dtype == CA_FP32) {
-        hipLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, p,
-                           static_cast<const float*>(q_in), static_cast<float*>(q_out),
+        hipExtLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, ev.start, ev.stop, 0, p.row_pos, p.row_page,
+                           inv_freq, static_cast<const float*>(q_in), static_cast<float*>(q_out),
                            static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                            static_cast<float*>(k_cache), static_cast<float*>(v_cache), sh.hq,
-                           sh.hkv, sh.d, sh.theta);
+                           sh.hkv, sh.d, p.page_size);
     } else {
-        hipLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, p,
-                           static_cast<const uint16_t*>(q_in), static_cast<uint16_t*>(q_out),
-                           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                           sh.hq, sh.hkv, sh.d, sh.theta);
+        hipExtLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, ev.start, ev.stop, 0, p.row_pos,
+                           p.row_page, inv_freq, static_cast<const uint16_t*>(q_in),
+                           static_cast<uint16_t*>(q_out), static_cast<const uint16_t*>(k_new),
+                           static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
+                           static_cast<uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, p.page_size);
     }
     return hipGetLastError();
 }

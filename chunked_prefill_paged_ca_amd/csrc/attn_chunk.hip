@@ -200,8 +200,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
             for (int jj = 1; jj < 8; ++jj) lmax = fmaxf(lmax, sc[jj]);
             lmax *= scale_log2;
             if (__any(lmax > m[nt] + kRescaleSlack)) {
-                float bm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                float bm = rows_max(lmax);
                 const bool grow = bm > m[nt] + kRescaleSlack;
                 const float alpha = grow ? exp2_fast(m[nt] - bm) : 1.0f;
                 l[nt] *= alpha;
@@ -296,8 +295,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
         float lt = l[nt];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        lt = rows_sum(lt);
         const int wc = 32 * w + 16 * nt + c;  // column within the workgroup
         const int col = cb + wc;
         if (col >= ncols) continue;
@@ -331,7 +329,8 @@ int chunk_max_split_keys() { return 16 * (kMaxItemPages - 2); }
 
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
                         const void* q, const void* k_cache, const void* v_cache, float* part_acc,
-                        float2* part_ml, void* o, float* lse, hipStream_t stream) {
+                        float2* part_ml, void* o, float* lse, hipStream_t stream,
+                        const LaunchEvents& ev) {
     if (num_items <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
     auto qq = static_cast<const uint16_t*>(q);
@@ -339,10 +338,10 @@ hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, in
     auto vc = static_cast<const uint16_t*>(v_cache);
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
-        hipLaunchKernelGGL(chunk_kernel<128>, dim3(num_items), dim3(64 * kWaves), 0, stream, p, items,
+        hipExtLaunchKernelGGL(chunk_kernel<128>, dim3(num_items), dim3(64 * kWaves), 0, stream, ev.start, ev.stop, 0, p, items,
                            qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
     else
-        hipLaunchKernelGGL(chunk_kernel<64>, dim3(num_items), dim3(64 * kWaves), 0, stream, p, items,
+        hipExtLaunchKernelGGL(chunk_kernel<64>, dim3(num_items), dim3(64 * kWaves), 0, stream, ev.start, ev.stop, 0, p, items,
                            qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
     return hipGetLastError();
 }

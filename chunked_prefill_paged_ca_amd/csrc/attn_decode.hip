@@ -6,17 +6,20 @@
 // request.  Decode is bound by reading the whole history K/V once (magicnetworld.com
 // "分块预填充与 Stall-free 调度", section 三: its arithmetic intensity is capped by the context
 // length), so the kernel is organised around HBM traffic:
-//   * one wavefront per work item (decode row, kv head, key range of a split); the G query heads
-//     sharing the kv head are the columns of one MFMA tile, so each K/V byte is read once for all
-//     of them;
+//   * the 32-key blocks of every (decode row, kv head), laid end to end, are cut into equal
+//     shares, one per wavefront the chip holds at once, so every wave streams the same number of
+//     bytes and there is no tail of short items; a share is a run of work items (decode row,
+//     kv head, key range) processed back to back;
+//   * the G query heads sharing a kv head are the columns of one MFMA tile, so each K/V byte is
+//     read once for all of them;
 //   * every K and V fragment is a 16-byte load issued straight from HBM into registers, and the
 //     next 32-key block is requested before the current one is consumed (register double buffer),
 //     so each wave keeps two blocks (16 KB) in flight;
 //   * QK^T and PV run on MFMA only so that the vector ALUs stay free: at G = 8 the fp32 vector
 //     work of a VALU dot product would need most of the chip's non-packed vector rate just to keep
 //     up with 8 TB/s of bf16 K/V.
-// Splits shorter than the whole context write fp32 partials (unnormalised o, running max, sum);
-// a single-split row writes its normalised output directly.
+// An item shorter than the whole context writes fp32 partials (unnormalised o, running max, sum);
+// an item covering a whole (row, kv head) writes its normalised output directly.
 
 #include <hip/hip_runtime.h>
 
@@ -60,27 +63,21 @@ __device__ __forceinline__ void load_block(Block<D>& b, const uint16_t* __restri
     for (int mt = 0; mt < D / 16; ++mt) b.v[mt] = load_frag(vp + 16 * 16 * mt);
 }
 
-// item = {seq, kv head, key begin, key end}; out = partial slot (>= 0) or -1 for direct output
+// One work item: the keys [kb, ke) of one (decode row, kv head).  rec0 = {kv head, kb, ke,
+// partial slot or -1 for direct output}, rec1 = {row, offset of the row's page ids, page count, 0}.
 template <int D>
-__global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
-    DevPlan p, const int4* __restrict__ items, const int32_t* __restrict__ item_out, int num_items,
+__device__ __forceinline__ void decode_item(
+    const int4 rec0, const int4 rec1, const int32_t* __restrict__ page_indices,
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
-    const int lane = threadIdx.x & 63;
-    // wave-uniform item index: everything derived from it (page ids included) lives in scalar
-    // registers and is read with scalar loads, which do not share the vector-load counter the
-    // K/V prefetch relies on
-    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    if (item >= num_items) return;
-    const int4 it = items[item];
-    const int s = it.x, g = it.y, kb = it.z, ke = it.w;
+    float* __restrict__ lse, int lane) {
+    const int g = rec0.x, kb = rec0.y, ke = rec0.z, out = rec0.w;
+    const int row = rec1.x;
+    const int32_t* pages = page_indices + rec1.y;
+    const int np = rec1.z;
     const int G = hq / hkv;
     const int c = lane & 15, q = lane >> 4;
-    const int row = p.qo_indptr[s];
-    const int32_t* pages = p.kv_page_indices + p.kv_page_indptr[s];
-    const int np = p.kv_page_indptr[s + 1] - p.kv_page_indptr[s];
 
     // Q^T fragments: column c is q head g*G + c (zero beyond the group)
     bf16x8 qf[D / 32];
@@ -120,8 +117,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
         float bm = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sc[j]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = rows_max(bm);
         bm *= scale_log2;  // finite: key0 < ke
         const bool grow = bm > m + kRescaleSlack;
         if (__any(grow)) {
@@ -150,13 +146,16 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
         }
     };
 
-    // Page ids of a 32-key block (two pages; a page past the sequence end is replaced by the
-    // first one and never used).  They are scalar loads, fetched one block ahead of the K/V
-    // loads that need them.
+    // Page ids of a 32-key block (two pages; past the sequence end the last page is read again
+    // and never used).  They are scalar loads, fetched one block ahead of the K/V loads that
+    // need them; the two loads are independent so that nothing waits for them before then.
     auto pages_of = [&](int key0, int& pa, int& pb) {
-        const int lp = key0 >> 4;
+        const int lp = key0 >> 4 < np ? key0 >> 4 : np - 1;
         pa = pages[lp];
-        pb = (lp + 1 < np) ? pages[lp + 1] : pa;
+        pb = pages[lp + 1 < np ? lp + 1 : lp];
+        // keep the scalar loads here, a block ahead: left alone, the scheduler sinks them to
+        // just before their use and the wave then stalls on them with no K/V load issued
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
     // Register double buffer: the next block's loads are in flight while a block is consumed.
@@ -174,7 +173,7 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
         pages_of(kb + 32 * (bi + 2), pa, pb);
         consume(ba, kb + 32 * bi);
         load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, c, q);  // block bi + 2
-        if (bi + 3 < nblk) pages_of(kb + 32 * (bi + 3), pa, pb);
+        pages_of(kb + 32 * (bi + 3), pa, pb);  // clamped past the end, never used there
         consume(bb, kb + 32 * (bi + 1));
     }
     if (bi + 1 < nblk) {
@@ -184,12 +183,10 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
     } else {
         consume(ba, kb + 32 * bi);
     }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = rows_sum(l);
 
     if (c >= G) return;
     const int h = g * G + c;
-    const int out = item_out[item];
     if (out < 0) {
         const float inv = 1.0f / l;
         uint16_t* op = o + (static_cast<int64_t>(row) * hq + h) * D + 4 * q;
@@ -209,26 +206,60 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
     }
 }
 
+// One wavefront per share of the step's decode key blocks: wave w runs the items
+// [wave_items[w], wave_items[w + 1]) one after another.
+template <int D>
+__global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
+    const int4* __restrict__ items, const int32_t* __restrict__ wave_items, int num_waves,
+    const int32_t* __restrict__ page_indices, const uint16_t* __restrict__ qg,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
+    float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    // wave-uniform indices: everything derived from them (item records, page ids) lives in
+    // scalar registers and is read with scalar loads, which do not share the vector-load
+    // counter the K/V prefetch relies on
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    if (w >= num_waves) return;
+    const int i_end = wave_items[w + 1];
+    for (int i = wave_items[w]; i < i_end; ++i)
+        decode_item<D>(items[2 * i], items[2 * i + 1], page_indices, qg, k_cache, v_cache, hq, hkv,
+                       scale_log2, part_acc, part_ml, o, lse, lane);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* item_out, int num_items, const void* q, const void* k_cache,
-                         const void* v_cache, float* part_acc, float2* part_ml, void* o, float* lse,
-                         hipStream_t stream) {
-    if (num_items <= 0) return hipSuccess;
+                         const int32_t* wave_items, int num_waves, const void* q,
+                         const void* k_cache, const void* v_cache, float* part_acc,
+                         float2* part_ml, void* o, float* lse, hipStream_t stream,
+                         const LaunchEvents& ev) {
+    if (num_waves <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
-    const dim3 grid((num_items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
+    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
     auto qq = static_cast<const uint16_t*>(q);
     auto kc = static_cast<const uint16_t*>(k_cache);
     auto vc = static_cast<const uint16_t*>(v_cache);
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
-        hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, p, items, item_out,
-                           num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+        hipExtLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, ev.start, ev.stop, 0, items, wave_items, num_waves,
+                           p.kv_page_indices, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml,
+                           oo, lse);
     else
-        hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p, items, item_out,
-                           num_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
+        hipExtLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, ev.start, ev.stop, 0, items, wave_items, num_waves,
+                           p.kv_page_indices, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml,
+                           oo, lse);
     return hipGetLastError();
+}
+
+// Wavefronts of the decode kernel one CU holds at once (register-limited).
+int decode_waves_per_cu(int d) {
+    int blocks = 0;
+    const hipError_t e = d == 128
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<128>, 64 * kWavesPerBlock, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<64>, 64 * kWavesPerBlock, 0);
+    if (e != hipSuccess || blocks <= 0) return kWavesPerBlock;
+    return blocks * kWavesPerBlock;
 }
 
 }  // namespace ca

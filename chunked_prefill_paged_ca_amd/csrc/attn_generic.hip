@@ -146,23 +146,23 @@ size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit) {
 hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0, const void* q,
                                     const void* k_cache, const void* v_cache, void* o,
                                     float* lse, float* partial, int nsplit,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, const LaunchEvents& ev) {
     if (p.num_tokens - row0 <= 0) return hipSuccess;
     dim3 grid(p.num_tokens - row0, sh.hq, nsplit);
     dim3 mgrid(p.num_tokens - row0, sh.hq);
     if (sh.dtype == CA_FP32) {
-        hipLaunchKernelGGL(attn_generic_kernel<float>, grid, dim3(kWave), 0, stream, p,
+        hipExtLaunchKernelGGL(attn_generic_kernel<float>, grid, dim3(kWave), 0, stream, ev.start, nullptr, 0, p,
                            static_cast<const float*>(q), static_cast<const float*>(k_cache),
                            static_cast<const float*>(v_cache), sh.hq, sh.hkv, sh.d, sh.scale,
                            nsplit, row0, partial);
-        hipLaunchKernelGGL(merge_kernel<float>, mgrid, dim3(sh.d), 0, stream, partial, sh.hq, sh.d,
+        hipExtLaunchKernelGGL(merge_kernel<float>, mgrid, dim3(sh.d), 0, stream, nullptr, ev.stop, 0, partial, sh.hq, sh.d,
                            nsplit, row0, static_cast<float*>(o), lse);
     } else {
-        hipLaunchKernelGGL(attn_generic_kernel<uint16_t>, grid, dim3(kWave), 0, stream, p,
+        hipExtLaunchKernelGGL(attn_generic_kernel<uint16_t>, grid, dim3(kWave), 0, stream, ev.start, nullptr, 0, p,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                            static_cast<const uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, sh.scale,
                            nsplit, row0, partial);
-        hipLaunchKernelGGL(merge_kernel<uint16_t>, mgrid, dim3(sh.d), 0, stream, partial, sh.hq,
+        hipExtLaunchKernelGGL(merge_kernel<uint16_t>, mgrid, dim3(sh.d), 0, stream, nullptr, ev.stop, 0, partial, sh.hq,
                            sh.d, nsplit, row0, static_cast<uint16_t*>(o), lse);
     }
     return hipGetLastError();

@@ -20,33 +20,24 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// fp64 -> bf16 in one rounding (nearest, ties to even), without passing through fp32.
-// The top 18 bits of the fp64 magnitude (11 exponent + 7 fraction) are kept and the remaining
-// 45 fraction bits decide the rounding; a carry into the exponent is handled by the integer add.
-// Results below the bf16 normal range take the subnormal spacing 2^-133.
+// fp64 -> bf16 in one rounding (nearest, ties to even).  x is first rounded to fp32 with
+// round-to-odd (truncate, then set the last bit if anything was cut off), then the hardware
+// fp32 -> bf16 conversion rounds to nearest even.  Because fp32 keeps more than two extra bits
+// beyond bf16's 8, the second rounding gives exactly the nearest-even bf16 of x (the
+// round-to-odd double-rounding property: Boldo and Melquiond, "Emulation of FMA and correctly
+// rounded sums: proved algorithms using rounding to odd", IEEE Trans. Computers 2008).
+// Truncation is derived from the nearest-even conversion: if it moved away from zero, step one
+// fp32 ulp back toward zero.  NaN stays NaN, overflow goes to infinity.
 __device__ __forceinline__ uint16_t double_to_bf16_bits(double x) {
-    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-    const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
-    const uint64_t mag = u & 0x7fffffffffffffffull;
-    if (mag >= 0x7ff0000000000000ull) {  // inf or nan
-        if (mag > 0x7ff0000000000000ull) return static_cast<uint16_t>(sign | 0x7fc0u);
-        return static_cast<uint16_t>(sign | 0x7f80u);
-    }
-    const int exp_d = static_cast<int>(mag >> 52);  // biased fp64 exponent
-    if (exp_d - 1023 < -126) {
-        // subnormal (or zero) in bf16: multiples of 2^-133, rounded half to even
-        const double scaled = __builtin_fabs(x) * 0x1p133;
-        const double r = __builtin_rint(scaled);  // exact integer <= 2^7
-        const uint32_t m = static_cast<uint32_t>(r);
-        return static_cast<uint16_t>(sign | m);  // m == 128 lands on the smallest normal
-    }
-    uint64_t keep = mag >> 45;
-    const uint64_t rem = mag & ((1ull << 45) - 1);
-    const uint64_t half = 1ull << 44;
-    if (rem > half || (rem == half && (keep & 1ull))) ++keep;
-    const int exp_f = static_cast<int>(keep >> 7) - 1023 + 127;
-    if (exp_f >= 255) return static_cast<uint16_t>(sign | 0x7f80u);
-    return static_cast<uint16_t>(sign | (static_cast<uint32_t>(exp_f) << 7) | static_cast<uint32_t>(keep & 0x7f));
+    const float f = static_cast<float>(x);
+    const double back = static_cast<double>(f);
+    uint32_t u = __float_as_uint(f);
+    u -= __builtin_fabs(back) > __builtin_fabs(x) ? 1u : 0u;  // toward zero: truncation
+    u |= back != x ? 1u : 0u;                                 // sticky bit: round to odd
+    const __bf16 b = static_cast<__bf16>(__uint_as_float(u));
+    uint16_t r;
+    __builtin_memcpy(&r, &b, sizeof(r));
+    return r;
 }
 
 template <typename T> struct Storage;

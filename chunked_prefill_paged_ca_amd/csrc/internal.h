@@ -1,6 +1,7 @@
 // internal.h -- declarations shared by the library's translation units (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -24,7 +25,9 @@ struct DevPlan {
     const int32_t* kv_page_indptr;
     const int32_t* kv_page_indices;
     const int32_t* kv_last_page_len;
-    const int32_t* row_seq;  // [num_tokens] sequence of each flat row (qo_indptr expanded)
+    const int32_t* row_seq;   // [num_tokens] sequence of each flat row (qo_indptr expanded)
+    const int32_t* row_pos;   // [num_tokens] absolute position of each row
+    const int32_t* row_page;  // [num_tokens] pool page that receives the row's K/V (slot pos % P)
     int32_t num_seqs;
     int32_t num_decodes;
     int32_t num_tokens;
@@ -39,10 +42,20 @@ struct Shape {
     ca_dtype dtype;
 };
 
+// Optional timing events of one library call, attached to its launches with hipExtLaunchKernel
+// (start with the first kernel of the call, stop with the last), so timing puts no extra packet
+// in the stream.  Null events: no timing.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // ---- launchers (each enqueues on `stream`; returns hipSuccess or the launch error) ----
-hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const void* q_in, void* q_out,
-                              const void* k_new, const void* v_new, void* k_cache,
-                              void* v_cache, hipStream_t stream);
+// inv_freq: [d / 2] fp64 table theta^(-2i/d) in device memory.
+hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
+                              const void* q_in, void* q_out, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, hipStream_t stream,
+                              const LaunchEvents& ev);
 
 // Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
 // partial: fp32 workspace of num_tokens * hq * nsplit * (d + 2) floats.
@@ -50,17 +63,22 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const void* q_i
 hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0, const void* q,
                                     const void* k_cache, const void* v_cache, void* o,
                                     float* lse, float* partial, int nsplit,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const LaunchEvents& ev);
 
 size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
 
-// MFMA split-KV decode (bf16, G <= 16).  items[i] = {seq, kv head, key begin, key end};
-// item_out[i] = partial slot or -1 (single split: the output is written directly).
-// part_acc: [slots][G][d] fp32, part_ml: [slots][G] (running max in log2 units, sum).
+// MFMA split-KV decode (bf16, G <= 16).  items: two int4 per item, {kv head, key begin, key
+// end, partial slot or -1 (the item covers the whole row: output written directly)}, {row, offset
+// of the row's page ids in kv_page_indices, page count, 0}.  Wave w runs items
+// [wave_items[w], wave_items[w + 1]).  part_acc: [slots][G][d] fp32, part_ml: [slots][G]
+// (running max in log2 units, sum).
 hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* item_out, int num_items, const void* q, const void* k_cache,
-                         const void* v_cache, float* part_acc, float2* part_ml, void* o, float* lse,
-                         hipStream_t stream);
+                         const int32_t* wave_items, int num_waves, const void* q,
+                         const void* k_cache, const void* v_cache, float* part_acc,
+                         float2* part_ml, void* o, float* lse, hipStream_t stream,
+                         const LaunchEvents& ev);
+// Decode wavefronts one CU holds at once.
+int decode_waves_per_cu(int d);
 
 }  // namespace ca
 
@@ -73,17 +91,19 @@ namespace ca {
 // units, sum).
 hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
                         const void* q, const void* k_cache, const void* v_cache, float* part_acc,
-                        float2* part_ml, void* o, float* lse, hipStream_t stream);
+                        float2* part_ml, void* o, float* lse, hipStream_t stream,
+                        const LaunchEvents& ev);
 int chunk_cols_per_block();
 
-// One launch combining every split: decode merges[j] = {seq, kv head, first slot, count}
+// One launch combining every split: decode merges[j] = {row, kv head, first slot, count}
 // (partials [slot][G][d]); chunk groups: two int4 {seq, kv head, first column, first slot},
-// {splits, 0, 0, 0} (partials [slot][chunk_cols_per_block()][d]).  Running maxima are in log2
-// units.  One wavefront per output (row, q head).
+// {splits, first row of the sequence, rows of the sequence, 0} (partials
+// [slot][chunk_cols_per_block()][d]).  Running maxima are in log2 units.  16 lanes per output
+// (row, q head).
 hipError_t launch_merge(const DevPlan& p, const Shape& sh, const int4* dec_merges, int num_dec,
                         const float* dec_acc, const float2* dec_ml, const int4* chunk_groups,
                         int num_chunk, const float* chunk_acc, const float2* chunk_ml, void* o,
-                        float* lse, hipStream_t stream);
+                        float* lse, hipStream_t stream, const LaunchEvents& ev);
 // Longest key range one chunk workgroup may cover (its page ids are staged in LDS).
 int chunk_max_split_keys();
 }  // namespace ca

@@ -8,9 +8,10 @@
 // this build parallelises one row over many keys; see the causal attention of
 // pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文", for what is merged.)
 //
-// One wavefront per output (row, q head): lane k reads split k's (m, l) (at most 64 splits per
-// wave step), the wave reduces M and the weighted sum, then each lane accumulates its output
-// dimensions over the splits with independent, unrolled loads.
+// Sixteen lanes per output column (row, q head), four columns per wavefront; a lane owns d / 16
+// consecutive output dimensions.  Every lane walks the column's splits itself (the (m, l) pairs
+// are the same few bytes for the 16 lanes), so there is no cross-lane traffic at all, and the
+// partial rows are read with 16-byte loads, several splits in flight at once.
 
 #include <hip/hip_runtime.h>
 
@@ -22,83 +23,85 @@
 namespace ca {
 namespace {
 
+constexpr int kLanes = 16;  // lanes per column
+
 template <int D>
-__device__ __forceinline__ void combine(const float2* __restrict__ ml_base, int64_t ml_stride,
-                                        const float* __restrict__ acc_base, int64_t acc_stride,
-                                        int nsplit, int lane, uint16_t* __restrict__ out,
+__device__ __forceinline__ void combine(const float2* __restrict__ ml, int64_t ml_stride,
+                                        const float* __restrict__ acc, int64_t acc_stride,
+                                        int nsplit, int sub, uint16_t* __restrict__ out,
                                         float* __restrict__ lse_out) {
+    constexpr int E = D / kLanes;  // dims per lane: 8 or 4
     float mx = -INFINITY;
-    for (int k = lane; k < nsplit; k += 64) {
-        const float2 ml = ml_base[k * ml_stride];
-        if (ml.y > 0.0f) mx = fmaxf(mx, ml.x);
+    for (int k = 0; k < nsplit; ++k) {
+        const float2 v = ml[k * ml_stride];
+        if (v.y > 0.0f) mx = fmaxf(mx, v.x);
     }
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o_, 64));
     float L = 0.0f;
-    float a[D / 64] = {};
-    for (int k0 = 0; k0 < nsplit; k0 += 64) {
-        float wk = 0.0f;
-        if (k0 + lane < nsplit) {
-            const float2 ml = ml_base[(k0 + lane) * ml_stride];
-            if (ml.y > 0.0f) {
-                wk = exp2_fast(ml.x - mx);
-                L += wk * ml.y;
-            }
-        }
-        const int n = nsplit - k0 < 64 ? nsplit - k0 : 64;
-        const float* base = acc_base + k0 * acc_stride + lane;
-#pragma unroll 8
-        for (int k = 0; k < n; ++k) {
-            const float wgt = __shfl(wk, k, 64);
+    float a[E] = {};
+    const float* base = acc + sub * E;
+#pragma unroll 4
+    for (int k = 0; k < nsplit; ++k) {
+        const float2 v = ml[k * ml_stride];
+        const float w = v.y > 0.0f ? exp2_fast(v.x - mx) : 0.0f;
+        L += w * v.y;
+        const float* src = base + k * acc_stride;
 #pragma unroll
-            for (int e = 0; e < D / 64; ++e) a[e] += wgt * base[k * acc_stride + 64 * e];
+        for (int e = 0; e < E; e += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(src + e);
+            a[e] += w * x.x;
+            a[e + 1] += w * x.y;
+            a[e + 2] += w * x.z;
+            a[e + 3] += w * x.w;
         }
     }
-#pragma unroll
-    for (int o_ = 32; o_ >= 1; o_ >>= 1) L += __shfl_xor(L, o_, 64);
     const float inv = 1.0f / L;
+    uint32_t packed[E / 2];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = f2bf(a[e] * inv);
-    if (lse_out && lane == 0) *lse_out = (mx + __log2f(L)) * 0.69314718055994531f;
+    for (int e = 0; e < E; e += 2)
+        packed[e / 2] = f2bf(a[e] * inv) | (static_cast<uint32_t>(f2bf(a[e + 1] * inv)) << 16);
+    if constexpr (E == 8) {
+        *reinterpret_cast<uint4*>(out + sub * E) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    } else {
+        *reinterpret_cast<uint2*>(out + sub * E) = make_uint2(packed[0], packed[1]);
+    }
+    if (lse_out && sub == 0) *lse_out = (mx + __log2f(L)) * 0.69314718055994531f;
 }
 
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(
-    DevPlan p, int hq, int hkv, int cols, const int4* __restrict__ dec_merges, int num_dec,
+    int hq, int hkv, int cols, const int4* __restrict__ dec_merges, int num_dec,
     const float* __restrict__ dec_acc, const float2* __restrict__ dec_ml,
     const int4* __restrict__ chunk_groups, int num_chunk, const float* __restrict__ chunk_acc,
     const float2* __restrict__ chunk_ml, uint16_t* __restrict__ o, float* __restrict__ lse) {
     const int G = hq / hkv;
-    const int lane = threadIdx.x & 63;
-    int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int dec_waves = num_dec * G;
-    if (wid < dec_waves) {
-        // decode: wave = (merge, q head c of the group); partials [slot][G][D]
-        const int4 mg = dec_merges[wid / G];
-        const int c = wid - (wid / G) * G;
-        const int row = p.qo_indptr[mg.x];
-        const int64_t orow = static_cast<int64_t>(row) * hq + mg.y * G + c;
+    const int sub = threadIdx.x & (kLanes - 1);
+    int col = (blockIdx.x * 256 + threadIdx.x) / kLanes;
+    const int dec_cols = num_dec * G;
+    if (col < dec_cols) {
+        // decode: column = (merge, q head c of the group); partials [slot][G][D]
+        const int4 mg = dec_merges[col / G];
+        const int c = col - (col / G) * G;
+        const int64_t orow = static_cast<int64_t>(mg.x) * hq + mg.y * G + c;
         combine<D>(dec_ml + static_cast<int64_t>(mg.z) * G + c, G,
                    dec_acc + (static_cast<int64_t>(mg.z) * G + c) * D, static_cast<int64_t>(G) * D,
-                   mg.w, lane, o + orow * D, lse ? lse + orow : nullptr);
+                   mg.w, sub, o + orow * D, lse ? lse + orow : nullptr);
         return;
     }
-    wid -= dec_waves;
-    if (wid >= num_chunk * cols) return;
-    // chunk: wave = (column block, column); partials [slot][cols][D]
-    const int grp = wid / cols, wc = wid - grp * cols;
+    col -= dec_cols;
+    if (col >= num_chunk * cols) return;
+    // chunk: column = (column block, column); partials [slot][cols][D]
+    const int grp = col / cols, wc = col - grp * cols;
     const int4 g0 = chunk_groups[2 * grp];
-    const int nsplit = chunk_groups[2 * grp + 1].x;
-    const int s = g0.x, g = g0.y, cb = g0.z, first = g0.w;
-    const int q0 = p.qo_indptr[s];
-    const int q_len = p.qo_indptr[s + 1] - q0;
-    const int col = cb + wc;
-    if (col >= q_len * G) return;
-    const int row = col / G, j = col - (col / G) * G;
+    const int4 g1 = chunk_groups[2 * grp + 1];
+    const int g = g0.y, cb = g0.z, first = g0.w;
+    const int nsplit = g1.x, q0 = g1.y, q_len = g1.z;
+    const int qc = cb + wc;  // (row, head) column inside the sequence's chunk
+    if (qc >= q_len * G) return;
+    const int row = qc / G, j = qc - (qc / G) * G;
     const int64_t orow = static_cast<int64_t>(q0 + row) * hq + g * G + j;
     combine<D>(chunk_ml + static_cast<int64_t>(first) * cols + wc, cols,
                chunk_acc + (static_cast<int64_t>(first) * cols + wc) * D, static_cast<int64_t>(cols) * D,
-               nsplit, lane, o + orow * D, lse ? lse + orow : nullptr);
+               nsplit, sub, o + orow * D, lse ? lse + orow : nullptr);
 }
 
 }  // namespace
@@ -106,18 +109,20 @@ __global__ void __launch_bounds__(256) merge_kernel(
 hipError_t launch_merge(const DevPlan& p, const Shape& sh, const int4* dec_merges, int num_dec,
                         const float* dec_acc, const float2* dec_ml, const int4* chunk_groups,
                         int num_chunk, const float* chunk_acc, const float2* chunk_ml, void* o,
-                        float* lse, hipStream_t stream) {
+                        float* lse, hipStream_t stream, const LaunchEvents& ev) {
+    (void)p;
     const int G = sh.hq / sh.hkv;
     const int cols = chunk_cols_per_block();
-    const int64_t waves = static_cast<int64_t>(num_dec) * G + static_cast<int64_t>(num_chunk) * cols;
-    if (waves <= 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+    const int64_t columns = static_cast<int64_t>(num_dec) * G + static_cast<int64_t>(num_chunk) * cols;
+    if (columns <= 0) return hipSuccess;
+    const int64_t per_block = 256 / kLanes;
+    const dim3 grid(static_cast<unsigned>((columns + per_block - 1) / per_block)), block(256);
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p, sh.hq, sh.hkv, cols, dec_merges,
+        hipExtLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, ev.start, ev.stop, 0, sh.hq, sh.hkv, cols, dec_merges,
                            num_dec, dec_acc, dec_ml, chunk_groups, num_chunk, chunk_acc, chunk_ml, oo, lse);
     else
-        hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, p, sh.hq, sh.hkv, cols, dec_merges,
+        hipExtLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, ev.start, ev.stop, 0, sh.hq, sh.hkv, cols, dec_merges,
                            num_dec, dec_acc, dec_ml, chunk_groups, num_chunk, chunk_acc, chunk_ml, oo, lse);
     return hipGetLastError();
 }

@@ -81,4 +81,24 @@ constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum over the four 16-lane rows of a wave for each column c = lane % 16; every lane gets
+// the result of lanes c, c + 16, c + 32, c + 48.  v_permlane16_swap exchanges rows 1 <-> 0 and
+// 3 <-> 2 of two copies, v_permlane32_swap rows {2, 3} <-> {0, 1} (checked on the device), so
+// max/sum of the two swapped copies reduces over row pairs, then over halves.  They are VALU
+// instructions: unlike ds_bpermute they leave the LDS/scalar-load counter alone, so a reduction
+// does not wait for page-id scalar loads still in flight.
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace ca

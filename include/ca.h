@@ -24,6 +24,8 @@
  *   - Errors: every call returns a ca_status; ca_last_error() gives a detail message for the
  *     calling thread.  Arguments are validated before anything is enqueued; on an error
  *     nothing is launched.
+ *   - Device buffers of q, k, v, the caches and o must be 16-byte aligned (the kernels move
+ *     16-byte vectors); lse 4-byte aligned.  A misaligned pointer is CA_ERR_INVALID_ARG.
  *
  * Paged KV cache layout (element type per ca_dtype, page size P, head dim d, Hkv kv heads):
  *   k_cache: [num_pool_pages][Hkv][P][d]   -- token-major inside a page
@@ -158,13 +160,14 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
                              int64_t num_pool_pages, void* o, float* lse, void* hip_stream);
 
 /*
- * Kernel timing (the tracing layer).  When enabled, every kernel the library enqueues is
- * bracketed by two HIP events recorded on the call's stream, so the figures are device time of
- * that launch alone.  ca_profile_read waits for the recorded events, copies up to `cap` records
+ * Kernel timing (the tracing layer).  When enabled, every launch the library makes carries a
+ * start/stop HIP event pair attached to the dispatch itself (hipExtLaunchKernel), so the
+ * figures are device time of that launch alone and timing adds no packet to the stream.  ca_profile_read waits for the recorded events, copies up to `cap` records
  * (oldest first), sets *count to the number copied and forgets every record read or not.
- * Names are static strings: "append_rope", "chunk", "decode", "merge" (both kinds of split
- * merge in one launch) and "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between
- * reads; later ones are not recorded.
+ * Names are static strings: "upload" (the step's metadata, host staging -> device), "append_rope",
+ * "chunk", "decode", "merge" (both kinds of split merge in one launch) and "generic" (the plain
+ * fp32 kernel with its merge).  At most 65536 launches are kept between reads; later ones are
+ * not recorded.
  */
 typedef struct {
     const char* kernel;
