@@ -6,11 +6,14 @@ ca_mixed_attention, on the Mistral-7B-shaped single-layer batch of the 512-token
 prefill P getting 300 tokens on 1200 cached and prefill Q getting 132 on 2048, pages permuted
 over a 64K-page pool.  Inputs are resident in HBM before the timed region starts.
 
-Prints ONE JSON line (rank 0).  `roofline` places the dominant kernel (the decode attention,
-HBM-bound) against the 8 TB/s HBM peak using algorithmic bytes and the kernel's own duration
-(HIP events the library records around its launches on the bench's stream); `mfma` does the same
-for the prefill-chunk kernel against the dense bf16 peak; `cpu_baseline` times the CPU oracle on
-the same step.
+Prints ONE JSON line.  `value` is tokens per second of whole steps over the timed region.
+`roofline` places the dominant kernel -- the attention launch, which runs the decode rows and
+the prefill-chunk rows side by side and is bound by reading the K/V pages -- against the 8 TB/s
+HBM peak, using algorithmic bytes and the launch's own duration (HIP events attached to that
+launch on the bench's stream, every step of the timed region).  `traffic` is the HBM bytes the
+counters measured for that launch (profiles/), used only while the kernel sources are unchanged.
+`parts` times the decode and chunk work as two separate launches in a second, untimed pass, for
+their own HBM and bf16 MFMA fractions.  `cpu_baseline` times the CPU oracle on the same step.
 """
 import argparse
 import json
@@ -25,10 +28,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_mistral7b_mixed_step.json")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def stored_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from chunked_prefill_paged_ca_amd.profiling import kernel_sources_sha256
+    if t.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(t["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(wl):
@@ -60,6 +77,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, copy this many MiB device to device once (a "
+                         "known-size reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -79,7 +100,6 @@ def main():
     wl = make_config(args.config)
     log(f"workload: {wl.name}")
     kc, vc = H.random_pool(wl, seed=wl.seed)
-    ctx = ca.create(0)
     desc = ca.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
     batch = ca.RequestBatch(wl.num_computed, wl.num_prompt_left, wl.block_tables, wl.token_budget,
                             wl.max_chunk, wl.page_size, wl.num_pool_pages)
@@ -98,36 +118,38 @@ def main():
                                  wl.head_dim, wl.page_size)
     stream = torch.cuda.current_stream()
 
-    def step():
-        plan = batch.plan()
-        ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages, stream=stream)
-        ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, lse, stream=stream)
+    def run_steps(ctx, n):
+        for _ in range(n):
+            plan = batch.plan()
+            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages, stream=stream)
+            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, lse, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    def kernel_means(recs):
+        per = {}
+        for name, ms in recs:
+            per.setdefault(name, []).append(ms)
+        return {k: float(np.mean(v)) for k, v in per.items()}
+
+    # ---- timed region: whole steps; the attention launch carries timing events ----
+    ctx = ca.create(0)
+    run_steps(ctx, args.warmup)
     torch.cuda.synchronize()
-    ctx.profile_read()  # drop anything recorded so far
-    ctx.profile_enable(True)
+    ctx.profile_read()
+    ctx.profile_enable(ca.PROFILE_ATTENTION)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    run_steps(ctx, args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ctx.profile_enable(False)
-    recs = ctx.profile_read()
-    per = {}
-    for name, ms in recs:
-        per.setdefault(name, []).append(ms)
-    kern_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    attn_ms = kernel_means(ctx.profile_read())["attention"]
+    ctx.close()
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
-    attn_ms = sum(kern_ms.get(k, 0.0) for k in ("chunk", "decode", "merge", "generic"))
 
-    # dominant kernel: the decode split-KV kernel (HBM-bound); the chunk kernel is MFMA-bound
-    dec_ms = kern_ms.get("decode", kern_ms.get("generic", float("nan")))
-    achieved = dec_w.bytes / (dec_ms * 1e-3) / 1e9
-    chunk_tflops = chk_w.flops / (kern_ms["chunk"] * 1e-3) / 1e12 if "chunk" in kern_ms else None
+    attn_bytes = dec_w.bytes + chk_w.bytes
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = stored_traffic()
     out = {
         "metric": "mixed chunked-prefill+decode attn tokens/s; % HBM peak and % MFMA peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -136,20 +158,51 @@ def main():
         "config": {"workload": wl.name, "tokens_per_step": T, "decodes": nd,
                    "token_budget": wl.token_budget, "page_size": wl.page_size,
                    "pool_pages": wl.num_pool_pages, "step": "plan + append_kv_rope + mixed_attention"},
-        "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
-        "attention_kernels_ms": round(attn_ms, 5),
-        "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": int(dec_w.bytes)},
-        "mfma": {"kernel": "chunk", "alg_flops_per_launch": int(chk_w.flops),
-                 "achieved_tflops": None if chunk_tflops is None else round(chunk_tflops, 2),
-                 "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": None if chunk_tflops is None else round(chunk_tflops / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "attention (decode + chunk rows, one launch)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": int(attn_bytes),
+                     "launch_ms": round(attn_ms, 5)},
     }
+
+    # ---- second pass (not timed for `value`): decode and chunk as separate launches ----
+    if not args.no_parts:
+        os.environ["CA_SPLIT_ATTENTION"] = "1"
+        ctx2 = ca.create(0)
+        del os.environ["CA_SPLIT_ATTENTION"]
+        run_steps(ctx2, args.warmup)
+        torch.cuda.synchronize()
+        ctx2.profile_read()
+        ctx2.profile_enable(True)
+        run_steps(ctx2, args.steps)
+        torch.cuda.synchronize()
+        ctx2.profile_enable(False)
+        km = kernel_means(ctx2.profile_read())
+        ctx2.close()
+        parts = {"kernel_ms": {k: round(v, 5) for k, v in km.items()}}
+        if "decode" in km:
+            bw = dec_w.bytes / (km["decode"] * 1e-3) / 1e9
+            parts["decode"] = {"bound": "hbm", "achieved": round(bw, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(bw / HBM_PEAK_GBS, 4),
+                               "alg_bytes_per_launch": int(dec_w.bytes)}
+        if "chunk" in km:
+            tf = chk_w.flops / (km["chunk"] * 1e-3) / 1e12
+            parts["chunk"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                              "alg_flops_per_launch": int(chk_w.flops)}
+        out["parts"] = parts
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step ...")
         out["cpu_baseline"] = cpu_baseline(wl)
-    ctx.close()
     print(json.dumps(out), flush=True)
 
 

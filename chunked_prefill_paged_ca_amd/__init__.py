@@ -3,5 +3,6 @@
 The library is libca.so (C ABI in include/ca.h); `binding` marshals arguments to it with ctypes.
 `workload` draws seeded synthetic inputs and `accounting` counts algorithmic bytes and flops.
 """
-from .binding import (CaError, Context, Plan, RequestBatch, create, destroy, header_symbols, lib,  # noqa: F401
-                      make_desc, plan_batch)
+from .binding import (PROFILE_ALL, PROFILE_APPEND, PROFILE_ATTENTION, PROFILE_MERGE,  # noqa: F401
+                      PROFILE_UPLOAD, CaError, Context, Plan, RequestBatch, create, destroy,
+                      header_symbols, lib, make_desc, plan_batch)

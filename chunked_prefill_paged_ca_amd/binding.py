@@ -57,6 +57,9 @@ class CaProfileRecord(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
 
+PROFILE_ALL, PROFILE_UPLOAD, PROFILE_APPEND, PROFILE_ATTENTION, PROFILE_MERGE = 1, 2, 4, 8, 16
+
+
 class CaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: status {status} ({status_string(status)}): {detail}")
@@ -273,8 +276,10 @@ class Context:
         except Exception:
             pass
 
-    def profile_enable(self, enable: bool = True):
-        _check(lib().ca_profile_enable(self.h, 1 if enable else 0), "ca_profile_enable")
+    def profile_enable(self, enable=True):
+        """True / False, or an OR of the PROFILE_* flags (time only those launches)."""
+        flags = PROFILE_ALL if enable is True else (0 if enable is False else int(enable))
+        _check(lib().ca_profile_enable(self.h, flags), "ca_profile_enable")
 
     def profile_read(self, cap: int = 65536):
         """[(kernel name, ms)] of the launches since the last read (waits for their events)."""

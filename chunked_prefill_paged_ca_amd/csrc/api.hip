@@ -175,6 +175,7 @@ struct DevWork {
     const int4* chunk_items = nullptr;   // two int4 per workgroup
     const int4* chunk_groups = nullptr;  // two int4 per multi-split row block
     int32_t num_dec_items = 0, num_dec_waves = 0, num_merges = 0, num_slots = 0;
+    int32_t dec_wgs = 0;  // decode workgroups of the attention launch
     int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0;
 };
 
@@ -184,7 +185,7 @@ struct Profiler {
         const char* name;
         hipEvent_t a, b;
     };
-    bool on = false;
+    int mask = 0;  // CA_PROFILE_* kinds being timed (0: off)
     std::vector<Rec> pending;
     std::vector<hipEvent_t> pool;
     hipEvent_t get() {
@@ -216,8 +217,8 @@ struct Timed {
     const char* name;
     ca::LaunchEvents ev{};
     bool committed = false;
-    Timed(Profiler& p, const char* n) : pf(p), name(n) {
-        if (pf.on && pf.pending.size() < 65536) {
+    Timed(Profiler& p, const char* n, int kind) : pf(p), name(n) {
+        if ((pf.mask & kind) && pf.pending.size() < 65536) {
             ev.start = pf.get();
             ev.stop = pf.get();
             if (!ev.start || !ev.stop) {
@@ -256,8 +257,9 @@ struct ca_ctx {
     DevBuf chk_acc_buf;     // fp32 [slots][cols][d]
     DevBuf chk_ml_buf;      // float2 [slots][cols]
     int32_t num_cus = 0;
-    int32_t dec_waves_per_cu[2] = {0, 0};  // d = 64, d = 128 (queried on first use)
-    int32_t dec_waves_override = 0;  // CA_DECODE_WAVES (decode shares), 0 = automatic
+    int32_t attn_wgs_per_cu[2] = {0, 0};  // d = 64, d = 128 (queried on first use)
+    int32_t dec_wgs_override = 0;  // CA_DECODE_WGS: decode workgroups of a mixed launch, 0 = auto
+    bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
 };
 
@@ -380,10 +382,13 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
     return CA_OK;
 }
 
-// Number of decode shares: the 32-key blocks of every (decode row, kv head), laid end to end, are
-// cut into this many equal runs, one per decode wavefront the device holds at once, so a single
-// round of waves streams the whole decode K/V with no tail.
-int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh) {
+// Decode workgroups of the attention launch and decode shares.  The 32-key blocks of every
+// (decode row, kv head), laid end to end, are cut into one equal share per decode wavefront, so a
+// single round of waves streams the whole decode K/V with no tail.  Alone (no chunk rows, or the
+// two parts launched separately) decode takes every workgroup slot of the device; in a mixed
+// launch it takes `mixed_share` of them (rounded to whole XCD rounds of 8) and the chunk
+// workgroups run beside it.  CA_DECODE_WGS sets the count of a mixed launch instead.  Returns the share count; *wgs gets the decode workgroups.
+int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t* wgs) {
     int64_t blocks = 0;
     for (int32_t s = 0; s < plan->num_decodes; ++s) {
         const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
@@ -391,13 +396,25 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh) {
         blocks += (kv_len + 31) / 32;
     }
     blocks *= sh.hkv;
-    int64_t W = ctx->dec_waves_override;
-    if (W <= 0) {
-        int32_t& per_cu = ctx->dec_waves_per_cu[sh.d == 128 ? 1 : 0];
-        if (per_cu == 0) per_cu = ca::decode_waves_per_cu(sh.d);
-        W = static_cast<int64_t>(ctx->num_cus) * per_cu;
+    int32_t& per_cu = ctx->attn_wgs_per_cu[sh.d == 128 ? 1 : 0];
+    if (per_cu == 0) per_cu = ca::attention_wgs_per_cu(sh.d);
+    const int32_t slots = ctx->num_cus * per_cu;
+    const bool mixed = plan->num_seqs > plan->num_decodes && !ctx->split_attention;
+    int32_t n = slots;
+    if (mixed) {
+        // measured on the 256-CU part (Mistral-7B, Yi-34B and LLaMA2-70B mixed steps): decode
+        // keeps its HBM rate on 3/4 of the CUs; fewer starve it, more starve the chunk work
+        constexpr double mixed_share = 0.75;
+        n = ctx->dec_wgs_override > 0 ? ctx->dec_wgs_override : static_cast<int32_t>(slots * mixed_share);
+        n = (n + 7) / 8 * 8;
+        if (n > slots) n = slots;
     }
-    return static_cast<int32_t>(W < blocks ? W : blocks);
+    const int64_t W = static_cast<int64_t>(n) * ca::attention_decode_waves_per_wg();
+    const int32_t shares = static_cast<int32_t>(W < blocks ? W : blocks);
+    const int32_t per_wg = ca::attention_decode_waves_per_wg();
+    *wgs = shares > 0 ? (shares + per_wg - 1) / per_wg : 0;
+    if (mixed) *wgs = (*wgs + 7) / 8 * 8;  // keep the chunk workgroups' XCD order
+    return shares;
 }
 
 // Keys per chunk split: a row block whose visible keys exceed this is cut into several
@@ -470,9 +487,10 @@ int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
 ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
                   hipStream_t stream) {
     const int G = sh.hq / sh.hkv;
+    int32_t dec_wgs = 0;
     const bool mfma = sh.dtype == CA_BF16 && G <= 16;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
-                mfma ? decode_shares(ctx, plan, sh) : -1,
+                mfma ? decode_shares(ctx, plan, sh, &dec_wgs) : -1,
                 mfma ? chunk_split_keys(plan, sh, ctx->csplit_override) : -1, sh.theta};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
     ca_status st = validate_plan_arrays(plan, pool);
@@ -607,7 +625,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     std::memcpy(h + off_citem, citems.data(), citems.size() * sizeof(int4));
     std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
     {
-        Timed t(ctx->prof, "upload");
+        Timed t(ctx->prof, "upload", CA_PROFILE_UPLOAD);
         e = ctx->staging.upload(slot, ctx->meta_buf.ptr, bytes, stream, t.ev);
         if (e == hipSuccess) t.commit();
     }
@@ -636,6 +654,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     w.chunk_groups = reinterpret_cast<const int4*>(d + off_group);
     w.num_dec_items = static_cast<int32_t>(n_items);
     w.num_dec_waves = wave_items.empty() ? 0 : static_cast<int32_t>(wave_items.size()) - 1;
+    w.dec_wgs = dec_wgs;
     w.num_merges = static_cast<int32_t>(n_merges);
     w.num_slots = slots;
     w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
@@ -670,7 +689,8 @@ ca_status ca_create(int device, ca_ctx** out) {
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     ca_ctx* ctx = new ca_ctx();
     ctx->device = device;
-    if (const char* env = std::getenv("CA_DECODE_WAVES")) ctx->dec_waves_override = std::atoi(env);
+    if (const char* env = std::getenv("CA_DECODE_WGS")) ctx->dec_wgs_override = std::atoi(env);
+    if (const char* env = std::getenv("CA_SPLIT_ATTENTION")) ctx->split_attention = std::atoi(env) != 0;
     e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess || ctx->num_cus <= 0) {
         delete ctx;
@@ -731,7 +751,7 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
     if (st != CA_OK) return st;
     hipError_t e;
     {
-        Timed t(ctx->prof, "append_rope");
+        Timed t(ctx->prof, "append_rope", CA_PROFILE_APPEND);
         e = ca::launch_append_rope(ctx->dplan, sh, ctx->inv_freq, q_in, q_out, k_new, v_new, k_cache,
                                    v_cache, stream, t.ev);
         if (e == hipSuccess) t.commit();
@@ -774,24 +794,36 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         float* dacc = static_cast<float*>(ctx->dec_acc_buf.ptr);
         float2* dml = static_cast<float2*>(ctx->dec_ml_buf.ptr);
         hipError_t e = hipSuccess;
-        // Chunk workgroups first (the long ones), then the decode splits.  Running them on two
-        // streams was measured and rejected: decode waves occupy every CU, the chunk
-        // workgroups (8 waves, 72 KB of LDS) only start where a CU drains completely, and the
-        // fork/join events stalled the host between steps.
-        if (w.num_chunk_items > 0) {
-            Timed t(ctx->prof, "chunk");
-            e = ca::launch_chunk(ctx->dplan, sh, w.chunk_items, w.num_chunk_items, q, k_cache,
-                                 v_cache, cacc, cml, o, lse, stream, t.ev);
+        // One launch holds both kinds of work (attn_mixed.hip): decode workgroups stream the
+        // decode K/V on part of the CUs while chunk workgroups run on the rest.  (Two launches on
+        // two streams were measured and rejected: decode waves occupied every CU, the chunk
+        // workgroups only started where a CU drained completely, and the fork/join events
+        // stalled the host between steps.)  CA_SPLIT_ATTENTION=1 runs the parts as two launches
+        // of the same kernel, each over the whole device, to time them separately.
+        if (!ctx->split_attention) {
+            Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION);
+            e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_items, w.dec_wave_items,
+                                     w.num_dec_waves, w.chunk_items, w.num_chunk_items, q, k_cache,
+                                     v_cache, dacc, dml, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
-        }
-        if (e == hipSuccess && w.num_dec_waves > 0) {
-            Timed t(ctx->prof, "decode");
-            e = ca::launch_decode(ctx->dplan, sh, w.dec_items, w.dec_wave_items, w.num_dec_waves, q,
-                                  k_cache, v_cache, dacc, dml, o, lse, stream, t.ev);
-            if (e == hipSuccess) t.commit();
+        } else {
+            if (w.num_chunk_items > 0) {
+                Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION);
+                e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_items, w.dec_wave_items, 0,
+                                         w.chunk_items, w.num_chunk_items, q, k_cache, v_cache,
+                                         dacc, dml, cacc, cml, o, lse, stream, t.ev);
+                if (e == hipSuccess) t.commit();
+            }
+            if (e == hipSuccess && w.num_dec_waves > 0) {
+                Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION);
+                e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_items, w.dec_wave_items,
+                                         w.num_dec_waves, w.chunk_items, 0, q, k_cache, v_cache,
+                                         dacc, dml, cacc, cml, o, lse, stream, t.ev);
+                if (e == hipSuccess) t.commit();
+            }
         }
         if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
-            Timed t(ctx->prof, "merge");
+            Timed t(ctx->prof, "merge", CA_PROFILE_MERGE);
             e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
                                  w.num_chunk_groups, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
@@ -805,7 +837,7 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
     if (e != hipSuccess) return device_error("partials allocation", e);
     {
-        Timed t(ctx->prof, "generic");
+        Timed t(ctx->prof, "generic", CA_PROFILE_ATTENTION);
         e = ca::launch_attention_generic(ctx->dplan, sh, 0, q, k_cache, v_cache, o, lse,
                                          static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream,
                                          t.ev);
@@ -818,7 +850,8 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
 ca_status ca_profile_enable(ca_ctx* ctx, int enable) {
     ca::clear_error();
     if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
-    ctx->prof.on = enable != 0;
+    if (enable < 0 || enable > 31) { ca::set_error("ca_profile_enable: unknown flags"); return CA_ERR_INVALID_ARG; }
+    ctx->prof.mask = (enable & CA_PROFILE_ALL) ? 0x1e : enable;
     return CA_OK;
 }
 

@@ -1,5 +1,6 @@
-// attn_chunk.hip -- causal paged attention for the prefill-chunk rows of a mixed step (bf16,
-// MFMA, K/V pages staged in LDS).  The merge of key splits is in merge.hip.
+// attn_chunk.h -- causal paged attention for the prefill-chunk rows of a mixed step (bf16,
+// MFMA, K/V pages staged in LDS): the per-workgroup work item, run by the attention kernel in
+// attn_mixed.hip.  The merge of key splits is in merge.hip.
 //
 // What it computes: pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文" --
 // the chunk's query at absolute position p attends to keys 0..p of its request: the history pages
@@ -22,6 +23,8 @@
 // Only blocks that cross a row's diagonal need the mask; keys past a column's position get
 // weight 0, and V slots past the sequence end are zeroed in LDS before they reach the MFMA.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,7 +33,7 @@
 #include "mfma.h"
 
 namespace ca {
-namespace {
+namespace chunk {
 
 constexpr int kWaves = 8;
 constexpr int kTiles = 2;  // 16-column MFMA tiles per wave -> 32 columns
@@ -91,8 +94,8 @@ __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __res
 // items: two int4 per item: {seq, kv head, first column (row * G + head), partial slot or -1},
 //                           {key begin, key end, 0, 0}   (seq -1: grid padding)
 template <int D>
-__global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
-    DevPlan p, const int4* __restrict__ items,
+__device__ __forceinline__ void chunk_item(
+    int item, DevPlan p, const int4* __restrict__ items,
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
@@ -106,8 +109,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, q = lane >> 4;
-    const int4 it0 = items[2 * blockIdx.x];
-    const int4 it1 = items[2 * blockIdx.x + 1];
+    const int4 it0 = items[2 * item];
+    const int4 it1 = items[2 * item + 1];
     const int s = it0.x, g = it0.y, cb = it0.z, slot = it0.w;
     const int kb = it1.x, ke = it1.y;
     if (s < 0) return;  // grid padding (uniform across the workgroup)
@@ -322,28 +325,5 @@ __global__ void __launch_bounds__(64 * kWaves, 1) chunk_kernel(
     }
 }
 
-}  // namespace
-
-int chunk_cols_per_block() { return kCols; }
-int chunk_max_split_keys() { return 16 * (kMaxItemPages - 2); }
-
-hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
-                        const void* q, const void* k_cache, const void* v_cache, float* part_acc,
-                        float2* part_ml, void* o, float* lse, hipStream_t stream,
-                        const LaunchEvents& ev) {
-    if (num_items <= 0) return hipSuccess;
-    const float scale_log2 = sh.scale * 1.4426950408889634f;
-    auto qq = static_cast<const uint16_t*>(q);
-    auto kc = static_cast<const uint16_t*>(k_cache);
-    auto vc = static_cast<const uint16_t*>(v_cache);
-    auto oo = static_cast<uint16_t*>(o);
-    if (sh.d == 128)
-        hipExtLaunchKernelGGL(chunk_kernel<128>, dim3(num_items), dim3(64 * kWaves), 0, stream, ev.start, ev.stop, 0, p, items,
-                           qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-    else
-        hipExtLaunchKernelGGL(chunk_kernel<64>, dim3(num_items), dim3(64 * kWaves), 0, stream, ev.start, ev.stop, 0, p, items,
-                           qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml, oo, lse);
-    return hipGetLastError();
-}
-
+}  // namespace chunk
 }  // namespace ca

@@ -1,4 +1,5 @@
-// attn_decode.hip -- split-KV paged attention for the decode rows of a mixed step (bf16, MFMA).
+// attn_decode.h -- split-KV paged attention for the decode rows of a mixed step (bf16, MFMA):
+// the per-wavefront work item, run by the attention kernel in attn_mixed.hip.
 // The log-sum-exp merge of the splits is in merge.hip.
 //
 // What it computes: pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文" --
@@ -21,6 +22,8 @@
 // An item shorter than the whole context writes fp32 partials (unnormalised o, running max, sum);
 // an item covering a whole (row, kv head) writes its normalised output directly.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -29,9 +32,7 @@
 #include "mfma.h"
 
 namespace ca {
-namespace {
-
-constexpr int kWavesPerBlock = 4;
+namespace decode {
 
 template <int D>
 struct Block {
@@ -206,60 +207,5 @@ __device__ __forceinline__ void decode_item(
     }
 }
 
-// One wavefront per share of the step's decode key blocks: wave w runs the items
-// [wave_items[w], wave_items[w + 1]) one after another.
-template <int D>
-__global__ void __launch_bounds__(64 * kWavesPerBlock, 2) decode_kernel(
-    const int4* __restrict__ items, const int32_t* __restrict__ wave_items, int num_waves,
-    const int32_t* __restrict__ page_indices, const uint16_t* __restrict__ qg,
-    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
-    float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
-    const int lane = threadIdx.x & 63;
-    // wave-uniform indices: everything derived from them (item records, page ids) lives in
-    // scalar registers and is read with scalar loads, which do not share the vector-load
-    // counter the K/V prefetch relies on
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    if (w >= num_waves) return;
-    const int i_end = wave_items[w + 1];
-    for (int i = wave_items[w]; i < i_end; ++i)
-        decode_item<D>(items[2 * i], items[2 * i + 1], page_indices, qg, k_cache, v_cache, hq, hkv,
-                       scale_log2, part_acc, part_ml, o, lse, lane);
-}
-
-}  // namespace
-
-hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* wave_items, int num_waves, const void* q,
-                         const void* k_cache, const void* v_cache, float* part_acc,
-                         float2* part_ml, void* o, float* lse, hipStream_t stream,
-                         const LaunchEvents& ev) {
-    if (num_waves <= 0) return hipSuccess;
-    const float scale_log2 = sh.scale * 1.4426950408889634f;
-    const dim3 grid((num_waves + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
-    auto qq = static_cast<const uint16_t*>(q);
-    auto kc = static_cast<const uint16_t*>(k_cache);
-    auto vc = static_cast<const uint16_t*>(v_cache);
-    auto oo = static_cast<uint16_t*>(o);
-    if (sh.d == 128)
-        hipExtLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, ev.start, ev.stop, 0, items, wave_items, num_waves,
-                           p.kv_page_indices, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml,
-                           oo, lse);
-    else
-        hipExtLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, ev.start, ev.stop, 0, items, wave_items, num_waves,
-                           p.kv_page_indices, qq, kc, vc, sh.hq, sh.hkv, scale_log2, part_acc, part_ml,
-                           oo, lse);
-    return hipGetLastError();
-}
-
-// Wavefronts of the decode kernel one CU holds at once (register-limited).
-int decode_waves_per_cu(int d) {
-    int blocks = 0;
-    const hipError_t e = d == 128
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<128>, 64 * kWavesPerBlock, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<64>, 64 * kWavesPerBlock, 0);
-    if (e != hipSuccess || blocks <= 0) return kWavesPerBlock;
-    return blocks * kWavesPerBlock;
-}
-
+}  // namespace decode
 }  // namespace ca

@@ -1,0 +1,100 @@
+// attn_mixed.hip -- one attention launch for a whole mixed step: decode rows and prefill-chunk
+// rows side by side.
+//
+// bowenzhou.top "Sarathi：让解码搭上 prefill 的顺风车", section "Decode-maximal batching", and
+// magicnetworld.com "分块预填充与 Stall-free 调度", section 一: a mixed batch pairs work that
+// is bound by memory traffic (decodes read their whole K/V history once) with work bound by
+// arithmetic (a prefill chunk reuses every K/V block for all its query rows), so the two kinds
+// of work can run on the chip at the same time instead of one after the other.
+//
+// The grid is [dec_wgs decode workgroups][chunk workgroups].  Workgroups are dispatched in index
+// order, so the decode workgroups (8 wavefronts each, every wave streaming its equal share of the
+// decode K/V blocks, attn_decode.h) start first and stay resident on dec_wgs CUs until their
+// shares are done; the chunk workgroups (attn_chunk.h) run on the remaining CUs from the start
+// and take over the decode CUs as those drain.  Decode reaches the HBM bandwidth on a fraction of
+// the CUs, so the chunk work fills CUs the decode stream does not need.  Either part may be
+// empty.
+
+#include <hip/hip_runtime.h>
+
+#include "attn_chunk.h"
+#include "attn_decode.h"
+#include "internal.h"
+
+namespace ca {
+namespace {
+
+constexpr int kThreads = 64 * chunk::kWaves;  // both kinds of workgroup: 8 wavefronts
+constexpr int kDecodeWaves = kThreads / 64;
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
+    DevPlan p, int dec_wgs, const int4* __restrict__ dec_items, const int32_t* __restrict__ wave_items,
+    int num_waves, const int4* __restrict__ chunk_items, const uint16_t* __restrict__ qg,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
+    float scale_log2, float* __restrict__ dec_acc, float2* __restrict__ dec_ml,
+    float* __restrict__ chunk_acc, float2* __restrict__ chunk_ml, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
+    if (static_cast<int>(blockIdx.x) < dec_wgs) {
+        // wave-uniform indices: everything derived from them (item records, page ids) lives in
+        // scalar registers and is read with scalar loads, which do not share the vector-load
+        // counter the K/V prefetch relies on
+        const int lane = threadIdx.x & 63;
+        const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + (threadIdx.x >> 6));
+        if (w >= num_waves) return;
+        const int i_end = wave_items[w + 1];
+        for (int i = wave_items[w]; i < i_end; ++i)
+            decode::decode_item<D>(dec_items[2 * i], dec_items[2 * i + 1], p.kv_page_indices, qg,
+                                   k_cache, v_cache, hq, hkv, scale_log2, dec_acc, dec_ml, o, lse,
+                                   lane);
+        return;
+    }
+    chunk::chunk_item<D>(blockIdx.x - dec_wgs, p, chunk_items, qg, k_cache, v_cache, hq, hkv,
+                         scale_log2, chunk_acc, chunk_ml, o, lse);
+}
+
+}  // namespace
+
+int chunk_cols_per_block() { return chunk::kCols; }
+int chunk_max_split_keys() { return 16 * (chunk::kMaxItemPages - 2); }
+int attention_decode_waves_per_wg() { return kDecodeWaves; }
+
+hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, const int4* dec_items,
+                            const int32_t* wave_items, int num_waves, const int4* chunk_items,
+                            int num_chunk_items, const void* q, const void* k_cache,
+                            const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
+                            float2* chunk_ml, void* o, float* lse, hipStream_t stream,
+                            const LaunchEvents& ev) {
+    if (num_waves <= 0) dec_wgs = 0;
+    if (dec_wgs * kDecodeWaves < num_waves) return hipErrorInvalidValue;
+    const int grid = dec_wgs + num_chunk_items;
+    if (grid <= 0) return hipSuccess;
+    const float scale_log2 = sh.scale * 1.4426950408889634f;
+    auto qq = static_cast<const uint16_t*>(q);
+    auto kc = static_cast<const uint16_t*>(k_cache);
+    auto vc = static_cast<const uint16_t*>(v_cache);
+    auto oo = static_cast<uint16_t*>(o);
+    if (sh.d == 128)
+        hipExtLaunchKernelGGL(mixed_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
+                              ev.stop, 0, p, dec_wgs, dec_items, wave_items, num_waves,
+                              chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              chunk_acc, chunk_ml, oo, lse);
+    else
+        hipExtLaunchKernelGGL(mixed_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
+                              ev.stop, 0, p, dec_wgs, dec_items, wave_items, num_waves,
+                              chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              chunk_acc, chunk_ml, oo, lse);
+    return hipGetLastError();
+}
+
+// Attention workgroups one CU holds at once (register-limited).
+int attention_wgs_per_cu(int d) {
+    int blocks = 0;
+    const hipError_t e = d == 128
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mixed_kernel<128>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mixed_kernel<64>, kThreads, 0);
+    if (e != hipSuccess || blocks <= 0) return 1;
+    return blocks;
+}
+
+}  // namespace ca

@@ -67,33 +67,31 @@ hipError_t launch_attention_generic(const DevPlan& p, const Shape& sh, int row0,
 
 size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
 
-// MFMA split-KV decode (bf16, G <= 16).  items: two int4 per item, {kv head, key begin, key
-// end, partial slot or -1 (the item covers the whole row: output written directly)}, {row, offset
-// of the row's page ids in kv_page_indices, page count, 0}.  Wave w runs items
-// [wave_items[w], wave_items[w + 1]).  part_acc: [slots][G][d] fp32, part_ml: [slots][G]
-// (running max in log2 units, sum).
-hipError_t launch_decode(const DevPlan& p, const Shape& sh, const int4* items,
-                         const int32_t* wave_items, int num_waves, const void* q,
-                         const void* k_cache, const void* v_cache, float* part_acc,
-                         float2* part_ml, void* o, float* lse, hipStream_t stream,
-                         const LaunchEvents& ev);
-// Decode wavefronts one CU holds at once.
-int decode_waves_per_cu(int d);
-
 }  // namespace ca
 
 namespace ca {
-// MFMA prefill-chunk attention (bf16, G <= 16).  A query column is one (row, q head) pair of a kv
-// head's group, numbered row * G + head.  items: two int4 per workgroup,
-// {seq, kv head, first column, partial slot or -1}, {key begin, key end, 0, 0} (seq -1: padding);
-// groups: two int4 per multi-split column block, {seq, kv head, first column, first slot},
-// {splits}.  Partials: [slot][chunk_cols_per_block()][d] fp32 and [slot][cols] (max in log2
-// units, sum).
-hipError_t launch_chunk(const DevPlan& p, const Shape& sh, const int4* items, int num_items,
-                        const void* q, const void* k_cache, const void* v_cache, float* part_acc,
-                        float2* part_ml, void* o, float* lse, hipStream_t stream,
-                        const LaunchEvents& ev);
+// MFMA attention for a whole mixed step (bf16, G <= 16), one launch: the grid is dec_wgs decode
+// workgroups followed by num_chunk_items chunk workgroups (attn_mixed.hip).
+//   decode: dec_items holds two int4 per item, {kv head, key begin, key end, partial slot or -1
+//     (the item covers the whole row: output written directly)}, {row, offset of the row's page
+//     ids in kv_page_indices, page count, 0}; decode wave w (of dec_wgs *
+//     attention_decode_waves_per_wg()) runs items [wave_items[w], wave_items[w + 1]) for
+//     w < num_waves.  Partials: dec_acc [slots][G][d] fp32, dec_ml [slots][G] (max in log2
+//     units, sum).
+//   chunk: a query column is one (row, q head) pair of a kv head's group, numbered row * G +
+//     head.  chunk_items: two int4 per workgroup, {seq, kv head, first column, partial slot or
+//     -1}, {key begin, key end, 0, 0} (seq -1: padding).  Partials: chunk_acc
+//     [slot][chunk_cols_per_block()][d] fp32 and chunk_ml [slot][cols].
+hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, const int4* dec_items,
+                            const int32_t* wave_items, int num_waves, const int4* chunk_items,
+                            int num_chunk_items, const void* q, const void* k_cache,
+                            const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
+                            float2* chunk_ml, void* o, float* lse, hipStream_t stream,
+                            const LaunchEvents& ev);
 int chunk_cols_per_block();
+int attention_decode_waves_per_wg();
+// Attention workgroups one CU holds at once.
+int attention_wgs_per_cu(int d);
 
 // One launch combining every split: decode merges[j] = {row, kv head, first slot, count}
 // (partials [slot][G][d]); chunk groups: two int4 {seq, kv head, first column, first slot},

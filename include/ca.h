@@ -152,8 +152,8 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
  *   lse[t,h] = log sum_{j<=p} exp(s_j)  (natural log; pass NULL to skip)
  * ([SS] "分块不等于截断上下文"; decodes are the case p = kv_len - 1.)
  *   q: [T, Hq, d] (already rotated), o: [T, Hq, d], lse: [T, Hq] fp32 or NULL.
- * Decode rows use a split-KV kernel whose partials are merged by log-sum-exp weights; chunk
- * rows use an LDS-staged bf16 MFMA kernel (fp32 storage uses a plain fp32 kernel).
+ * bf16 with Hq/Hkv <= 16: one launch runs decode rows (split-KV, partials merged by log-sum-exp
+ * weights) beside chunk rows (LDS-staged bf16 MFMA); fp32 storage uses a plain fp32 kernel.
  */
 ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
                              const void* q, const void* k_cache, const void* v_cache,
@@ -165,14 +165,27 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
  * figures are device time of that launch alone and timing adds no packet to the stream.  ca_profile_read waits for the recorded events, copies up to `cap` records
  * (oldest first), sets *count to the number copied and forgets every record read or not.
  * Names are static strings: "upload" (the step's metadata, host staging -> device), "append_rope",
- * "chunk", "decode", "merge" (both kinds of split merge in one launch) and "generic" (the plain
- * fp32 kernel with its merge).  At most 65536 launches are kept between reads; later ones are
+ * "attention" (decode and prefill-chunk rows in one launch; with CA_SPLIT_ATTENTION=1 in the
+ * environment at ca_create they are two launches named "chunk" and "decode"), "merge" (both
+ * kinds of split merge in one launch) and "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between reads; later ones are
  * not recorded.
  */
 typedef struct {
     const char* kernel;
     float ms;
 } ca_profile_record;
+
+/* ca_profile_enable's `enable`: 0 = off, CA_PROFILE_ALL = every launch, or an OR of the
+ * single-kind flags to time only those launches (each timed launch costs a few microseconds of
+ * device time, so a throughput run times only what it reports).  ATTENTION covers "attention",
+ * "chunk", "decode" and "generic". */
+enum {
+    CA_PROFILE_ALL = 1,
+    CA_PROFILE_UPLOAD = 2,
+    CA_PROFILE_APPEND = 4,
+    CA_PROFILE_ATTENTION = 8,
+    CA_PROFILE_MERGE = 16
+};
 
 ca_status ca_profile_enable(ca_ctx* ctx, int enable);
 ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int32_t* count);

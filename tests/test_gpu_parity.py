@@ -265,7 +265,7 @@ def test_profile_records_every_kernel(env):
     recs = ctx.profile_read()
     names = [n for n, _ in recs]
     _log(f"[profile] {recs}")
-    assert names[:2] == ["upload", "append_rope"] and "decode" in names and "chunk" in names
+    assert names[:2] == ["upload", "append_rope"] and "attention" in names and "merge" in names
     assert names.count("upload") == 1  # the attention call reuses the step's metadata
     assert all(ms > 0 for _, ms in recs)
     assert ctx.profile_read() == []
