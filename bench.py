@@ -142,7 +142,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ctx.profile_enable(False)
-    attn_ms = kernel_means(ctx.profile_read())["attention"]
+    km0 = kernel_means(ctx.profile_read())
+    attn_ms = km0["attention"] if "attention" in km0 else km0["generic"]  # fp32 storage: plain kernel
     ctx.close()
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
