@@ -11,7 +11,7 @@
 // Sixteen lanes per output column (row, q head), four columns per wavefront; a lane owns d / 16
 // consecutive output dimensions.  Every lane walks the column's splits itself (the (m, l) pairs
 // are the same few bytes for the 16 lanes), so there is no cross-lane traffic at all, and the
-// partial rows are read with 16-byte loads, several splits in flight at once.
+// partial rows are read with 16-byte loads, eight splits in flight at once.
 
 #include <hip/hip_runtime.h>
 
@@ -31,27 +31,45 @@ __device__ __forceinline__ void combine(const float2* __restrict__ ml, int64_t m
                                         int nsplit, int sub, uint16_t* __restrict__ out,
                                         float* __restrict__ lse_out) {
     constexpr int E = D / kLanes;  // dims per lane: 8 or 4
-    float mx = -INFINITY;
-    for (int k = 0; k < nsplit; ++k) {
-        const float2 v = ml[k * ml_stride];
-        if (v.y > 0.0f) mx = fmaxf(mx, v.x);
-    }
-    float L = 0.0f;
+    constexpr int C = 8;           // splits whose loads are in flight together
+    // One pass over the splits in chunks of C: every load of a chunk is issued before any of its
+    // values is used (indices past the end are clamped and weighted 0), so a chunk costs one
+    // memory round trip; the running max and sums are rescaled when a chunk raises the max.
+    float M = -INFINITY, L = 0.0f;
     float a[E] = {};
     const float* base = acc + sub * E;
-#pragma unroll 4
-    for (int k = 0; k < nsplit; ++k) {
-        const float2 v = ml[k * ml_stride];
-        const float w = v.y > 0.0f ? exp2_fast(v.x - mx) : 0.0f;
-        L += w * v.y;
-        const float* src = base + k * acc_stride;
+    for (int k0 = 0; k0 < nsplit; k0 += C) {
+        float2 v[C];
+        float4 x[C][E / 4];
 #pragma unroll
-        for (int e = 0; e < E; e += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(src + e);
-            a[e] += w * x.x;
-            a[e + 1] += w * x.y;
-            a[e + 2] += w * x.z;
-            a[e + 3] += w * x.w;
+        for (int j = 0; j < C; ++j) {
+            const int k = k0 + j < nsplit ? k0 + j : nsplit - 1;
+            v[j] = ml[k * ml_stride];
+            if (k0 + j >= nsplit) v[j].y = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) x[j][e / 4] = *reinterpret_cast<const float4*>(base + k * acc_stride + e);
+        }
+        float cm = M;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            if (v[j].y > 0.0f) cm = fmaxf(cm, v[j].x);
+        if (cm == -INFINITY) continue;  // no split of this chunk saw a key
+        const float r = exp2_fast(M - cm);  // 0 while M is still -inf
+        L *= r;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] *= r;
+        M = cm;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const float w = v[j].y > 0.0f ? exp2_fast(v[j].x - M) : 0.0f;
+            L += w * v[j].y;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                a[e] += w * x[j][e / 4].x;
+                a[e + 1] += w * x[j][e / 4].y;
+                a[e + 2] += w * x[j][e / 4].z;
+                a[e + 3] += w * x[j][e / 4].w;
+            }
         }
     }
     const float inv = 1.0f / L;
@@ -64,7 +82,7 @@ __device__ __forceinline__ void combine(const float2* __restrict__ ml, int64_t m
     } else {
         *reinterpret_cast<uint2*>(out + sub * E) = make_uint2(packed[0], packed[1]);
     }
-    if (lse_out && sub == 0) *lse_out = (mx + __log2f(L)) * 0.69314718055994531f;
+    if (lse_out && sub == 0) *lse_out = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 template <int D>

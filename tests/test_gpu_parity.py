@@ -200,6 +200,42 @@ def test_sweep_chunked_vs_one_shot(env, c):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
+@pytest.mark.parametrize("mode", ["split", "few-decode-wgs", "decode-only"])
+def test_attention_launch_layouts(env, mode):
+    """The Mistral-7B step through the other layouts of the attention launch: decode and chunk
+    rows as two launches (CA_SPLIT_ATTENTION=1), a mixed launch with only 8 decode workgroups (so
+    every decode wave runs many items, crossing many (row, kv head) boundaries), and a step with
+    decodes only (no chunk workgroups at all)."""
+    import os
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import Workload, make_config
+    _, oracle = env
+    setting = {"split": ("CA_SPLIT_ATTENTION", "1"), "few-decode-wgs": ("CA_DECODE_WGS", "8"),
+               "decode-only": None}[mode]
+    if setting:
+        os.environ[setting[0]] = setting[1]
+    try:
+        ctx = ca.create(0)
+    finally:
+        if setting:
+            del os.environ[setting[0]]
+    try:
+        wl = make_config(2)
+        if mode == "decode-only":
+            keep = [r for r in range(wl.n) if wl.is_decode(r)]
+            uids = np.arange(wl.n) if wl.uids is None else wl.uids
+            wl = Workload(**{**wl.__dict__, "num_computed": wl.num_computed[keep],
+                             "num_prompt_left": wl.num_prompt_left[keep],
+                             "block_tables": [wl.block_tables[r] for r in keep],
+                             "stream_len": wl.stream_len[keep], "uids": uids[keep]})
+        res, _, _ = run_and_check(ctx, oracle, wl, label=f"layout-{mode}")
+        p = res[0][0]
+        assert p["num_decodes"] == 80
+        assert (p["num_seqs"] == 80) == (mode == "decode-only")
+    finally:
+        ctx.close()
+
+
 def test_edge_cases(env):
     """kv_len 1 decode, a decode filling its last page exactly, 1-row chunks, a chunk starting
     on a page boundary, GQA group 8 with d = 64, and page-permutation invariance."""
