@@ -118,10 +118,18 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
             }
             if (u < units) {
                 const int h = u / per_head;
-                T* dst = h < hq ? q_out + (static_cast<int64_t>(t) * hq + h) * d
-                                : k_cache + ((static_cast<int64_t>(page) * hkv + (h - hq)) * P + slot) * d;
-                store16(dst + i0[j], ra);
-                store16(dst + i0[j] + half, rb);
+                if (h < hq) {
+                    T* dst = q_out + (static_cast<int64_t>(t) * hq + h) * d;
+                    store16(dst + i0[j], ra);
+                    store16(dst + i0[j] + half, rb);
+                } else {
+                    // K page: the slot's 8-dim runs, one per 8-dim block (a vector unit never
+                    // straddles two blocks: it starts at a multiple of its length, which divides 8)
+                    T* dst = k_cache + (static_cast<int64_t>(page) * hkv + (h - hq)) * P * d;
+                    const int e0 = i0[j], e1 = i0[j] + half;
+                    store16(dst + ((e0 >> 3) * P + slot) * 8 + (e0 & 7), ra);
+                    store16(dst + ((e1 >> 3) * P + slot) * 8 + (e1 & 7), rb);
+                }
             }
         }
     };
@@ -140,14 +148,16 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
         rotate_pass(base);
     }
 
-    // V goes unrotated into the dimension-major page: element e of the slot lands at [e][slot]
+    // V goes unrotated into its page: dim e of the slot lands in the run of 16-dim block e / 16
+    // and 4-slot group slot / 4, at (e % 16) * 4 + slot % 4 (a vector unit stays in one block)
     for (int vu = tid; vu < v_units; vu += kThreads) {
         if (vu != tid) vv = load16(v_new + static_cast<int64_t>(t) * hkv * d + vu * N);
         const int g = (vu * N) / d;
         const int e0 = vu * N - g * d;
-        T* vp = v_cache + ((static_cast<int64_t>(page) * hkv + g) * d + e0) * P + slot;
+        T* vp = v_cache + (static_cast<int64_t>(page) * hkv + g) * P * d +
+                (((e0 >> 4) * (P >> 2) + (slot >> 2)) * 16 + (e0 & 15)) * 4 + (slot & 3);
 #pragma unroll
-        for (int e = 0; e < N; ++e) vp[static_cast<int64_t>(e) * P] = vv.e[e];
+        for (int e = 0; e < N; ++e) vp[4 * e] = vv.e[e];
     }
 }
 

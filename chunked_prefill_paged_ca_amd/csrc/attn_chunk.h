@@ -17,9 +17,8 @@
 // columns.  Per 32-key block (two pages): the workgroup copies the two K pages and two V pages
 // (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), kept three blocks
 // ahead of the block being consumed (four LDS stages); each wave then runs S^T = K Q^T and
-// O^T = V^T P^T on
-// v_mfma_f32_16x16x32_bf16 with an online softmax per column.  K rows in LDS are XOR-swizzled
-// in 16-byte units so that the 16 keys an MFMA fragment reads fall on distinct banks.
+// O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with an online softmax per column.  The pages keep
+// their cache layout in LDS, where every fragment read is a bank-conflict-free contiguous run.
 // Only blocks that cross a row's diagonal need the mask; keys past a column's position get
 // weight 0, and V slots past the sequence end are zeroed in LDS before they reach the MFMA.
 
@@ -40,14 +39,13 @@ constexpr int kTiles = 2;  // 16-column MFMA tiles per wave -> 32 columns
 constexpr int kCols = 16 * kTiles * kWaves;  // 256 columns per workgroup
 constexpr int kMaxItemPages = 2048;  // page ids of one workgroup's key range kept in LDS
 
-// 16-byte unit swizzle of K row `key` (block key 0..31): spreads the 16 rows an S^T fragment
-// reads (keys 8a + 4t + b, a, b in 0..3) over 16 distinct units.
-__device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
-
-// One stage = K block (32 keys x D, 16-byte units swizzled per key) then V block
-// (2 pages x [d][16 slots]) = 64 D halves.  The two stages are separate __shared__ objects so
-// the compiler can tell that the DMA filling one never aliases reads of the other (with one
-// array indexed at run time it waits for every DMA before any LDS read).
+// One stage = the block's four page runs as they lie in the caches: K page a, K page b, V page
+// a, V page b (16 D halves each, 64 D in all).  With the cache layouts every MFMA fragment read
+// from a stage is then a contiguous run across the wave (16 bytes per lane for K, 8 bytes per
+// lane and page for V), which is free of LDS bank conflicts without any swizzle.  The stages are
+// separate __shared__ objects so the compiler can tell that the DMA filling one never aliases
+// reads of another (with one array indexed at run time it waits for every DMA before any LDS
+// read).
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
@@ -56,38 +54,32 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
     return r;
 }
 
+__device__ __forceinline__ bf16x8 lds_frag_pair(const uint16_t* a, const uint16_t* b) {
+    const uint2 x = *reinterpret_cast<const uint2*>(a);
+    const uint2 y = *reinterpret_cast<const uint2*>(b);
+    const uint4 v = make_uint4(x.x, x.y, y.x, y.y);
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
 // Copy one 32-key block straight from HBM into LDS stage `stage` (16-byte DMA per lane, no
-// registers).  The stage holds 8D 16-byte units: K units first (key-major, D/8 per key), then
-// the two V pages.  Wave w's instruction u fills the contiguous units (w*U + u)*64 + lane; the
-// first half of the waves fetch K (and apply the K swizzle on the load side), the rest V.
+// registers).  The stage holds 8D 16-byte units, 2D per page run; wave w's instruction u fills
+// the contiguous units (w*U + u)*64 + lane, all inside one run (2D is a multiple of 64), so
+// every instruction copies 1 KB of one page run.
 template <int D>
 __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __restrict__ k_cache,
                                           const uint16_t* __restrict__ v_cache, int pa, int pb,
                                           int g, int hkv, int w, int lane) {
     constexpr int U = 8 * D / (64 * kWaves);  // instructions per wave
-    constexpr int KUNITS = 32 * D / 8;
-    if (w < kWaves / 2) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int first = (w * U + u) * 64;
-            const int x = first + lane;
-            const int key = x / (D / 8);
-            const int phys = x - key * (D / 8);
-            const int unit = phys ^ (kswz(key) & (D / 8 - 1));
-            const int page = (key >> 4) ? pb : pa;
-            const uint16_t* src = k_cache + ((static_cast<int64_t>(page) * hkv + g) * 16 + (key & 15)) * D + 8 * unit;
-            __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int first = (w * U + u) * 64;
-            const int y = first - KUNITS + lane;
-            const int page = (y >= 2 * D) ? pb : pa;
-            const int off = (y >= 2 * D) ? y - 2 * D : y;
-            const uint16_t* src = v_cache + (static_cast<int64_t>(page) * hkv + g) * 16 * D + 8 * off;
-            __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
-        }
+    for (int u = 0; u < U; ++u) {
+        const int first = (w * U + u) * 64;
+        const int run = first / (2 * D);  // 0, 1: K of pages a, b; 2, 3: V of pages a, b
+        const int page = (run & 1) ? pb : pa;
+        const uint16_t* src = (run < 2 ? k_cache : v_cache) + (static_cast<int64_t>(page) * hkv + g) * 16 * D +
+                              8 * (first - run * 2 * D + lane);
+        __builtin_amdgcn_global_load_lds(src, stage + 8 * first, 16, 0, 0);
     }
 }
 
@@ -170,11 +162,10 @@ __device__ __forceinline__ void chunk_item(
         for (int nt = 0; nt < kTiles; ++nt) st[nt][0] = st[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int key = ((c >> 2) << 3) + 4 * t + (c & 3);
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                const int phys = (4 * kk + q) ^ (kswz(key) & (D / 8 - 1));
-                const bf16x8 kf = lds_frag(stg + key * D + 8 * phys);
+                // tile t = page t: row c = slot c, dims 32 kk + 8 q .. = 8-dim block 4 kk + q
+                const bf16x8 kf = lds_frag(stg + 16 * D * t + 512 * kk + 8 * lane);
 #pragma unroll
                 for (int nt = 0; nt < kTiles; ++nt) st[nt][t] = mfma16x16x32(kf, qf[nt][kk], st[nt][t]);
             }
@@ -190,9 +181,14 @@ __device__ __forceinline__ void chunk_item(
                 sc[4 + i] = st[nt][1][i];
             }
             if (!full) {
-                const int valid = lim[nt] - (key0 + 8 * q) + 1;
+                // keys key0 + 4q + j (page a) and key0 + 16 + 4q + j (page b) up to lim
+                const int va = lim[nt] - (key0 + 4 * q) + 1;
+                const int vb = va - 16;
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) sc[jj] = (jj < valid) ? sc[jj] : -INFINITY;
+                for (int jj = 0; jj < 4; ++jj) {
+                    sc[jj] = (jj < va) ? sc[jj] : -INFINITY;
+                    sc[4 + jj] = (jj < vb) ? sc[4 + jj] : -INFINITY;
+                }
             }
             // Each lane checks its own 8 scores against the column's reference max; only when
             // some score of the wave exceeds it by more than the slack (the first block, and
@@ -223,7 +219,7 @@ __device__ __forceinline__ void chunk_item(
         // O^T += V^T P^T; V fragments are read once and reused by both tiles
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
-            const bf16x8 vf = lds_frag(stg + 32 * D + (q >> 1) * 16 * D + (16 * mt + c) * 16 + 8 * (q & 1));
+            const bf16x8 vf = lds_frag_pair(stg + 32 * D + 256 * mt + 4 * lane, stg + 48 * D + 256 * mt + 4 * lane);
 #pragma unroll
             for (int nt = 0; nt < kTiles; ++nt) acc[nt][mt] = mfma16x16x32(vf, pf[nt], acc[nt][mt]);
         }
@@ -235,7 +231,8 @@ __device__ __forceinline__ void chunk_item(
         if (key0 + 32 <= kv_len) return;
         const int first_bad = kv_len - key0;  // block slots [first_bad, 32) are past the end
         for (int i = tid; i < 2 * D * 16; i += 64 * kWaves) {
-            const int slot = 16 * (i / (D * 16)) + (i & 15);
+            // V page run element i: slot 4 ((i / 64) % 4) + i % 4 of page i / (16 D)
+            const int slot = 16 * (i / (D * 16)) + 4 * ((i >> 6) & 3) + (i & 3);
             if (slot >= first_bad) stg[32 * D + i] = 0;
         }
         __syncthreads();

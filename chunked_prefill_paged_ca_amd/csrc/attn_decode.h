@@ -13,9 +13,10 @@
 //     kv head, key range) processed back to back;
 //   * the G query heads sharing a kv head are the columns of one MFMA tile, so each K/V byte is
 //     read once for all of them;
-//   * every K and V fragment is a 16-byte load issued straight from HBM into registers, and the
-//     next 32-key block is requested before the current one is consumed (register double buffer),
-//     so each wave keeps two blocks (16 KB) in flight;
+//   * K and V fragments are loaded straight from HBM into registers, each load instruction one
+//     contiguous run of a page (16 bytes per lane for K, 8 for V; the page layouts are chosen
+//     for it), and the next 32-key block is requested before the current one is consumed
+//     (register double buffer), so each wave keeps two blocks (16 KB) in flight;
 //   * QK^T and PV run on MFMA only so that the vector ALUs stay free: at G = 8 the fp32 vector
 //     work of a VALU dot product would need most of the chip's non-packed vector rate just to keep
 //     up with 8 TB/s of bf16 K/V.
@@ -36,46 +37,44 @@ namespace decode {
 
 template <int D>
 struct Block {
-    bf16x8 k0[D / 32];  // S^T tile 0 A fragments, one per 32-dim k step
-    bf16x8 k1[D / 32];  // S^T tile 1
+    bf16x8 k0[D / 32];  // S^T tile 0 (page a) A fragments, one per 32-dim k step
+    bf16x8 k1[D / 32];  // S^T tile 1 (page b)
     bf16x8 v[D / 16];   // O^T A fragments, one per 16-dim output tile
 };
 
+// One 32-key block = pages pa, pb of kv head g.  Every load instruction of the wave reads one
+// contiguous run: 1 KB (16 bytes per lane) of an 8-dim block of K, or 512 bytes (8 per lane) of
+// a 16-dim block of V, the pair from pages a and b making one fragment.
 template <int D>
 __device__ __forceinline__ void load_block(Block<D>& b, const uint16_t* __restrict__ k_cache,
                                            const uint16_t* __restrict__ v_cache, int pa, int pb,
-                                           int g, int hkv, int c, int q) {
-    // S^T rows: tile t row c holds block key 8 (c / 4) + 4 t + c % 4
-    const int kt0 = ((c >> 2) << 3) + (c & 3);
-    const int kt1 = kt0 + 4;
-    const int page0 = (kt0 >> 4) ? pb : pa;
-    const int page1 = (kt1 >> 4) ? pb : pa;
-    const uint16_t* kp0 = k_cache + ((static_cast<int64_t>(page0) * hkv + g) * 16 + (kt0 & 15)) * D + 8 * q;
-    const uint16_t* kp1 = k_cache + ((static_cast<int64_t>(page1) * hkv + g) * 16 + (kt1 & 15)) * D + 8 * q;
+                                           int g, int hkv, int lane) {
+    const int64_t ra = (static_cast<int64_t>(pa) * hkv + g) * 16 * D;
+    const int64_t rb = (static_cast<int64_t>(pb) * hkv + g) * 16 * D;
+    // tile row c = slot c, k = 8q + j = dim 32 kk + 8 q + j: 8-dim block 4 kk + q, slot c
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        b.k0[kk] = load_frag(kp0 + 32 * kk);
-        b.k1[kk] = load_frag(kp1 + 32 * kk);
+        b.k0[kk] = load_frag(k_cache + ra + 512 * kk + 8 * lane);
+        b.k1[kk] = load_frag(k_cache + rb + 512 * kk + 8 * lane);
     }
-    // O^T A fragment: dim 16 mt + c, keys 8q .. 8q+7 = page (q / 2), slots 8 (q % 2) ..
-    const int pv = (q >> 1) ? pb : pa;
-    const uint16_t* vp = v_cache + ((static_cast<int64_t>(pv) * hkv + g) * D + c) * 16 + 8 * (q & 1);
+    // O^T row c = dim 16 mt + c, keys: slots 4q .. 4q+3 of page a, then of page b
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) b.v[mt] = load_frag(vp + 16 * 16 * mt);
+    for (int mt = 0; mt < D / 16; ++mt)
+        b.v[mt] = load_frag_pair(v_cache + ra + 256 * mt + 4 * lane, v_cache + rb + 256 * mt + 4 * lane);
 }
 
 // One work item: the keys [kb, ke) of one (decode row, kv head).  rec0 = {kv head, kb, ke,
 // partial slot or -1 for direct output}, rec1 = {row, offset of the row's page ids, page count, 0}.
 template <int D>
 __device__ __forceinline__ void decode_item(
-    const int4 rec0, const int4 rec1, const int32_t* __restrict__ page_indices,
+    const int4 rec0, const int4 rec1, ConstPtr<int32_t> page_indices,
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse, int lane) {
     const int g = rec0.x, kb = rec0.y, ke = rec0.z, out = rec0.w;
     const int row = rec1.x;
-    const int32_t* pages = page_indices + rec1.y;
+    const ConstPtr<int32_t> pages = page_indices + rec1.y;
     const int np = rec1.z;
     const int G = hq / hkv;
     const int c = lane & 15, q = lane >> 4;
@@ -94,8 +93,9 @@ __device__ __forceinline__ void decode_item(
     float m = -INFINITY, l = 0.0f;
 
     // One 32-key block: scores, online-softmax update, PV.  Lane group q holds the scores of
-    // keys key0 + 8q .. key0 + 8q + 7 of query column c.  Only an item's last block can run past
-    // its end, so the masks are taken on that block alone (the test is wave-uniform).
+    // keys key0 + 4q .. key0 + 4q + 3 (page a) and key0 + 16 + 4q .. (page b) of query column c.
+    // Only an item's last block can run past its end, so the masks are taken on that block alone
+    // (the test is wave-uniform).
     auto consume = [&](const Block<D>& b, int key0) {
         floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -104,7 +104,8 @@ __device__ __forceinline__ void decode_item(
             s1 = mfma16x16x32(b.k1[kk], qf[kk], s1);
         }
         const bool full = key0 + 32 <= ke;
-        const int valid = ke - (key0 + 8 * q);  // keys of this lane inside the item
+        const int va = ke - (key0 + 4 * q);  // keys of this lane's page-a run inside the item
+        const int vb = va - 16;               // and of its page-b run
         float sc[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -113,7 +114,10 @@ __device__ __forceinline__ void decode_item(
         }
         if (!full) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sc[j] = (j < valid) ? sc[j] : -INFINITY;
+            for (int j = 0; j < 4; ++j) {
+                sc[j] = (j < va) ? sc[j] : -INFINITY;
+                sc[4 + j] = (j < vb) ? sc[4 + j] : -INFINITY;
+            }
         }
         float bm = sc[0];
 #pragma unroll
@@ -143,7 +147,7 @@ __device__ __forceinline__ void decode_item(
             for (int mt = 0; mt < D / 16; ++mt) acc[mt] = mfma16x16x32(b.v[mt], pf, acc[mt]);
         } else {
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) acc[mt] = mfma16x16x32(mask_frag(b.v[mt], valid), pf, acc[mt]);
+            for (int mt = 0; mt < D / 16; ++mt) acc[mt] = mfma16x16x32(mask_frag(b.v[mt], va, vb), pf, acc[mt]);
         }
     };
 
@@ -166,19 +170,19 @@ __device__ __forceinline__ void decode_item(
     Block<D> ba, bb;
     int pa, pb;
     pages_of(kb, pa, pb);
-    load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, c, q);
+    load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, lane);
     if (nblk > 1) pages_of(kb + 32, pa, pb);
     int bi = 0;
     for (; bi + 2 < nblk; bi += 2) {
-        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, c, q);  // block bi + 1
+        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, lane);  // block bi + 1
         pages_of(kb + 32 * (bi + 2), pa, pb);
         consume(ba, kb + 32 * bi);
-        load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, c, q);  // block bi + 2
+        load_block<D>(ba, k_cache, v_cache, pa, pb, g, hkv, lane);  // block bi + 2
         pages_of(kb + 32 * (bi + 3), pa, pb);  // clamped past the end, never used there
         consume(bb, kb + 32 * (bi + 1));
     }
     if (bi + 1 < nblk) {
-        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, c, q);
+        load_block<D>(bb, k_cache, v_cache, pa, pb, g, hkv, lane);
         consume(ba, kb + 32 * bi);
         consume(bb, kb + 32 * (bi + 1));
     } else {

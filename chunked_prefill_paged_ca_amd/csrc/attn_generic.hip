@@ -75,9 +75,9 @@ __global__ void __launch_bounds__(kWave) attn_generic_kernel(
         if (j < k1) {
             const int page = p.kv_page_indices[page0 + j / P];
             const int64_t run = (static_cast<int64_t>(page) * hkv + g) * P * d;
-            const T* kr = k_cache + run + static_cast<int64_t>(j % P) * d;
+            const T* kr = k_cache + run + (j % P) * 8;  // slot's run in 8-dim block 0
             float dot = 0.0f;
-            for (int e = 0; e < d; ++e) dot += s_q[e] * Storage<T>::load(kr + e);
+            for (int e = 0; e < d; ++e) dot += s_q[e] * Storage<T>::load(kr + (e >> 3) * P * 8 + (e & 7));
             sc = dot * scale;
         }
         const float mb = wave_max(sc);
@@ -94,10 +94,13 @@ __global__ void __launch_bounds__(kWave) attn_generic_kernel(
         for (int jj = 0; jj < nb; ++jj) {
             const int key = kb + jj;
             const int page = p.kv_page_indices[page0 + key / P];
-            const T* vr = v_cache + (static_cast<int64_t>(page) * hkv + g) * d * P + key % P;
+            const int slot = key % P;
+            const T* vr = v_cache + (static_cast<int64_t>(page) * hkv + g) * d * P + (slot >> 2) * 64 + (slot & 3);
             const float wj = s_w[jj];
-            if (lane < d) acc0 += wj * Storage<T>::load(vr + static_cast<int64_t>(lane) * P);
-            if (lane + kWave < d) acc1 += wj * Storage<T>::load(vr + static_cast<int64_t>(lane + kWave) * P);
+            // dim e of the slot: 16-dim block e / 16 (P * 16 elements each), then (e % 16) * 4
+            const int e0 = lane, e1 = lane + kWave;
+            if (e0 < d) acc0 += wj * Storage<T>::load(vr + (e0 >> 4) * P * 16 + (e0 & 15) * 4);
+            if (e1 < d) acc1 += wj * Storage<T>::load(vr + (e1 >> 4) * P * 16 + (e1 & 15) * 4);
         }
         __syncthreads();
     }

@@ -42,9 +42,11 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
         const int lane = threadIdx.x & 63;
         const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + (threadIdx.x >> 6));
         if (w >= num_waves) return;
-        const int i_end = wave_items[w + 1];
-        for (int i = wave_items[w]; i < i_end; ++i)
-            decode::decode_item<D>(dec_items[2 * i], dec_items[2 * i + 1], p.kv_page_indices, qg,
+        const ConstPtr<int32_t> bounds = as_const(wave_items);
+        const ConstPtr<int32_t> recs = as_const(reinterpret_cast<const int32_t*>(dec_items));
+        const int i_end = bounds[w + 1];
+        for (int i = bounds[w]; i < i_end; ++i)
+            decode::decode_item<D>(load_rec(recs, 2 * i), load_rec(recs, 2 * i + 1), as_const(p.kv_page_indices), qg,
                                    k_cache, v_cache, hq, hkv, scale_log2, dec_acc, dec_ml, o, lse,
                                    lane);
         return;

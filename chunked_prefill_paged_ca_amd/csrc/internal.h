@@ -35,6 +35,25 @@ struct DevPlan {
     int32_t page_size;
 };
 
+// Read-only plan metadata seen through the constant address space.  The attention kernel only
+// reads the plan arrays (they are written by earlier launches), and saying so lets the compiler
+// serve wave-uniform reads of them with scalar loads.  Through a generic pointer it cannot prove
+// that the kernel's own stores (outputs, partials) leave them alone, and falls back to vector
+// loads, which share the in-order vector-memory counter with the K/V loads: waiting for a page
+// id would then also wait for every K/V load issued before it.
+template <typename T>
+using ConstPtr = const __attribute__((address_space(4))) T*;
+
+template <typename T>
+__device__ __forceinline__ ConstPtr<T> as_const(const T* p) {
+    return (ConstPtr<T>)(p);
+}
+
+// Record i of an int4 array read through the constant address space.
+__device__ __forceinline__ int4 load_rec(ConstPtr<int32_t> p, int i) {
+    return make_int4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+}
+
 struct Shape {
     int32_t hq, hkv, d, P;
     float scale;

@@ -4,13 +4,16 @@
 //   A (16 x 32): row c, k = 8q .. 8q+7      B (32 x 16): column c, k = 8q .. 8q+7
 //   C (16 x 16): column c, rows 4q .. 4q+3
 // The kernels compute S^T = K Q^T (A = 16 keys x 32 dims, B = Q^T) and O^T = V^T P^T
-// (A = 16 dims x 32 keys from a dimension-major V page, B = P^T).  Both A fragments are one
-// contiguous 16-byte load, and in both products the lane's C column is one query column, so
-// the running max / sum of a query column never leaves its lane group.
+// (A = 16 dims x 32 keys, B = P^T).  In both products the lane's C column is one query column,
+// so the running max / sum of a query column never leaves its lane group.
 //
-// Key order inside a 32-key block: the S^T tile t (t = 0, 1) row r holds key 8 (r / 4) + 4 t +
-// r % 4.  Lane group q then holds the scores of keys 8q .. 8q+7 (tile 0 gives 8q..8q+3, tile 1
-// gives 8q+4..8q+7), which is exactly the k range of its P^T fragment in O^T = V^T P^T.
+// Key order inside a 32-key block (two pages a, b): S^T tile t is page t, its row r is slot r.
+// Lane group q then holds the scores of slots 4q .. 4q+3 of page a (tile 0) and of page b
+// (tile 1), and those eight keys, in that order, are the k range 8q .. 8q+7 of its P^T fragment
+// in O^T = V^T P^T; the V^T fragment takes the same keys.  With the page layouts of the caches
+// (8-dim blocks of 16 slots for K, 4-slot groups of 16 dims for V) every fragment a wavefront
+// loads from a page is one contiguous run: lane l reads 16 bytes at 16 l for K, and 8 bytes at
+// 8 l from each of the two pages for V.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,16 +44,27 @@ __device__ __forceinline__ bf16x8 zero_frag() {
     return r;
 }
 
-// Zero the bf16 elements j of a fragment whose j >= valid (valid in [0, 8]).
-__device__ __forceinline__ bf16x8 mask_frag(bf16x8 f, int valid) {
-    if (valid >= 8) return f;
+// Two 8-byte loads (4 bf16 each: the lane's keys of page a, then of page b) as one fragment.
+__device__ __forceinline__ bf16x8 load_frag_pair(const uint16_t* a, const uint16_t* b) {
+    const uint2 x = *reinterpret_cast<const uint2*>(a);
+    const uint2 y = *reinterpret_cast<const uint2*>(b);
+    const uint4 v = make_uint4(x.x, x.y, y.x, y.y);
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+// Zero fragment elements by key: element j < 4 is kept when j < va, element 4 + j when j < vb
+// (va, vb: keys of the lane's page-a and page-b runs that are inside the range).
+__device__ __forceinline__ bf16x8 mask_frag(bf16x8 f, int va, int vb) {
     uint4 v;
     __builtin_memcpy(&v, &f, sizeof(v));
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int j = 2 * i;
-        uint32_t keep = (j < valid ? 0x0000ffffu : 0u) | (j + 1 < valid ? 0xffff0000u : 0u);
+        const int n = i < 2 ? va : vb;
+        const int j = 2 * (i & 1);
+        const uint32_t keep = (j < n ? 0x0000ffffu : 0u) | (j + 1 < n ? 0xffff0000u : 0u);
         w[i] &= keep;
     }
     v = make_uint4(w[0], w[1], w[2], w[3]);

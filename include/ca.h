@@ -28,10 +28,16 @@
  *     16-byte vectors); lse 4-byte aligned.  A misaligned pointer is CA_ERR_INVALID_ARG.
  *
  * Paged KV cache layout (element type per ca_dtype, page size P, head dim d, Hkv kv heads):
- *   k_cache: [num_pool_pages][Hkv][P][d]   -- token-major inside a page
- *   v_cache: [num_pool_pages][Hkv][d][P]   -- dimension-major inside a page ("transposed" V page)
+ *   k_cache: [num_pool_pages][Hkv][d/8][P][8]
+ *       slot s, dim e of a page at ((e/8)*P + s)*8 + e%8: for each block of 8 dims, the P slots'
+ *       8-element runs one after another
+ *   v_cache: [num_pool_pages][Hkv][d/16][P/4][16][4]
+ *       slot s, dim e of a page at (((e/16)*(P/4) + s/4)*16 + e%16)*4 + s%4: for each block of
+ *       16 dims and each group of 4 slots, the 16 dims' 4-slot runs one after another
  * Each (page, kv head) block is one contiguous P*d run in both caches.  Token at absolute
- * position p of a request lives in logical page p / P, slot p % P.
+ * position p of a request lives in logical page p / P, slot p % P.  (Both layouts put the
+ * elements one matrix-core operand fragment needs from a page in a single run per wavefront
+ * load: 16 bytes per lane for K, 8 for V.)
  */
 #ifndef CA_H
 #define CA_H

@@ -1,7 +1,9 @@
 """Test/bench harness: lay workload inputs into the library's paged layout and read them back.
 
-Page layout of the library (include/ca.h): k_cache [pool][Hkv][P][d], v_cache [pool][Hkv][d][P].
-These helpers only move data (scatter / gather by block table); they compute nothing.
+Page layout of the library (include/ca.h): k_cache [pool][Hkv][d/8][P][8],
+v_cache [pool][Hkv][d/16][P/4][16][4].  The pool tensors are allocated with those shapes, so a
+(page, slot) pair indexes them directly.  These helpers only move data (scatter / gather by
+block table); they compute nothing.
 """
 from __future__ import annotations
 
@@ -19,8 +21,8 @@ def alloc_pool(wl, device="cuda", fill: Optional[float] = float("nan")):
     import torch
     td = torch_dtype(wl.dtype)
     P, H, d = wl.page_size, wl.num_kv_heads, wl.head_dim
-    k = torch.empty((wl.num_pool_pages, H, P, d), dtype=td, device=device)
-    v = torch.empty((wl.num_pool_pages, H, d, P), dtype=td, device=device)
+    k = torch.empty((wl.num_pool_pages, H, d // 8, P, 8), dtype=td, device=device)
+    v = torch.empty((wl.num_pool_pages, H, d // 16, P // 4, 16, 4), dtype=td, device=device)
     if fill is not None:
         k.fill_(fill)
         v.fill_(fill)
@@ -47,6 +49,21 @@ def _slots(table: np.ndarray, P: int, start: int, stop: int):
     return table[pos // P].astype(np.int64), (pos % P).astype(np.int64)
 
 
+def _scatter(k_cache, v_cache, pi, si, k, v):
+    """Write dense k, v [n, Hkv, d] to (page pi[i], slot si[i])."""
+    n, H, d = k.shape
+    k_cache[pi, :, :, si, :] = k.reshape(n, H, d // 8, 8).to(k_cache.device, k_cache.dtype)
+    v_cache[pi, :, :, si // 4, :, si % 4] = v.reshape(n, H, d // 16, 16).to(v_cache.device, v_cache.dtype)
+
+
+def _gather(k_cache, v_cache, pi, si):
+    """Read (page pi[i], slot si[i]) back as dense k, v [n, Hkv, d]."""
+    k = k_cache[pi, :, :, si, :]
+    v = v_cache[pi, :, :, si // 4, :, si % 4]
+    n, H = k.shape[0], k.shape[1]
+    return k.reshape(n, H, -1), v.reshape(n, H, -1)
+
+
 def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None):
     """Scatter each request's drawn history (positions 0..nc-1) into its pages."""
     import torch
@@ -60,8 +77,7 @@ def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None
         pages, slots = _slots(wl.block_tables[r], wl.page_size, 0, nc)
         pi = torch.from_numpy(pages).to(dev)
         si = torch.from_numpy(slots).to(dev)
-        k_cache[pi, :, si, :] = torch.from_numpy(hk).to(dev, k_cache.dtype)
-        v_cache[pi, :, :, si] = torch.from_numpy(hv).to(dev, v_cache.dtype)
+        _scatter(k_cache, v_cache, pi, si, torch.from_numpy(hk), torch.from_numpy(hv))
 
 
 def read_dense(k_cache, v_cache, table: np.ndarray, P: int, kv_len: int):
@@ -70,9 +86,8 @@ def read_dense(k_cache, v_cache, table: np.ndarray, P: int, kv_len: int):
     pages, slots = _slots(table, P, 0, kv_len)
     pi = torch.from_numpy(pages).to(k_cache.device)
     si = torch.from_numpy(slots).to(k_cache.device)
-    k = k_cache[pi, :, si, :].float().cpu().numpy().astype(np.float64)
-    v = v_cache[pi, :, :, si].float().cpu().numpy().astype(np.float64)
-    return k, v
+    k, v = _gather(k_cache, v_cache, pi, si)
+    return (k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64))
 
 
 def to_device(x: np.ndarray, dt: str, device="cuda"):
