@@ -382,12 +382,18 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
     return CA_OK;
 }
 
+// Share of the CUs the decode rows get when they share the attention launch with chunk rows.
+// Measured on the 256-CU part (Mistral-7B, Yi-34B and LLaMA2-70B mixed steps): decode keeps its
+// HBM rate on 3/4 of the CUs; fewer starve it, more starve the chunk work.
+constexpr double kMixedDecodeShare = 0.75;
+
 // Decode workgroups of the attention launch and decode shares.  The 32-key blocks of every
 // (decode row, kv head), laid end to end, are cut into one equal share per decode wavefront, so a
 // single round of waves streams the whole decode K/V with no tail.  Alone (no chunk rows, or the
 // two parts launched separately) decode takes every workgroup slot of the device; in a mixed
-// launch it takes `mixed_share` of them (rounded to whole XCD rounds of 8) and the chunk
-// workgroups run beside it.  CA_DECODE_WGS sets the count of a mixed launch instead.  Returns the share count; *wgs gets the decode workgroups.
+// launch it takes kMixedDecodeShare of them (rounded to whole XCD rounds of 8) and the chunk
+// workgroups run beside it.  CA_DECODE_WGS sets the count of a mixed launch instead.  Returns
+// the share count; *wgs gets the decode workgroups.
 int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t* wgs) {
     int64_t blocks = 0;
     for (int32_t s = 0; s < plan->num_decodes; ++s) {
@@ -402,10 +408,7 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t
     const bool mixed = plan->num_seqs > plan->num_decodes && !ctx->split_attention;
     int32_t n = slots;
     if (mixed) {
-        // measured on the 256-CU part (Mistral-7B, Yi-34B and LLaMA2-70B mixed steps): decode
-        // keeps its HBM rate on 3/4 of the CUs; fewer starve it, more starve the chunk work
-        constexpr double mixed_share = 0.75;
-        n = ctx->dec_wgs_override > 0 ? ctx->dec_wgs_override : static_cast<int32_t>(slots * mixed_share);
+        n = ctx->dec_wgs_override > 0 ? ctx->dec_wgs_override : static_cast<int32_t>(slots * kMixedDecodeShare);
         n = (n + 7) / 8 * 8;
         if (n > slots) n = slots;
     }
@@ -419,7 +422,8 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t
 
 // Keys per chunk split: a row block whose visible keys exceed this is cut into several
 // workgroups (merged afterwards) so that a step with few chunk rows still covers the CUs.
-int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t override_keys) {
+int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh,
+                         int32_t override_keys) {
     const int32_t G = sh.hq / sh.hkv;
     const int32_t cols_per_block = ca::chunk_cols_per_block();
     if (override_keys > 0) {
@@ -447,6 +451,34 @@ int32_t chunk_split_keys(const ca_plan* plan, const Shape& sh, int32_t override_
     const int64_t target = 1024;  // workgroups (one per CU at a time; several rounds)
     int64_t L = (work + target - 1) / target;
     if (L < 512) L = 512;
+    // When decode rows share the launch they set its length (their K/V stream), and the chunk
+    // workgroups run beside them on the CUs the decode rows leave free.  If all the chunk work
+    // fits there within that time, splitting a row block only adds its partials' round trip
+    // through HBM and the merge: keep each block whole, as long as its workgroup still ends well
+    // inside the decode time.  Measured on the part: one 32-key block of a 256-column workgroup
+    // takes ~1.75 us at d = 128, and the decode rows stream ~5.5 TB/s.
+    const bool fused = plan->num_decodes > 0 && plan->num_seqs > plan->num_decodes && !ctx->split_attention;
+    if (fused) {
+        int64_t dec_keys = 0;
+        for (int32_t s = 0; s < plan->num_decodes; ++s) {
+            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            dec_keys += (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        }
+        const double dec_us = static_cast<double>(dec_keys) * sh.hkv * sh.d * 4 / 5.5e6;  // K + V bf16
+        const double block_us = sh.d == 128 ? 1.75 : 0.9;
+        const double chunk_cus = ctx->num_cus * (1.0 - kMixedDecodeShare);
+        if (static_cast<double>(work) / 32 * block_us <= 0.75 * chunk_cus * dec_us) {
+            int32_t longest = 0;
+            for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+                const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+                const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+                if (kv_len > longest) longest = kv_len;
+            }
+            const int64_t whole = static_cast<int64_t>(0.9 * dec_us / block_us) * 32;
+            const int64_t keep = longest < whole ? longest : whole;
+            if (keep > L) L = keep;
+        }
+    }
     // the split merge handles at most 64 splits of one row block
     int32_t longest = 0;
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
@@ -491,7 +523,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     const bool mfma = sh.dtype == CA_BF16 && G <= 16;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
                 mfma ? decode_shares(ctx, plan, sh, &dec_wgs) : -1,
-                mfma ? chunk_split_keys(plan, sh, ctx->csplit_override) : -1, sh.theta};
+                mfma ? chunk_split_keys(ctx, plan, sh, ctx->csplit_override) : -1, sh.theta};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
     ca_status st = validate_plan_arrays(plan, pool);
     if (st != CA_OK) return st;
