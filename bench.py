@@ -48,8 +48,8 @@ def stored_traffic():
     return int(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands on the whole step (every row), best of 3 runs."""
+def cpu_baseline(wl, min_seconds=10.0):
+    """The oracle as it stands on the whole step (every row), repeated for at least min_seconds."""
     import oracle
     from chunked_prefill_paged_ca_amd.workload import StreamCursor
     sess = oracle.Session(wl)
@@ -59,15 +59,16 @@ def cpu_baseline(wl):
     T = p["num_tokens"]
     threads = oracle.default_threads()
     times = []
-    for _ in range(3):
+    while sum(times) < min_seconds:
         fresh = sess.fork()
         t0 = time.perf_counter()
         fresh.step(p, q, k, v, nthreads=threads)
         times.append(time.perf_counter() - t0)
-    dt = min(times)
+    dt = float(np.mean(times))
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole step: all {T} rows ({nd} decode rows + 2 prefill chunks), "
-                      f"fp64 C oracle on {threads} threads, best of 3 runs of {dt:.2f} s each"}
+                      f"fp64 C oracle on {threads} threads, mean of {len(times)} runs "
+                      f"({sum(times):.1f} s of work, {dt:.2f} s per step)"}
 
 
 def main():
