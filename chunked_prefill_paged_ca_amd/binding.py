@@ -32,7 +32,7 @@ class CaRequest(ctypes.Structure):
 
 class CaPlanParams(ctypes.Structure):
     _fields_ = [("token_budget", ctypes.c_int32), ("max_chunk", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("chunk_align", ctypes.c_int32),
                 ("num_pool_pages", ctypes.c_int64)]
 
 
@@ -164,7 +164,7 @@ class RequestBatch:
     """
 
     def __init__(self, num_computed, num_prompt_left, block_tables, token_budget: int,
-                 max_chunk: int, page_size: int, num_pool_pages: int):
+                 max_chunk: int, page_size: int, num_pool_pages: int, chunk_align: int = 0):
         n = len(num_computed)
         self.n = n
         self.tables = [np.ascontiguousarray(b, dtype=np.int32) for b in block_tables]
@@ -173,7 +173,7 @@ class RequestBatch:
             self.reqs[i].num_pages = int(self.tables[i].shape[0])
             self.reqs[i].block_table = self.tables[i].ctypes.data_as(_i32p) if self.tables[i].size else None
         self.update(num_computed, num_prompt_left)
-        self.prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), 0,
+        self.prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), int(chunk_align),
                                 int(num_pool_pages))
         self.out = Plan(n, int(sum(t.shape[0] for t in self.tables)))
 
@@ -192,7 +192,8 @@ class RequestBatch:
 def plan_batch(num_computed: Sequence[int], num_prompt_left: Sequence[int],
                block_tables: Sequence[np.ndarray], token_budget: int, max_chunk: int,
                page_size: int, num_pool_pages: int, cap_seqs: Optional[int] = None,
-               cap_pages: Optional[int] = None, raise_on_error: bool = True) -> Plan:
+               cap_pages: Optional[int] = None, raise_on_error: bool = True,
+               chunk_align: int = 0) -> Plan:
     """ca_plan_batch over the given requests; the Plan's arrays are filled by the library."""
     n = len(num_computed)
     tables = [np.ascontiguousarray(b, dtype=np.int32) for b in block_tables]
@@ -202,7 +203,8 @@ def plan_batch(num_computed: Sequence[int], num_prompt_left: Sequence[int],
         reqs[i].num_prompt_left = int(num_prompt_left[i])
         reqs[i].num_pages = int(tables[i].shape[0])
         reqs[i].block_table = tables[i].ctypes.data_as(_i32p) if tables[i].size else None
-    prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), 0, int(num_pool_pages))
+    prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), int(chunk_align),
+                       int(num_pool_pages))
     if cap_seqs is None:
         cap_seqs = n
     if cap_pages is None:

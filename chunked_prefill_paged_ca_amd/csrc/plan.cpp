@@ -7,7 +7,9 @@
 // order) and section "7.3" (a per-request chunk cap, max_chunk here), and magicnetworld.com
 // "分块预填充与 Stall-free 调度", section "六·补二" (a chunk is the smaller of the budget left and
 // the prompt left).  The output is the ragged metadata named in "Sarathi-Serve 完全拆解", section
-// "混合批不是把两类注意力强行做成同一个形状".
+// "混合批不是把两类注意力强行做成同一个形状".  Optional tile alignment of chunks that do not end
+// their prompt: "Sarathi-Serve 完全拆解", section "257 为什么可能比 256 慢 32%" (chunk sizes one past
+// a tile multiple waste a row of tiles; candidate sizes are aligned to multiples such as 32).
 
 #include <atomic>
 #include <cstdint>
@@ -33,8 +35,10 @@ extern "C" ca_status ca_plan_batch(const ca_request* reqs, int32_t n, const ca_p
     if (!prm || !plan) { ca::set_error("ca_plan_batch: null params or plan"); return CA_ERR_INVALID_ARG; }
     if (n < 0 || (n > 0 && !reqs)) { ca::set_error("ca_plan_batch: bad request array"); return CA_ERR_INVALID_ARG; }
     const int64_t P = prm->page_size;
-    if (prm->token_budget <= 0 || P <= 0 || prm->max_chunk < 0 || prm->num_pool_pages <= 0) {
-        ca::set_error("ca_plan_batch: token_budget, page_size and num_pool_pages must be > 0, max_chunk >= 0");
+    if (prm->token_budget <= 0 || P <= 0 || prm->max_chunk < 0 || prm->num_pool_pages <= 0 ||
+        prm->chunk_align < 0) {
+        ca::set_error("ca_plan_batch: token_budget, page_size and num_pool_pages must be > 0, "
+                      "max_chunk and chunk_align >= 0");
         return CA_ERR_INVALID_ARG;
     }
     for (int32_t i = 0; i < n; ++i) {
@@ -74,6 +78,8 @@ extern "C" ca_status ca_plan_batch(const ca_request* reqs, int32_t n, const ca_p
         if (prm->max_chunk > 0 && take > prm->max_chunk) take = prm->max_chunk;
         const int64_t room = static_cast<int64_t>(r.num_pages) * P - r.num_computed;
         if (take > room) take = room;
+        // a chunk that leaves part of the prompt for later steps is cut to a tile multiple
+        if (prm->chunk_align > 1 && take < r.num_prompt_left) take -= take % prm->chunk_align;
         if (take <= 0) continue;
         picks.push_back({i, static_cast<int32_t>(take)});
         budget -= take;

@@ -70,6 +70,7 @@ class Workload:
     uids: Optional[np.ndarray] = None  # stable request ids keying the random draws
     q_scale: float = 1.0              # > 1 makes scores peaky (stresses the running max)
     kv_value: Optional[float] = None  # if set, every V entry is this constant (property tests)
+    chunk_align: int = 0              # planner tile multiple for chunks that leave prompt behind
     notes: dict = field(default_factory=dict)
 
     @property

@@ -73,7 +73,10 @@ typedef struct {
     int32_t token_budget;   /* tau: total query tokens of the step, decodes included (> 0) */
     int32_t max_chunk;      /* per-request cap on a prefill chunk; 0 = no cap */
     int32_t page_size;      /* P (> 0) */
-    int32_t reserved;
+    int32_t chunk_align;    /* tile multiple A for chunks that do not end their prompt; 0 or 1 =
+                               none ([SS] "257 为什么可能比 256 慢 32%": a chunk one token past a
+                               tile multiple costs a whole extra row of tiles, and candidate chunk
+                               sizes are aligned to tile multiples such as 32) */
     int64_t num_pool_pages; /* page ids must lie in [0, num_pool_pages) */
 } ca_plan_params;
 
@@ -124,9 +127,13 @@ ca_status ca_destroy(ca_ctx* ctx);
  *   2. prefills, in caller order (list in-progress chunks before new requests), each getting
  *      min(num_prompt_left, budget left, max_chunk if > 0, free slots of its block table);
  *      the scan stops when the budget is used up.  Several chunks may share a step.
+ *   3. with chunk_align = A > 1, a chunk that does not finish its prompt is cut down to a
+ *      multiple of A; one cut to 0 is not scheduled (the budget stays for the requests after
+ *      it), and the chunk that finishes a prompt is never cut.
  * For each scheduled sequence: kv_len = num_computed + q, pages = ceil(kv_len / P) taken from
  * the front of its block table, kv_last_page_len = kv_len - (pages - 1) * P.
- * Errors: CA_ERR_INVALID_ARG (n < 0, budget/page size <= 0, negative fields, missing table,
+ * Errors: CA_ERR_INVALID_ARG (n < 0, budget/page size <= 0, negative fields or chunk_align,
+ * missing table,
  * a scheduled page id outside the pool), CA_ERR_NO_PAGES (a decode whose table has fewer than
  * num_computed + 1 slots), CA_ERR_CAPACITY (num_seqs > cap_seqs or num_pages > cap_pages; the
  * counts then hold the required sizes).

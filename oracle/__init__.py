@@ -37,7 +37,8 @@ def lib():
         L = ctypes.CDLL(path)
         L.oracle_plan.restype = ctypes.c_int
         L.oracle_plan.argtypes = [ctypes.c_int32, _i32p, _i32p, _i32p, _i64p, _i32p,
-                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int32,
                                   _i32p, _i32p, _i32p, _i32p, _i32p, _i32p]
         L.oracle_rope.restype = None
@@ -69,7 +70,8 @@ def default_threads() -> int:
 
 def plan(num_computed, num_prompt_left, block_tables: List[np.ndarray], token_budget: int,
          max_chunk: int, page_size: int, num_pool_pages: int,
-         cap_seqs: Optional[int] = None, cap_pages: Optional[int] = None) -> Dict:
+         cap_seqs: Optional[int] = None, cap_pages: Optional[int] = None,
+         chunk_align: int = 0) -> Dict:
     """Decode-first budget plan.  Returns {"status", and on OK the metadata arrays + counts}."""
     nc = np.ascontiguousarray(num_computed, dtype=np.int32)
     nl = np.ascontiguousarray(num_prompt_left, dtype=np.int32)
@@ -90,7 +92,8 @@ def plan(num_computed, num_prompt_left, block_tables: List[np.ndarray], token_bu
     last = np.zeros(max(cap_seqs, 1), dtype=np.int32)
     counts = np.zeros(5, dtype=np.int32)
     st = lib().oracle_plan(n, _p(nc, _i32p), _p(nl, _i32p), _p(npg, _i32p), _p(off, _i64p),
-                           _p(bt, _i32p), token_budget, max_chunk, page_size, num_pool_pages,
+                           _p(bt, _i32p), token_budget, max_chunk, chunk_align, page_size,
+                           num_pool_pages,
                            cap_seqs, cap_pages, _p(req_ids, _i32p), _p(qo, _i32p),
                            _p(kvp, _i32p), _p(idx, _i32p), _p(last, _i32p), _p(counts, _i32p))
     out = {"status": int(st)}
@@ -189,7 +192,8 @@ class Session:
     def plan(self) -> Dict:
         wl = self.wl
         return plan(self.num_computed, self.num_prompt_left, wl.block_tables, wl.token_budget,
-                    wl.max_chunk, wl.page_size, wl.num_pool_pages)
+                    wl.max_chunk, wl.page_size, wl.num_pool_pages,
+                    chunk_align=getattr(wl, "chunk_align", 0))
 
     def step(self, p: Dict, q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray,
              rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> Dict:

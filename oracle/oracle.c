@@ -57,6 +57,10 @@
  *     leaves this open; keeping the cap is the reading taken).
  * A prefill is also capped by the free slots of its block table (num_pages*page_size minus the
  * tokens already cached); a decode without a free slot is an error (CA-style status 2).
+ * With chunk_align > 1, a prefill chunk that does not reach the end of its prompt is rounded
+ * down to a multiple of chunk_align, and skipped if that leaves nothing ([SS] "257 为什么可能比
+ * 256 慢 32%": chunk sizes are snapped to tile multiples such as 32 because one token past a
+ * multiple costs a whole extra row of tiles; the final chunk of a prompt is whatever is left).
  *
  * Output metadata for scheduled sequence s (decodes first), with kv_len = num_computed + q:
  *   qo_indptr[s+1]   = qo_indptr[s] + q
@@ -67,11 +71,12 @@
  */
 int oracle_plan(int32_t n, const int32_t* num_computed, const int32_t* num_prompt_left,
                 const int32_t* num_pages, const int64_t* bt_offset, const int32_t* bt,
-                int32_t token_budget, int32_t max_chunk, int32_t page_size,
+                int32_t token_budget, int32_t max_chunk, int32_t chunk_align, int32_t page_size,
                 int64_t num_pool_pages, int32_t cap_seqs, int32_t cap_pages,
                 int32_t* req_ids, int32_t* qo_indptr, int32_t* kv_page_indptr,
                 int32_t* kv_page_indices, int32_t* kv_last_page_len, int32_t* counts) {
-    if (n < 0 || token_budget <= 0 || page_size <= 0 || max_chunk < 0 || num_pool_pages <= 0)
+    if (n < 0 || token_budget <= 0 || page_size <= 0 || max_chunk < 0 || chunk_align < 0 ||
+        num_pool_pages <= 0)
         return ORACLE_INVALID_ARG;
     if (n > 0 && (num_computed == NULL || num_prompt_left == NULL || num_pages == NULL ||
                   bt_offset == NULL))
@@ -108,6 +113,9 @@ int oracle_plan(int32_t n, const int32_t* num_computed, const int32_t* num_promp
         if (max_chunk > 0 && max_chunk < q) q = max_chunk;
         int64_t room = (int64_t)num_pages[i] * page_size - num_computed[i];
         if (room < q) q = room;
+        /* Tile alignment: a chunk after which prompt tokens remain is rounded down to a
+         * multiple of chunk_align; the last chunk of a prompt keeps its length. */
+        if (chunk_align > 1 && q < num_prompt_left[i]) q = (q / chunk_align) * chunk_align;
         if (q <= 0) continue;
         sched_req[ns] = i; sched_q[ns] = (int32_t)q; ns++;
         left -= q;

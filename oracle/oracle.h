@@ -18,7 +18,7 @@ enum { ORACLE_OK = 0, ORACLE_INVALID_ARG = 1, ORACLE_NO_PAGES = 2, ORACLE_CAPACI
  * num_tokens, num_pages, num_deferred_decodes}, written on OK and on CAPACITY. */
 int oracle_plan(int32_t n, const int32_t* num_computed, const int32_t* num_prompt_left,
                 const int32_t* num_pages, const int64_t* bt_offset, const int32_t* bt,
-                int32_t token_budget, int32_t max_chunk, int32_t page_size,
+                int32_t token_budget, int32_t max_chunk, int32_t chunk_align, int32_t page_size,
                 int64_t num_pool_pages, int32_t cap_seqs, int32_t cap_pages,
                 int32_t* req_ids, int32_t* qo_indptr, int32_t* kv_page_indptr,
                 int32_t* kv_page_indices, int32_t* kv_last_page_len, int32_t* counts);

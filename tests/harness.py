@@ -125,4 +125,4 @@ def gpu_step(ctx, wl, plan, q_raw, k_raw, v_raw, k_cache, v_cache, want_lse=True
 def lib_plan(wl, num_computed, num_prompt_left):
     import chunked_prefill_paged_ca_amd as ca
     return ca.plan_batch(num_computed, num_prompt_left, wl.block_tables, wl.token_budget,
-                         wl.max_chunk, wl.page_size, wl.num_pool_pages)
+                         wl.max_chunk, wl.page_size, wl.num_pool_pages, chunk_align=wl.chunk_align)

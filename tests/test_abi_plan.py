@@ -30,10 +30,12 @@ def test_status_strings(L):
         assert binding.status_string(s)
 
 
-def _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=None, cap_pages=None):
-    o = oracle_mod.plan(nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, cap_pages=cap_pages)
+def _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=None, cap_pages=None,
+             align=0):
+    o = oracle_mod.plan(nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, cap_pages=cap_pages,
+                        chunk_align=align)
     p = ca.plan_batch(nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, cap_pages=cap_pages,
-                      raise_on_error=False)
+                      raise_on_error=False, chunk_align=align)
     assert p.status == o["status"], (p.status, o["status"], binding.last_error())
     if o["status"] in (0, 3):
         for k in ("num_seqs", "num_decodes", "num_tokens", "num_pages", "num_deferred_decodes"):
@@ -47,10 +49,11 @@ def _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=None, cap_
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 4, 5])
-def test_plan_matches_oracle_on_configs(L, oracle_mod, cfg):
+@pytest.mark.parametrize("align", [0, 32])
+def test_plan_matches_oracle_on_configs(L, oracle_mod, cfg, align):
     wl = make_config(cfg)
     p, o = _compare(oracle_mod, wl.num_computed, wl.num_prompt_left, wl.block_tables,
-                    wl.token_budget, wl.max_chunk, wl.page_size, wl.num_pool_pages)
+                    wl.token_budget, wl.max_chunk, wl.page_size, wl.num_pool_pages, align=align)
     assert o["status"] == 0 and o["num_tokens"] <= wl.token_budget
 
 
@@ -75,9 +78,10 @@ req = st.tuples(st.integers(0, 200), st.integers(0, 300), st.integers(0, 3))
 @given(reqs=st.lists(req, min_size=0, max_size=30), tau=st.integers(1, 700),
        mc=st.sampled_from([0, 0, 1, 7, 64]), P=st.sampled_from([1, 16, 5]),
        decode_frac=st.floats(0, 1), seed=st.integers(0, 2 ** 31 - 1),
-       bad_page=st.booleans(), cap_cut=st.integers(0, 3))
+       bad_page=st.booleans(), cap_cut=st.integers(0, 3),
+       align=st.sampled_from([0, 0, 1, 16, 32, 100]))
 def test_plan_matches_oracle_random(L, oracle_mod, reqs, tau, mc, P, decode_frac, seed,
-                                    bad_page, cap_cut):
+                                    bad_page, cap_cut, align):
     rng = np.random.default_rng(seed)
     nc, left, tables = [], [], []
     next_page = 0
@@ -95,7 +99,7 @@ def test_plan_matches_oracle_random(L, oracle_mod, reqs, tau, mc, P, decode_frac
         tables[0] = tables[0].copy()
         tables[0][0] = pool + 3
     cap_seqs = max(0, len(reqs) - cap_cut) if cap_cut == 3 else None
-    _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs)
+    _compare(oracle_mod, nc, left, tables, tau, mc, P, pool, cap_seqs=cap_seqs, align=align)
 
 
 def test_plan_rejects_bad_params(L, oracle_mod):
@@ -103,4 +107,5 @@ def test_plan_rejects_bad_params(L, oracle_mod):
     for args in ((t, 0, 0, 16, 4), (t, 8, -1, 16, 4), (t, 8, 0, 0, 4), (t, 8, 0, 16, 0)):
         _compare(oracle_mod, [1], [0], *args)
     _compare(oracle_mod, [-3], [0], t, 8, 0, 16, 4)
+    _compare(oracle_mod, [1], [0], t, 8, 0, 16, 4, align=-1)
     _compare(oracle_mod, [3], [-1], t, 8, 0, 16, 4)

@@ -180,16 +180,20 @@ def test_llama70b_share_sampled(env):
     run_and_check(ctx, oracle, wl, rows_per_seq=24, track=track, pool=(kc, vc), label="70b-share")
 
 
-@pytest.mark.parametrize("c", [512, 2048])
-def test_sweep_chunked_vs_one_shot(env, c):
-    """Config 3: one 8192-token prompt in chunks of c against the oracle (sampled rows each
-    step), then against the GPU's own one-shot run: same final cache bit for bit."""
+@pytest.mark.parametrize("c,align", [(512, 0), (2048, 0), (257, 32)])
+def test_sweep_chunked_vs_one_shot(env, c, align):
+    """Config 3: one 8192-token prompt at token budget c (chunks snapped to multiples of `align`
+    when set: 257 with 32 gives 32 chunks of 256) against the oracle (sampled rows each step),
+    then against the GPU's own one-shot run: same final cache bit for bit."""
     from chunked_prefill_paged_ca_amd.workload import make_config
     from tests import harness as H
     ctx, oracle = env
     wl = make_config(3, chunk=c)
+    wl.chunk_align = align
+    if align:
+        wl.steps = -(-8192 // (c - c % align))
     res, (kc, vc), _ = run_and_check(ctx, oracle, wl, rows_per_seq=6, check_cache=False,
-                                     label=f"sweep-c{c}")
+                                     label=f"sweep-c{c}-a{align}")
     one = make_config(3, one_shot=True)
     res1, (kc1, vc1), _ = run_and_check(ctx, oracle, one, rows_per_seq=16, check_cache=False,
                                         label="sweep-oneshot")

@@ -1,7 +1,9 @@
 """Pins for the CPU oracle: each test ties an oracle function to something other than itself.
 
 Pins used (none re-types the oracle's own formula):
-  * the pages' worked example of a 512-token budget (tests/golden/worked_example_512.json);
+  * the pages' worked example of a 512-token budget (tests/golden/worked_example_512.json), also
+    with chunk sizes aligned to 32 as the pages' tile-quantisation section describes, and a
+    downward brute-force search for aligned chunk sizes;
   * brute force: a NumPy masked-softmax matrix formulation on tiny inputs;
   * closed forms: V == 1 gives 1, one-hot V gives the probability row, kv_len 1 gives v_0,
     K == 0 gives the prefix mean, two keys give a logistic weight (scipy.special.expit);
@@ -59,6 +61,80 @@ def test_plan_worked_example(oracle_mod):
     e2 = g["expected_step2_q"]
     assert p2["num_decodes"] == e2["decodes"]
     assert q2[-1] == e2["Q"] and p2["num_tokens"] == e2["total"]
+
+
+def test_plan_worked_example_aligned(oracle_mod):
+    g = _load("worked_example_512.json")
+    nd = g["num_decodes"]
+    nc = [40] * nd + [500, 700]
+    left = [0] * nd + g["prefills_left"]
+    tables = [np.arange(200 * i, 200 * i + 200, dtype=np.int32) for i in range(nd + 2)]
+    p = oracle_mod.plan(nc, left, tables, g["token_budget"], 0, 16, 200 * (nd + 2), chunk_align=32)
+    e = g["aligned_32"]["expected_step1_q"]
+    q = np.diff(p["qo_indptr"])
+    assert list(q[nd:]) == [e["P"], e["Q"]] and p["num_tokens"] == e["total"]
+    # alignment 0 and 1 are the base rule
+    for a in (0, 1):
+        p1 = oracle_mod.plan(nc, left, tables, g["token_budget"], 0, 16, 200 * (nd + 2), chunk_align=a)
+        assert list(np.diff(p1["qo_indptr"])[nd:]) == [300, 132]
+
+
+def _aligned_chunks_brute_force(nc, left, tables, tau, mc, P, A):
+    """Prefill chunk sizes by a downward search: the largest q <= every cap that is either a
+    multiple of A or the whole rest of the prompt (no arithmetic shortcut)."""
+    budget = tau - min(tau, sum(1 for x in left if x == 0))
+    out = {}
+    for r in range(len(nc)):
+        if left[r] == 0 or budget <= 0:
+            continue
+        cap = min(left[r], budget, len(tables[r]) * P - nc[r])
+        if mc:
+            cap = min(cap, mc)
+        q = cap
+        while q > 0 and not (q == left[r] or q % A == 0):
+            q -= 1
+        if q > 0:
+            out[r] = q
+            budget -= q
+    return out
+
+
+def test_plan_alignment_brute_force(oracle_mod):
+    rng = np.random.default_rng(11)
+    P = 16
+    for trial in range(300):
+        n = int(rng.integers(1, 25))
+        nc = rng.integers(0, 300, size=n).astype(np.int32)
+        left = np.where(rng.random(n) < 0.4, 0, rng.integers(1, 400, size=n)).astype(np.int32)
+        pages = [-(-(int(nc[i]) + max(1, int(left[i]))) // P) + int(rng.integers(0, 2)) - int(rng.random() < 0.2)
+                 for i in range(n)]
+        pages = [max(p_, -(-(int(nc[i]) + 1) // P)) for i, p_ in enumerate(pages)]
+        tables = _tables(n, pages, rng.permutation(sum(pages) + 10))
+        tau = int(rng.integers(1, 600))
+        mc = int(rng.choice([0, 0, 40, 64]))
+        A = int(rng.choice([2, 16, 32, 100]))
+        p = oracle_mod.plan(nc, left, tables, tau, mc, P, sum(pages) + 10, chunk_align=A)
+        assert p["status"] == 0
+        q = np.diff(p["qo_indptr"])
+        nd = p["num_decodes"]
+        got = {int(r): int(x) for r, x in zip(p["req_ids"][nd:], q[nd:])}
+        assert got == _aligned_chunks_brute_force(nc, left, tables, tau, mc, P, A)
+        for r, x in got.items():
+            assert x == left[r] or x % A == 0
+
+
+def test_plan_aligned_sweep_shape(oracle_mod):
+    # One prompt, budget c = 257 with 32-alignment: every chunk but the last is 256.
+    L, c = 1000, 257
+    nc, left = 0, L
+    tab = [np.arange(-(-L // 16), dtype=np.int32)]
+    qs = []
+    while left > 0:
+        p = oracle_mod.plan([nc], [left], tab, c, 0, 16, 1000, chunk_align=32)
+        qs.append(int(p["num_tokens"]))
+        nc += qs[-1]
+        left -= qs[-1]
+    assert qs == [256, 256, 256, 232]
 
 
 def _check_plan_invariants(p, nc, left, tables, tau, max_chunk, P):
