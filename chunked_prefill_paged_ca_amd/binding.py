@@ -18,7 +18,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libca.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ca.h")
 
-CA_OK, CA_ERR_INVALID_ARG, CA_ERR_NO_PAGES, CA_ERR_CAPACITY, CA_ERR_UNSUPPORTED, CA_ERR_DEVICE = range(6)
+(CA_OK, CA_ERR_INVALID_ARG, CA_ERR_NO_PAGES, CA_ERR_CAPACITY, CA_ERR_UNSUPPORTED, CA_ERR_DEVICE,
+ CA_ERR_INTERNAL) = range(7)
+CA_REQ_WAITING, CA_REQ_RUNNING, CA_REQ_FINISHED = 0, 1, 2
 CA_BF16, CA_FP32 = 0, 1
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -51,6 +53,13 @@ class CaAttnDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("rope_theta", ctypes.c_float)]
+
+
+class CaSchedRequest(ctypes.Structure):
+    _fields_ = [("state", ctypes.c_int32), ("num_computed", ctypes.c_int32),
+                ("num_prompt_left", ctypes.c_int32), ("num_generated", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("num_preemptions", ctypes.c_int32),
+                ("block_table", _i32p)]
 
 
 class CaProfileRecord(ctypes.Structure):
@@ -89,8 +98,19 @@ def lib() -> ctypes.CDLL:
         L.ca_profile_enable.argtypes = [vp, ctypes.c_int]
         L.ca_profile_read.argtypes = [vp, ctypes.POINTER(CaProfileRecord), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
+        L.ca_sched_create.argtypes = [ctypes.POINTER(CaPlanParams), ctypes.POINTER(vp)]
+        L.ca_sched_destroy.argtypes = [vp]
+        L.ca_sched_add.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                   ctypes.POINTER(ctypes.c_int32)]
+        L.ca_sched_step.argtypes = [vp, ctypes.POINTER(CaPlan)]
+        L.ca_sched_commit.argtypes = [vp]
+        L.ca_sched_get.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(CaSchedRequest)]
+        L.ca_sched_free_pages.argtypes = [vp]
+        L.ca_sched_free_pages.restype = ctypes.c_int64
         for fn in ("ca_create", "ca_destroy", "ca_plan_batch", "ca_append_kv_rope",
-                   "ca_mixed_attention", "ca_profile_enable", "ca_profile_read"):
+                   "ca_mixed_attention", "ca_profile_enable", "ca_profile_read", "ca_sched_create",
+                   "ca_sched_destroy", "ca_sched_add", "ca_sched_step", "ca_sched_commit",
+                   "ca_sched_get"):
             getattr(L, fn).restype = ctypes.c_int
         L.ca_status_string.argtypes = [ctypes.c_int]
         L.ca_status_string.restype = ctypes.c_char_p
@@ -154,6 +174,65 @@ class Plan:
                 "kv_page_indptr": self.kv_page_indptr[:ns + 1].copy(),
                 "kv_page_indices": self.kv_page_indices[:npg].copy(),
                 "kv_last_page_len": self.kv_last_page_len[:ns].copy()}
+
+
+class Scheduler:
+    """ca_sched: requests, the page pool's free list and one planned round at a time."""
+
+    def __init__(self, token_budget: int, max_chunk: int, page_size: int, num_pool_pages: int,
+                 chunk_align: int = 0):
+        self.prm = CaPlanParams(int(token_budget), int(max_chunk), int(page_size), int(chunk_align),
+                                int(num_pool_pages))
+        h = ctypes.c_void_p()
+        _check(lib().ca_sched_create(ctypes.byref(self.prm), ctypes.byref(h)), "ca_sched_create")
+        self.h = h
+        self.num_pool_pages = int(num_pool_pages)
+        self.n = 0
+
+    def close(self):
+        if self.h:
+            lib().ca_sched_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, prompt_len: int, max_new_tokens: int, num_cached: int = 0,
+            cached_pages: Optional[np.ndarray] = None) -> int:
+        rid = ctypes.c_int32()
+        pages = None if cached_pages is None else np.ascontiguousarray(cached_pages, dtype=np.int32)
+        ptr = pages.ctypes.data_as(_i32p) if pages is not None and pages.size else None
+        if pages is not None and ptr is None:
+            ptr = (ctypes.c_int32 * 1)()  # an empty prefix list, not "allocate for me"
+        _check(lib().ca_sched_add(self.h, int(prompt_len), int(max_new_tokens), int(num_cached),
+                                  ptr, ctypes.byref(rid)), "ca_sched_add")
+        self.n += 1
+        return int(rid.value)
+
+    def step(self) -> Plan:
+        plan = Plan(max(self.n, 1), self.num_pool_pages)
+        st = lib().ca_sched_step(self.h, ctypes.byref(plan.c))
+        plan.status = st
+        _check(st, "ca_sched_step")
+        return plan
+
+    def commit(self):
+        _check(lib().ca_sched_commit(self.h), "ca_sched_commit")
+
+    def get(self, rid: int) -> dict:
+        r = CaSchedRequest()
+        _check(lib().ca_sched_get(self.h, int(rid), ctypes.byref(r)), "ca_sched_get")
+        table = (np.ctypeslib.as_array(r.block_table, shape=(r.num_pages,)).copy()
+                 if r.num_pages > 0 else np.zeros(0, dtype=np.int32))
+        return {"state": r.state, "num_computed": r.num_computed, "num_prompt_left": r.num_prompt_left,
+                "num_generated": r.num_generated, "num_preemptions": r.num_preemptions,
+                "block_table": table}
+
+    def free_pages(self) -> int:
+        return int(lib().ca_sched_free_pages(self.h))
 
 
 class RequestBatch:

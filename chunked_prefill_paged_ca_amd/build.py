@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libca.so")
-SOURCES = ["api.hip", "plan.cpp", "append_rope.hip", "attn_generic.hip", "attn_mixed.hip", "merge.hip"]
+SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "append_rope.hip", "attn_generic.hip", "attn_mixed.hip",
+           "merge.hip"]
 
 
 def hipcc() -> str:

@@ -919,6 +919,7 @@ const char* ca_status_string(ca_status s) {
         case CA_ERR_CAPACITY: return "plan arrays too small";
         case CA_ERR_UNSUPPORTED: return "unsupported shape";
         case CA_ERR_DEVICE: return "HIP device error";
+        case CA_ERR_INTERNAL: return "internal consistency check failed";
     }
     return "unknown status";
 }

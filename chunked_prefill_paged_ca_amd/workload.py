@@ -269,3 +269,99 @@ class StreamCursor:
             self.consumed[r] += m
             row += m
         return q, k, v
+
+
+@dataclass
+class ServeScenario:
+    """A seeded serving scenario for the multi-step loop: requests arriving over rounds.
+
+    Request r arrives before round arrival[r] with a prompt of prompt_len[r] tokens, of which
+    the first num_cached[r] are already in the cache (a prefix hit: their K/V are drawn here,
+    already rotated, like a config's history), and decodes max_new[r] steps after its prompt.
+    Its token at absolute position p has raw q, k, v that depend only on (seed, request, p), so a
+    request that is preempted and recomputed gets the very same inputs again.
+    """
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str
+    token_budget: int
+    max_chunk: int
+    chunk_align: int
+    num_pool_pages: int
+    arrival: np.ndarray
+    prompt_len: np.ndarray
+    num_cached: np.ndarray
+    max_new: np.ndarray
+    rounds: int
+    rope_theta: float = 10000.0
+    _streams: dict = field(default_factory=dict)
+
+    @property
+    def n(self) -> int:
+        return int(self.arrival.shape[0])
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def history(self, r: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Cached K (already rotated) and V of the prefix of request r: [num_cached, Hkv, d]."""
+        nc = int(self.num_cached[r])
+        rng = np.random.default_rng([self.seed, 1, r])
+        shape = (nc, self.num_kv_heads, self.head_dim)
+        k = rng.standard_normal(shape, dtype=np.float32)
+        v = rng.standard_normal(shape, dtype=np.float32)
+        return round_to_storage(k, self.dtype), round_to_storage(v, self.dtype)
+
+    def _stream(self, r: int):
+        if r not in self._streams:
+            m = int(self.prompt_len[r]) + int(self.max_new[r])
+            rng = np.random.default_rng([self.seed, 2, r])
+            q = rng.standard_normal((m, self.num_q_heads, self.head_dim), dtype=np.float32)
+            k = rng.standard_normal((m, self.num_kv_heads, self.head_dim), dtype=np.float32)
+            v = rng.standard_normal((m, self.num_kv_heads, self.head_dim), dtype=np.float32)
+            self._streams[r] = tuple(round_to_storage(x, self.dtype) for x in (q, k, v))
+        return self._streams[r]
+
+    def take(self, req_ids, starts, q_lens):
+        """Raw q, k, v rows of positions [starts[s], starts[s] + q_lens[s]) of request
+        req_ids[s], concatenated in plan order."""
+        T = int(np.sum(q_lens)) if len(q_lens) else 0
+        q = np.empty((T, self.num_q_heads, self.head_dim), dtype=np.float32)
+        k = np.empty((T, self.num_kv_heads, self.head_dim), dtype=np.float32)
+        v = np.empty((T, self.num_kv_heads, self.head_dim), dtype=np.float32)
+        row = 0
+        for r, s0, m in zip(req_ids, starts, q_lens):
+            sq, sk, sv = self._stream(int(r))
+            s0, m = int(s0), int(m)
+            q[row:row + m] = sq[s0:s0 + m]
+            k[row:row + m] = sk[s0:s0 + m]
+            v[row:row + m] = sv[s0:s0 + m]
+            row += m
+        return q, k, v
+
+
+def make_serve_scenario(seed: int = 3, *, n: int = 14, rounds: int = 60, pool_pages: int = 48,
+                        token_budget: int = 96, max_chunk: int = 0, chunk_align: int = 0,
+                        dtype: str = "bf16", heads=(16, 4, 128)) -> ServeScenario:
+    """Requests arriving over the first half of the rounds: prompts of 8..300 tokens (a third
+    with a cached prefix of up to half the prompt), 2..24 decode steps each.  The pool is small
+    enough that decodes run out of pages and get preempted."""
+    rng = np.random.default_rng([seed, 9])
+    arrival = np.sort(rng.integers(0, rounds // 2, size=n))
+    arrival[0] = 0
+    prompt = rng.integers(8, 301, size=n)
+    cached = np.where(rng.random(n) < 1 / 3, (prompt * rng.uniform(0, 0.5, size=n)).astype(np.int64), 0)
+    max_new = rng.integers(2, 25, size=n)
+    Hq, Hkv, d = heads
+    return ServeScenario(name=f"serving loop: {n} requests, pool {pool_pages} pages, tau={token_budget}",
+                         seed=seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, page_size=16,
+                         dtype=dtype, token_budget=token_budget, max_chunk=max_chunk,
+                         chunk_align=chunk_align, num_pool_pages=pool_pages,
+                         arrival=arrival.astype(np.int32), prompt_len=prompt.astype(np.int32),
+                         num_cached=cached.astype(np.int32), max_new=max_new.astype(np.int32),
+                         rounds=rounds)

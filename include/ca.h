@@ -54,7 +54,8 @@ typedef enum {
     CA_ERR_NO_PAGES = 2,    /* a decode's block table has no free slot for its new token */
     CA_ERR_CAPACITY = 3,    /* caller arrays too small; required sizes are in the counts */
     CA_ERR_UNSUPPORTED = 4, /* a valid but unimplemented shape (e.g. head_dim not 64/128) */
-    CA_ERR_DEVICE = 5       /* a HIP runtime error */
+    CA_ERR_DEVICE = 5,      /* a HIP runtime error */
+    CA_ERR_INTERNAL = 6     /* a consistency check inside the library failed (a library bug) */
 } ca_status;
 
 typedef enum { CA_BF16 = 0, CA_FP32 = 1 } ca_dtype;
@@ -202,6 +203,64 @@ enum {
 
 ca_status ca_profile_enable(ca_ctx* ctx, int enable);
 ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int32_t* count);
+
+/*
+ * ---- Multi-step driver: ca_sched (host only, no device work) ----
+ * The serving loop around ca_plan_batch, following [SF] "六·补二、调度器每一轮在做什么" (each round:
+ * running decodes first, one token each; a decode that needs KV space when none is left is
+ * preempted and later recomputed from its first token; the budget left goes to prefill chunks;
+ * an unfinished prompt is taken up again next round) and [SS] "一个 512-token 预算的例子" step 4 (a
+ * prefill that finishes its prompt is a decode from the next round on).
+ *   - The scheduler owns the page pool [0, num_pool_pages) as a first-in first-out free list
+ *     (initially 0, 1, ..., N-1; pages are taken from the front and returned to the back).
+ *   - ca_sched_step plans one round over the unfinished requests in admission order, with the
+ *     rules and parameters of ca_plan_batch, after giving each scheduled request the pages its
+ *     new tokens need: a decode whose token needs a page when the free list is empty is
+ *     preempted instead (its pages go back to the free list; it waits, not scheduled this round,
+ *     to recompute all the tokens it had cached), and a chunk is also cut to the slots its pages
+ *     plus the free list can hold (then aligned again).  plan->req_ids holds request ids.  The
+ *     plan arrays need cap_seqs >= unfinished requests and cap_pages >= their pages.
+ *   - The caller then runs the round (ca_append_kv_rope + ca_mixed_attention with the plan) and
+ *     calls ca_sched_commit: every scheduled request advances by its tokens; a prefill that
+ *     reaches the end of its prompt starts decoding (or finishes, when it has already run
+ *     max_new_tokens decode steps); a decode step counts towards max_new_tokens, and a request
+ *     that reaches it finishes and returns its pages.
+ * Not thread-safe: one caller at a time per ca_sched.
+ */
+typedef struct ca_sched ca_sched;
+
+enum { CA_REQ_WAITING = 0, CA_REQ_RUNNING = 1, CA_REQ_FINISHED = 2 };
+
+typedef struct {
+    int32_t state;              /* CA_REQ_WAITING (prompt or recompute left), _RUNNING (decoding), _FINISHED */
+    int32_t num_computed;       /* tokens in the cache */
+    int32_t num_prompt_left;    /* tokens left to prefill (0 unless waiting) */
+    int32_t num_generated;      /* decode steps run */
+    int32_t num_pages;          /* entries of block_table */
+    int32_t num_preemptions;
+    const int32_t* block_table; /* host memory owned by the scheduler; valid until its next call */
+} ca_sched_request;
+
+/* Errors: CA_ERR_INVALID_ARG for null pointers or parameters ca_plan_batch would reject. */
+ca_status ca_sched_create(const ca_plan_params* params, ca_sched** out);
+ca_status ca_sched_destroy(ca_sched* s);
+/* Admit a request of prompt_len tokens whose first num_cached (< prompt_len) are already in the
+ * cache (a prefix hit): in cached_pages (ceil(num_cached / P) distinct free pages, which leave
+ * the free list), or, with cached_pages NULL, in pages taken from the free list for the caller
+ * to fill (read them with ca_sched_get).  It decodes max_new_tokens steps after its prompt.
+ * *id receives the request id (0, 1, ... in admission order).  Errors: CA_ERR_INVALID_ARG (bad
+ * sizes, a cached page outside the pool or not free, a step awaiting commit), CA_ERR_NO_PAGES
+ * (not enough free pages for the prefix). */
+ca_status ca_sched_add(ca_sched* s, int32_t prompt_len, int32_t max_new_tokens, int32_t num_cached,
+                       const int32_t* cached_pages, int32_t* id);
+/* Plan the next round into `plan` (see above).  Errors: those of ca_plan_batch, and
+ * CA_ERR_INVALID_ARG when the previous round is not committed. */
+ca_status ca_sched_step(ca_sched* s, ca_plan* plan);
+/* Advance the requests of the planned round.  CA_ERR_INVALID_ARG when no round is planned. */
+ca_status ca_sched_commit(ca_sched* s);
+ca_status ca_sched_get(const ca_sched* s, int32_t id, ca_sched_request* out);
+/* Pages on the free list (-1 for a null scheduler). */
+int64_t ca_sched_free_pages(const ca_sched* s);
 
 const char* ca_status_string(ca_status s);
 /* Detail message of the calling thread's last failed call ("" if none). */

@@ -233,3 +233,181 @@ class Session:
             if self.num_prompt_left[r] > 0:
                 self.num_prompt_left[r] -= e - b
         return {"q_rot": q_rot, "k_rot": k_rot, "o": o, "lse": lse, "pos": pos}
+
+
+# ---------------------------------------------------------------------------------------------
+# Multi-step serving loop
+# ---------------------------------------------------------------------------------------------
+
+class SchedModel:
+    """Plain model of the serving loop around the plan, round by round.
+
+    magicnetworld.com "分块预填充与 Stall-free 调度", section "六·补二、调度器每一轮在做什么": in each
+    round every running decode takes one token, and one that needs KV space when none is left is
+    preempted (its cache is dropped and it is recomputed from its first token later); the budget
+    left goes to prefill chunks, and an unfinished prompt is continued next round.
+    pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "一个 512-token 预算的例子", step 4: a prompt
+    that finishes is a decode from the next round on.  The packing of a round is `plan` above.
+
+    Readings where the pages are silent (the same ones the library takes): the page pool is a
+    first-in first-out free list starting as 0 .. N-1; a preempted request is not scheduled again
+    in the round that preempted it; a chunk is also cut to the slots its pages and the free list
+    can hold; a request decodes max_new steps after its prompt, then its pages go back to the
+    free list (in block-table order).
+    """
+
+    WAITING, RUNNING, FINISHED = 0, 1, 2
+
+    def __init__(self, token_budget: int, max_chunk: int, page_size: int, num_pool_pages: int,
+                 chunk_align: int = 0):
+        from collections import deque
+        self.tau, self.mc, self.P, self.A = token_budget, max_chunk, page_size, chunk_align
+        self.N = num_pool_pages
+        self.free = deque(range(num_pool_pages))
+        self.reqs: List[Dict] = []
+        self.pending = None
+
+    def add(self, prompt_len: int, max_new: int, num_cached: int = 0) -> int:
+        """A request whose first num_cached tokens are already cached, in pages taken from the
+        free list (the caller fills them)."""
+        assert 1 <= prompt_len and 0 <= num_cached < prompt_len and max_new >= 0
+        n_pages = -(-num_cached // self.P)
+        assert len(self.free) >= n_pages
+        pages = [self.free.popleft() for _ in range(n_pages)]
+        self.reqs.append({"state": self.WAITING, "nc": num_cached, "left": prompt_len - num_cached,
+                          "generated": 0, "max_new": max_new, "pages": pages, "preemptions": 0})
+        return len(self.reqs) - 1
+
+    def _cut(self, q: int, left: int) -> int:
+        return q - q % self.A if self.A > 1 and q < left else q
+
+    def step(self) -> Dict:
+        assert self.pending is None, "commit the previous round first"
+        budget = self.tau
+        held_back = set()
+        # decodes: one token each, in admission order, while the budget lasts
+        for i, r in enumerate(self.reqs):
+            if r["state"] != self.RUNNING or budget == 0:
+                continue
+            if r["nc"] + 1 > len(r["pages"]) * self.P:
+                if not self.free:
+                    self.free.extend(r["pages"])
+                    r["pages"] = []
+                    r["left"], r["nc"] = r["nc"], 0
+                    r["state"] = self.WAITING
+                    r["preemptions"] += 1
+                    held_back.add(i)
+                    continue
+                r["pages"].append(self.free.popleft())
+            budget -= 1
+        # prefill chunks from what is left, in admission order
+        for i, r in enumerate(self.reqs):
+            if budget <= 0:
+                break
+            if r["state"] != self.WAITING or i in held_back:
+                continue
+            q = min(r["left"], budget)
+            if self.mc:
+                q = min(q, self.mc)
+            q = self._cut(q, r["left"])
+            fits = (len(r["pages"]) + len(self.free)) * self.P - r["nc"]
+            if q > fits:
+                q = self._cut(fits, r["left"])
+            if q <= 0:
+                continue
+            while len(r["pages"]) * self.P < r["nc"] + q:
+                r["pages"].append(self.free.popleft())
+            budget -= q
+        # the round's plan over the requests still in play
+        ids = [i for i, r in enumerate(self.reqs) if r["state"] != self.FINISHED and i not in held_back]
+        rs = [self.reqs[i] for i in ids]
+        p = plan([r["nc"] for r in rs], [r["left"] if r["state"] == self.WAITING else 0 for r in rs],
+                 [np.asarray(r["pages"], dtype=np.int32) for r in rs], self.tau, self.mc, self.P,
+                 self.N, chunk_align=self.A)
+        assert p["status"] == OK, p["status"]
+        p["req_ids"] = np.asarray([ids[k] for k in p["req_ids"]], dtype=np.int32)
+        self.pending = list(zip(p["req_ids"].tolist(), np.diff(p["qo_indptr"]).tolist()))
+        return p
+
+    def commit(self):
+        assert self.pending is not None, "no planned round"
+        for i, q in self.pending:
+            r = self.reqs[i]
+            r["nc"] += q
+            if r["state"] == self.WAITING:
+                r["left"] -= q
+                if r["left"] == 0:
+                    r["state"] = self.FINISHED if r["generated"] >= r["max_new"] else self.RUNNING
+            else:
+                r["generated"] += 1
+                if r["generated"] >= r["max_new"]:
+                    r["state"] = self.FINISHED
+            if r["state"] == self.FINISHED:
+                self.free.extend(r["pages"])
+                r["pages"] = []
+        self.pending = None
+
+
+class ServeSession:
+    """The serving loop (SchedModel) with the oracle's dense per-request cache.
+
+    sc is a ServeScenario: request r is admitted with its cached prefix (sc.history) and later
+    rounds append its tokens at their absolute positions.  A request the loop preempted starts
+    again from an empty cache (its recompute appends every token again).
+    """
+
+    def __init__(self, sc):
+        self.sc = sc
+        self.model = SchedModel(sc.token_budget, sc.max_chunk, sc.page_size, sc.num_pool_pages,
+                                sc.chunk_align)
+        self.k: Dict[int, np.ndarray] = {}
+        self.v: Dict[int, np.ndarray] = {}
+
+    def free_pages(self) -> int:
+        return len(self.model.free)
+
+    def add(self, r: int) -> int:
+        sc = self.sc
+        i = self.model.add(int(sc.prompt_len[r]), int(sc.max_new[r]), int(sc.num_cached[r]))
+        hk, hv = sc.history(r)
+        self.k[i] = hk.astype(np.float64)
+        self.v[i] = hv.astype(np.float64)
+        return i
+
+    def plan(self) -> Dict:
+        p = self.model.step()
+        for i, r in enumerate(self.model.reqs):
+            if r["nc"] == 0:
+                shape = (0, self.sc.num_kv_heads, self.sc.head_dim)
+                self.k[i] = np.zeros(shape)
+                self.v[i] = np.zeros(shape)
+        return p
+
+    def starts(self, p: Dict) -> np.ndarray:
+        """First absolute position of each scheduled sequence of the planned round."""
+        return np.asarray([self.model.reqs[int(i)]["nc"] for i in p["req_ids"]], dtype=np.int32)
+
+    def step(self, p: Dict, q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray,
+             nthreads: Optional[int] = None) -> Dict:
+        """Append the round's tokens, attend every row, then commit the round."""
+        sc = self.sc
+        T = int(p["num_tokens"])
+        qo = p["qo_indptr"]
+        pos = np.empty(T, dtype=np.int32)
+        for s, st in enumerate(self.starts(p)):
+            b, e = int(qo[s]), int(qo[s + 1])
+            pos[b:e] = st + np.arange(e - b, dtype=np.int32)
+        q_rot = round_to(rope(q_raw, pos, sc.rope_theta), sc.dtype)
+        k_rot = round_to(rope(k_raw, pos, sc.rope_theta), sc.dtype)
+        v_new = np.asarray(v_raw, dtype=np.float64)
+        o = np.full((T, sc.num_q_heads, sc.head_dim), np.nan)
+        lse = np.full((T, sc.num_q_heads), np.nan)
+        for s, i in enumerate(p["req_ids"]):
+            i = int(i)
+            b, e = int(qo[s]), int(qo[s + 1])
+            self.k[i] = np.concatenate([self.k[i], k_rot[b:e]], axis=0)
+            self.v[i] = np.concatenate([self.v[i], v_new[b:e]], axis=0)
+            o[b:e], lse[b:e] = attention(q_rot[b:e], pos[b:e], self.k[i], self.v[i], sc.sm_scale,
+                                         nthreads)
+        self.model.commit()
+        return {"q_rot": q_rot, "o": o, "lse": lse, "pos": pos}

@@ -80,6 +80,18 @@ def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None
         _scatter(k_cache, v_cache, pi, si, torch.from_numpy(hk), torch.from_numpy(hv))
 
 
+def write_positions(k_cache, v_cache, table: np.ndarray, P: int, k: np.ndarray, v: np.ndarray):
+    """Scatter dense k, v [n, Hkv, d] to positions 0..n-1 of a request with block table `table`."""
+    import torch
+    n = k.shape[0]
+    if n == 0:
+        return
+    pages, slots = _slots(np.asarray(table), P, 0, n)
+    dev = k_cache.device
+    _scatter(k_cache, v_cache, torch.from_numpy(pages).to(dev), torch.from_numpy(slots).to(dev),
+             torch.from_numpy(np.ascontiguousarray(k)), torch.from_numpy(np.ascontiguousarray(v)))
+
+
 def read_dense(k_cache, v_cache, table: np.ndarray, P: int, kv_len: int):
     """Gather positions 0..kv_len-1 of one request back into dense [kv_len, Hkv, d] float64."""
     import torch

@@ -109,3 +109,102 @@ def test_plan_rejects_bad_params(L, oracle_mod):
     _compare(oracle_mod, [-3], [0], t, 8, 0, 16, 4)
     _compare(oracle_mod, [1], [0], t, 8, 0, 16, 4, align=-1)
     _compare(oracle_mod, [3], [-1], t, 8, 0, 16, 4)
+
+
+# ------------------------------------------------------------------------------------------
+# ca_sched: the serving loop, library against the oracle's model, round by round
+# ------------------------------------------------------------------------------------------
+
+def _run_loop_both(oracle_mod, rng, N, tau, mc, align, rounds, arrivals, P=16):
+    lib_s = ca.Scheduler(tau, mc, P, N, chunk_align=align)
+    ref = oracle_mod.SchedModel(tau, mc, P, N, align)
+    pending = list(arrivals)
+    preempts = 0
+    for rnd in range(rounds):
+        while pending and pending[0][0] <= rnd:
+            _, L, new, c = pending[0]
+            assert lib_s.free_pages() == len(ref.free)
+            if len(ref.free) < -(-c // P):
+                break
+            pending.pop(0)
+            assert lib_s.add(L, new, c) == ref.add(L, new, c)
+        p = lib_s.step()
+        o = ref.step()
+        for k in ("num_seqs", "num_decodes", "num_tokens", "num_pages", "num_deferred_decodes"):
+            assert getattr(p, k) == o[k], (rnd, k)
+        a = p.arrays()
+        for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
+            assert np.array_equal(a[k], o[k]), (rnd, k)
+        lib_s.commit()
+        ref.commit()
+        for i, r in enumerate(ref.reqs):
+            g = lib_s.get(i)
+            assert g["state"] == r["state"] and g["num_computed"] == r["nc"], (rnd, i)
+            assert g["num_generated"] == r["generated"] and g["num_preemptions"] == r["preemptions"]
+            assert np.array_equal(g["block_table"], np.asarray(r["pages"], dtype=np.int32))
+            preempts += r["preemptions"]
+    return preempts
+
+
+def test_sched_matches_oracle_random(L, oracle_mod):
+    rng = np.random.default_rng(5)
+    total_preempts = 0
+    for trial in range(60):
+        N = int(rng.integers(3, 60))
+        tau = int(rng.integers(1, 300))
+        mc = int(rng.choice([0, 0, 24, 64]))
+        align = int(rng.choice([0, 0, 8, 32]))
+        arr = []
+        for _ in range(int(rng.integers(1, 16))):
+            Lp = int(rng.integers(1, 200))
+            c = int(rng.integers(0, Lp)) if rng.random() < 0.3 else 0
+            arr.append((int(rng.integers(0, 40)), Lp, int(rng.integers(0, 10)), c))
+        arr.sort(key=lambda x: x[0])
+        total_preempts += _run_loop_both(oracle_mod, rng, N, tau, mc, align, 90, arr)
+    assert total_preempts > 0
+
+
+def test_sched_worked_example_library(L):
+    s = ca.Scheduler(512, 0, 16, 20000)
+    for _ in range(80):
+        s.add(2, 10, 1)
+    s.step()
+    s.commit()
+    P = s.add(1500, 10, 1200)
+    Q = s.add(2948, 10, 2048)
+    p = s.step()
+    a = p.arrays()
+    assert p.num_decodes == 80 and list(np.diff(a["qo_indptr"])[-2:]) == [300, 132]
+    assert list(a["req_ids"][-2:]) == [P, Q]
+    s.commit()
+    p = s.step()
+    assert p.num_decodes == 81 and p.num_tokens == 512
+
+
+def test_sched_errors(L):
+    s = ca.Scheduler(64, 0, 16, 4)
+    with pytest.raises(binding.CaError):
+        s.commit()                      # nothing planned
+    with pytest.raises(binding.CaError):
+        s.add(10, 1, 10)                # num_cached must stay below the prompt
+    with pytest.raises(binding.CaError):
+        s.add(0, 1)                     # empty prompt
+    with pytest.raises(binding.CaError):
+        s.add(100, 1, 80)               # prefix needs 5 pages, the pool has 4
+    with pytest.raises(binding.CaError):
+        s.add(40, 1, 20, cached_pages=np.array([1, 7], dtype=np.int32))  # page outside the pool
+    r = s.add(40, 1, 20, cached_pages=np.array([2, 3], dtype=np.int32))
+    assert s.free_pages() == 2 and list(s.get(r)["block_table"]) == [2, 3]
+    with pytest.raises(binding.CaError):
+        s.add(40, 1, 20, cached_pages=np.array([3, 0], dtype=np.int32))  # page 3 is taken
+    assert s.free_pages() == 2
+    s.step()
+    with pytest.raises(binding.CaError):
+        s.step()                        # the planned round is not committed
+    with pytest.raises(binding.CaError):
+        s.add(5, 1)                     # nor can requests join before the commit
+    s.commit()
+    with pytest.raises(binding.CaError):
+        s.get(7)
+    with pytest.raises(binding.CaError):
+        ca.Scheduler(64, 0, 16, 4, chunk_align=-2)

@@ -204,6 +204,68 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
+def test_serving_loop_matches_oracle(env):
+    """ca_sched driving 60 rounds of a serving loop (arrivals, prefix hits, finishing requests
+    and preemptions on a 48-page pool) through append + attention: every round's plan equals the
+    oracle's loop bit for bit, every row's output is within tolerance, and the cache of every
+    scheduled request holds exactly the oracle's tokens (recomputed ones included)."""
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import make_serve_scenario
+    from tests import harness as H
+    ctx, oracle = env
+    sc = make_serve_scenario()
+    dt = sc.dtype
+    sched = ca.Scheduler(sc.token_budget, sc.max_chunk, sc.page_size, sc.num_pool_pages, sc.chunk_align)
+    serve = oracle.ServeSession(sc)
+    k_cache, v_cache = H.alloc_pool(sc)
+    added, preempted, rows = 0, 0, 0
+    for rnd in range(sc.rounds):
+        while added < sc.n and sc.arrival[added] <= rnd:
+            assert sched.free_pages() == serve.free_pages()
+            if serve.free_pages() < -(-int(sc.num_cached[added]) // sc.page_size):
+                break
+            rid = sched.add(int(sc.prompt_len[added]), int(sc.max_new[added]), int(sc.num_cached[added]))
+            assert rid == serve.add(added) == added
+            hk, hv = sc.history(added)
+            H.write_positions(k_cache, v_cache, sched.get(rid)["block_table"], sc.page_size, hk, hv)
+            added += 1
+        ref_plan = serve.plan()
+        plan = sched.step()
+        a = plan.arrays()
+        for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
+            assert np.array_equal(a[k], ref_plan[k]), (rnd, k)
+        if plan.num_tokens == 0:
+            serve.step(ref_plan, *sc.take([], [], []))
+            sched.commit()
+            continue
+        q, k, v = sc.take(ref_plan["req_ids"], serve.starts(ref_plan), np.diff(ref_plan["qo_indptr"]))
+        q_out, o, lse = H.gpu_step(ctx, sc, plan, q, k, v, k_cache, v_cache)
+        torch.cuda.synchronize()
+        ref = serve.step(ref_plan, q, k, v)
+        sched.commit()
+        go = o.float().cpu().numpy().astype(np.float64)
+        gl = lse.cpu().numpy().astype(np.float64)
+        uq = H.ulp_distance(q_out.float().cpu().numpy().astype(np.float64), ref["q_rot"], dt)
+        err = np.abs(go - ref["o"]).max()
+        lerr = np.abs(gl - ref["lse"]).max()
+        rows += plan.num_tokens
+        _log(f"[serving] round {rnd}: T={plan.num_tokens} seqs={plan.num_seqs} decodes={plan.num_decodes} "
+             f"free pages={sched.free_pages()} max|do|={err:.3e} max|dlse|={lerr:.3e}")
+        assert uq.max() <= 1.0 and err <= TOL_O[dt] and lerr <= TOL_LSE[dt], (rnd, uq.max(), err, lerr)
+        for i in ref_plan["req_ids"]:
+            g = sched.get(int(i))
+            if g["state"] == ca.CA_REQ_FINISHED:
+                continue
+            gk, gv = H.read_dense(k_cache, v_cache, g["block_table"], sc.page_size, g["num_computed"])
+            assert H.ulp_distance(gk, serve.k[int(i)], dt).max() <= 1.0, (rnd, i, "k cache")
+            assert np.array_equal(gv, serve.v[int(i)]), (rnd, i, "v cache")
+    states = [sched.get(i)["state"] for i in range(added)]
+    preempted = sum(sched.get(i)["num_preemptions"] for i in range(added))
+    _log(f"[serving] {rows} rows, {states.count(ca.CA_REQ_FINISHED)} of {added} finished, {preempted} preemptions")
+    assert added == sc.n and preempted > 0 and states.count(ca.CA_REQ_FINISHED) >= sc.n - 2
+
+
 @pytest.mark.parametrize("mode", ["split", "few-decode-wgs", "decode-only"])
 def test_attention_launch_layouts(env, mode):
     """The Mistral-7B step through the other layouts of the attention launch: decode and chunk

@@ -4,6 +4,9 @@ Pins used (none re-types the oracle's own formula):
   * the pages' worked example of a 512-token budget (tests/golden/worked_example_512.json), also
     with chunk sizes aligned to 32 as the pages' tile-quantisation section describes, and a
     downward brute-force search for aligned chunk sizes;
+  * the serving loop: the worked example over two rounds (P becomes a decode, Q gets 431), the
+    pages' rounds-to-first-token example (tests/golden/rounds_to_first_token.json), and pool /
+    preemption invariants over random arrivals;
   * brute force: a NumPy masked-softmax matrix formulation on tiny inputs;
   * closed forms: V == 1 gives 1, one-hot V gives the probability row, kv_len 1 gives v_0,
     K == 0 gives the prefix mean, two keys give a logistic weight (scipy.special.expit);
@@ -135,6 +138,100 @@ def test_plan_aligned_sweep_shape(oracle_mod):
         nc += qs[-1]
         left -= qs[-1]
     assert qs == [256, 256, 256, 232]
+
+
+# ------------------------------------------------------------------------------------------
+# Serving loop (SchedModel)
+# ------------------------------------------------------------------------------------------
+
+def _running_decodes(m, n, ctx=2048, max_new=1000):
+    """n requests that are decoding: one prefill round of their last prompt token first."""
+    ids = [m.add(ctx + 1, max_new, ctx) for _ in range(n)]
+    m.step()
+    m.commit()
+    assert all(m.reqs[i]["state"] == m.RUNNING for i in ids)
+    return ids
+
+
+def test_sched_worked_example_two_rounds(oracle_mod):
+    g = _load("worked_example_512.json")
+    nd = g["num_decodes"]
+    m = oracle_mod.SchedModel(g["token_budget"], 0, 16, 20000)
+    _running_decodes(m, nd, ctx=1)
+    P = m.add(1500, 10, 1500 - g["prefills_left"][0])
+    Q = m.add(2948, 10, 2948 - g["prefills_left"][1])
+    e1, e2 = g["expected_step1_q"], g["expected_step2_q"]
+    p = m.step()
+    q = np.diff(p["qo_indptr"])
+    assert p["num_decodes"] == nd and list(q[nd:]) == [e1["P"], e1["Q"]] and p["num_tokens"] == e1["total"]
+    assert list(p["req_ids"][nd:]) == [P, Q]
+    m.commit()
+    assert m.reqs[P]["state"] == m.RUNNING and m.reqs[Q]["left"] == 900 - 132
+    p = m.step()
+    q = np.diff(p["qo_indptr"])
+    assert p["num_decodes"] == e2["decodes"] and q[-1] == e2["Q"] and p["num_tokens"] == e2["total"]
+
+
+def test_sched_rounds_to_first_token(oracle_mod):
+    g = _load("rounds_to_first_token.json")
+    D, C = g["decodes"], g["prefill_share"]
+    m = oracle_mod.SchedModel(D + C, 0, 16, 100000)
+    _running_decodes(m, D)
+    r = m.add(g["prompt_len"], 5)
+    rounds = 0
+    while m.reqs[r]["state"] == m.WAITING:
+        p = m.step()
+        assert p["num_decodes"] == D
+        m.commit()
+        rounds += 1
+    assert rounds == g["expected_rounds"]
+
+
+def test_sched_invariants_random(oracle_mod):
+    """Pool conservation, table sizes, what a preemption does, exactly max_new decode steps per
+    finished request, budget per round."""
+    rng = np.random.default_rng(21)
+    P = 16
+    preempted_total = 0
+    for trial in range(40):
+        N = int(rng.integers(4, 40))
+        tau = int(rng.integers(1, 200))
+        m = oracle_mod.SchedModel(tau, int(rng.choice([0, 0, 32])), P, N, int(rng.choice([0, 0, 16])))
+        arrivals = sorted(rng.integers(0, 30, size=int(rng.integers(1, 12))).tolist())
+        steps_run = {}
+        for rnd in range(80):
+            while arrivals and arrivals[0] <= rnd:
+                L = int(rng.integers(1, 120))
+                c = int(rng.integers(0, L)) if rng.random() < 0.3 else 0
+                if len(m.free) < -(-c // P):
+                    break
+                arrivals.pop(0)
+                m.add(L, int(rng.integers(0, 8)), c)
+            states_before = [(r["state"], r["nc"]) for r in m.reqs]
+            p = m.step()
+            assert p["num_tokens"] <= tau
+            for i, r in enumerate(m.reqs):
+                if states_before[i][0] == m.RUNNING and r["state"] == m.WAITING:
+                    preempted_total += 1
+                    assert r["nc"] == 0 and r["left"] == states_before[i][1] and not r["pages"]
+                    assert i not in p["req_ids"]
+            for s, i in enumerate(p["req_ids"]):
+                if s < p["num_decodes"]:
+                    steps_run[i] = steps_run.get(i, 0) + 1
+            m.commit()
+            owned = [pg for r in m.reqs for pg in r["pages"]]
+            assert len(owned) == len(set(owned)) and len(owned) + len(m.free) == N
+            assert set(owned).isdisjoint(set(m.free))
+            for r in m.reqs:
+                if r["state"] == m.FINISHED:
+                    assert not r["pages"]
+                else:
+                    assert len(r["pages"]) == -(-r["nc"] // P)
+        for i, r in enumerate(m.reqs):
+            assert steps_run.get(i, 0) == r["generated"]
+            if r["state"] == m.FINISHED:
+                assert r["generated"] == r["max_new"]
+    assert preempted_total > 0  # the random pools are small enough to exercise preemption
 
 
 def _check_plan_invariants(p, nc, left, tables, tau, max_chunk, P):
