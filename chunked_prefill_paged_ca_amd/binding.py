@@ -188,6 +188,7 @@ class Scheduler:
         self.h = h
         self.num_pool_pages = int(num_pool_pages)
         self.n = 0
+        self._plan = None
 
     def close(self):
         if self.h:
@@ -213,7 +214,10 @@ class Scheduler:
         return int(rid.value)
 
     def step(self) -> Plan:
-        plan = Plan(max(self.n, 1), self.num_pool_pages)
+        """Plan the next round.  The returned Plan's arrays are reused by the next step()."""
+        if self._plan is None or self._plan.c.cap_seqs < self.n:
+            self._plan = Plan(max(2 * self.n, 16), self.num_pool_pages)
+        plan = self._plan
         st = lib().ca_sched_step(self.h, ctypes.byref(plan.c))
         plan.status = st
         _check(st, "ca_sched_step")

@@ -46,7 +46,9 @@ struct DevBuf {
             ptr = nullptr;
             bytes = 0;
         }
-        size_t cap = want + want / 4 + 4096;
+        // doubling with a 1 MiB floor: a serving loop whose plans grow over time reallocates
+        // (a stream synchronisation plus hipFree/hipMalloc) only a few times
+        size_t cap = want * 2 > (size_t(1) << 20) ? want * 2 : (size_t(1) << 20);
         hipError_t e = hipMalloc(&ptr, cap);
         if (e != hipSuccess) { ptr = nullptr; return e; }
         bytes = cap;
@@ -106,7 +108,7 @@ struct Staging {
             host[i] = nullptr;
             dev[i] = nullptr;
             cap[i] = 0;
-            size_t want = (bytes + bytes / 4 + 4096 + 15) / 16 * 16;
+            size_t want = bytes * 2 > (size_t(1) << 20) ? bytes * 2 : (size_t(1) << 20);  // see DevBuf
             hipError_t e = hipHostMalloc(&host[i], want, hipHostMallocMapped | hipHostMallocCoherent);
             if (e != hipSuccess) { host[i] = nullptr; return e; }
             e = hipHostGetDevicePointer(&dev[i], host[i], 0);
