@@ -245,7 +245,8 @@ typedef struct {
 ca_status ca_sched_create(const ca_plan_params* params, ca_sched** out);
 ca_status ca_sched_destroy(ca_sched* s);
 /* Admit a request of prompt_len tokens whose first num_cached (< prompt_len) are already in the
- * cache (a prefix hit): in cached_pages (ceil(num_cached / P) distinct free pages, which leave
+ * cache (a prefix hit; [CP] "7.1 chunked prefill 与 prefix caching 的相互影响": the rounds then
+ * chunk only the tokens after the cached prefix): in cached_pages (ceil(num_cached / P) distinct free pages, which leave
  * the free list), or, with cached_pages NULL, in pages taken from the free list for the caller
  * to fill (read them with ca_sched_get).  It decodes max_new_tokens steps after its prompt.
  * *id receives the request id (0, 1, ... in admission order).  Errors: CA_ERR_INVALID_ARG (bad
