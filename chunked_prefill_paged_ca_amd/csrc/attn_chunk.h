@@ -144,11 +144,16 @@ __device__ __forceinline__ void chunk_item(
 #pragma unroll
     for (int o_ = 32; o_ >= 1; o_ >>= 1) wmin = min(wmin, __shfl_xor(wmin, o_, 64));
 
+    // Per column: running max m (log2 units), weight sum l (this lane's keys; summed over the
+    // lane groups at the end) and the O^T accumulator.  m starts at a finite floor far below any
+    // score, so a column that has seen no key yet needs no special case: its masked scores (-inf)
+    // give weight 0, and the first real score always raises m.
+    constexpr float kNoKey = -1.0e30f;
     floatx4 acc[kTiles][D / 16];
     float m[kTiles], l[kTiles];
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
-        m[nt] = -INFINITY;
+        m[nt] = kNoKey;
         l[nt] = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -157,18 +162,34 @@ __device__ __forceinline__ void chunk_item(
     // One 32-key block held in LDS stage `stg`.  Blocks wholly inside every column's visible
     // range (the common case) skip the causal mask; the mask test is wave-uniform.
     auto consume = [&](const uint16_t* stg, int key0) {
+        // All of the block's K fragments are requested before the first MFMA, and all of its V
+        // fragments right after the last QK MFMA, so the LDS latency is paid once per operand
+        // (under the MFMAs, then under the softmax) instead of once per pair of reads.
+        bf16x8 kf[2][D / 32];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                // tile t = page t: row c = slot c, dims 32 kk + 8 q .. = 8-dim block 4 kk + q
+                kf[t][kk] = lds_frag(stg + 16 * D * t + 512 * kk + 8 * lane);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs that use them
         floatx4 st[kTiles][2];
 #pragma unroll
         for (int nt = 0; nt < kTiles; ++nt) st[nt][0] = st[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                // tile t = page t: row c = slot c, dims 32 kk + 8 q .. = 8-dim block 4 kk + q
-                const bf16x8 kf = lds_frag(stg + 16 * D * t + 512 * kk + 8 * lane);
+            for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-                for (int nt = 0; nt < kTiles; ++nt) st[nt][t] = mfma16x16x32(kf, qf[nt][kk], st[nt][t]);
-            }
+                for (int nt = 0; nt < kTiles; ++nt) st[nt][t] = mfma16x16x32(kf[t][kk], qf[nt][kk], st[nt][t]);
+        // a fragment's two halves (pages a and b) sit 16 D halves apart: read as one pair, kept
+        // apart from the other fragments' reads so the pair is what gets merged into one
+        // two-address LDS read, straight into the fragment's registers
+        bf16x8 vf[D / 16];
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            vf[mt] = lds_frag_pair(stg + 32 * D + 256 * mt + 4 * lane, stg + 48 * D + 256 * mt + 4 * lane);
+            __builtin_amdgcn_sched_barrier(0);
         }
         const bool full = key0 + 31 <= wmin;
         bf16x8 pf[kTiles];
@@ -207,22 +228,19 @@ __device__ __forceinline__ void chunk_item(
                 for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] *= alpha;
                 m[nt] = grow ? bm : m[nt];
             }
-            const float m_use = (m[nt] == -INFINITY) ? 0.0f : m[nt];  // column with no key yet
             float pr[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                pr[jj] = exp2_fast(__builtin_fmaf(sc[jj], scale_log2, -m_use));
+                pr[jj] = exp2_fast(__builtin_fmaf(sc[jj], scale_log2, -m[nt]));
                 l[nt] += pr[jj];
             }
             pf[nt] = pack_frag(pr);
         }
-        // O^T += V^T P^T; V fragments are read once and reused by both tiles
+        // O^T += V^T P^T; each V fragment serves both tiles
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) {
-            const bf16x8 vf = lds_frag_pair(stg + 32 * D + 256 * mt + 4 * lane, stg + 48 * D + 256 * mt + 4 * lane);
+        for (int mt = 0; mt < D / 16; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < kTiles; ++nt) acc[nt][mt] = mfma16x16x32(vf, pf[nt], acc[nt][mt]);
-        }
+            for (int nt = 0; nt < kTiles; ++nt) acc[nt][mt] = mfma16x16x32(vf[mt], pf[nt], acc[nt][mt]);
     };
     // The block holding the sequence's last key may carry stale (even non-finite) bytes in the
     // slots after it; they get p = 0, and 0 * NaN must not reach the accumulator, so those V
@@ -294,8 +312,7 @@ __device__ __forceinline__ void chunk_item(
 
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
-        float lt = l[nt];
-        lt = rows_sum(lt);
+        const float lt = rows_sum(l[nt]);
         const int wc = 32 * w + 16 * nt + c;  // column within the workgroup
         const int col = cb + wc;
         if (col >= ncols) continue;
