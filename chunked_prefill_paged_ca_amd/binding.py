@@ -67,6 +67,7 @@ class CaProfileRecord(ctypes.Structure):
 
 
 PROFILE_ALL, PROFILE_UPLOAD, PROFILE_APPEND, PROFILE_ATTENTION, PROFILE_MERGE = 1, 2, 4, 8, 16
+PROFILE_PROJECTION = 32
 
 
 class CaError(RuntimeError):
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.ca_mixed_attention.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
                                          vp, vp, vp, ctypes.c_int64, vp, vp, vp]
+        L.ca_append_kv_rope_packed.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
+                                               vp, vp, vp, vp, ctypes.c_int64, vp]
+        L.ca_qkv_projection.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.c_int32, ctypes.c_int32,
+                                        vp, vp, vp, vp]
         L.ca_profile_enable.argtypes = [vp, ctypes.c_int]
         L.ca_profile_read.argtypes = [vp, ctypes.POINTER(CaProfileRecord), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -108,7 +113,8 @@ def lib() -> ctypes.CDLL:
         L.ca_sched_free_pages.argtypes = [vp]
         L.ca_sched_free_pages.restype = ctypes.c_int64
         for fn in ("ca_create", "ca_destroy", "ca_plan_batch", "ca_append_kv_rope",
-                   "ca_mixed_attention", "ca_profile_enable", "ca_profile_read", "ca_sched_create",
+                   "ca_mixed_attention", "ca_append_kv_rope_packed", "ca_qkv_projection",
+                   "ca_profile_enable", "ca_profile_read", "ca_sched_create",
                    "ca_sched_destroy", "ca_sched_add", "ca_sched_step", "ca_sched_commit",
                    "ca_sched_get"):
             getattr(L, fn).restype = ctypes.c_int
@@ -386,6 +392,28 @@ class Context:
                                      _ptr(q_out), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                      _ptr(v_cache), int(num_pool_pages), _stream(stream))
         _check(st, "ca_append_kv_rope")
+
+    def append_kv_rope_packed(self, desc: CaAttnDesc, plan: Plan, qkv, q_out, k_cache, v_cache,
+                              num_pool_pages: int, stream=None):
+        eb = 2 if desc.dtype == CA_BF16 else 4
+        T, hq, hkv, d, P = plan.num_tokens, desc.num_q_heads, desc.num_kv_heads, desc.head_dim, desc.page_size
+        for name, t, n in (("qkv", qkv, T * (hq + 2 * hkv) * d), ("q_out", q_out, T * hq * d),
+                           ("k_cache", k_cache, num_pool_pages * hkv * P * d),
+                           ("v_cache", v_cache, num_pool_pages * hkv * P * d)):
+            _check_tensor(name, t, n, eb)
+        st = lib().ca_append_kv_rope_packed(self.h, ctypes.byref(desc), ctypes.byref(plan.c), _ptr(qkv),
+                                            _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+                                            int(num_pool_pages), _stream(stream))
+        _check(st, "ca_append_kv_rope_packed")
+
+    def qkv_projection(self, desc: CaAttnDesc, num_tokens: int, hidden: int, x, w, qkv, stream=None):
+        """qkv[T][Hq + 2 Hkv][d] = x[T][hidden] . w^T (w: [(Hq + 2 Hkv) d][hidden]), bf16."""
+        N = (desc.num_q_heads + 2 * desc.num_kv_heads) * desc.head_dim
+        for name, t, n in (("x", x, num_tokens * hidden), ("w", w, N * hidden), ("qkv", qkv, num_tokens * N)):
+            _check_tensor(name, t, n, 2)
+        st = lib().ca_qkv_projection(self.h, ctypes.byref(desc), int(num_tokens), int(hidden), _ptr(x),
+                                     _ptr(w), _ptr(qkv), _stream(stream))
+        _check(st, "ca_qkv_projection")
 
     def mixed_attention(self, desc: CaAttnDesc, plan: Plan, q, k_cache, v_cache,
                         num_pool_pages: int, o, lse=None, stream=None):

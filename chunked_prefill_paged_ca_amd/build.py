@@ -12,8 +12,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libca.so")
-SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "append_rope.hip", "attn_generic.hip", "attn_mixed.hip",
-           "merge.hip"]
+SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "linear.cpp", "append_rope.hip", "attn_generic.hip",
+           "attn_mixed.hip", "merge.hip"]
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]  # the QKV projection's GEMM
 
 
 def hipcc() -> str:
@@ -51,7 +52,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + LIBS
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

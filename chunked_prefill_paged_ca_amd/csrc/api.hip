@@ -263,6 +263,7 @@ struct ca_ctx {
     int32_t dec_wgs_override = 0;  // CA_DECODE_WGS: decode workgroups of a mixed launch, 0 = auto
     bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
+    ca::Linear* linear = nullptr;  // hipBLASLt state of ca_qkv_projection (created on first use)
 };
 
 namespace {
@@ -753,15 +754,21 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->chk_acc_buf.release();
     ctx->chk_ml_buf.release();
     ctx->prof.release();
+    ca::linear_release(ctx->linear);
     delete ctx;
     return CA_OK;
 }
 
-ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
-                            const void* q_in, void* q_out, const void* k_new, const void* v_new,
-                            void* k_cache, void* v_cache, int64_t num_pool_pages,
-                            void* hip_stream) {
-    ca::clear_error();
+}  // extern "C"
+
+namespace {
+
+// ca_append_kv_rope and ca_append_kv_rope_packed: q rows q_row elements apart, k and v rows
+// kv_row apart.
+ca_status append_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan, const void* q_in,
+                      void* q_out, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, int64_t num_pool_pages, void* hip_stream, int64_t q_row,
+                      int64_t kv_row) {
     if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
     ca_status st = check_plan(plan);
     if (st != CA_OK) return st;
@@ -787,10 +794,69 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
     {
         Timed t(ctx->prof, "append_rope", CA_PROFILE_APPEND);
         e = ca::launch_append_rope(ctx->dplan, sh, ctx->inv_freq, q_in, q_out, k_new, v_new, k_cache,
-                                   v_cache, stream, t.ev);
+                                   v_cache, q_row < 0 ? int64_t(sh.hq) * sh.d : q_row,
+                                   kv_row < 0 ? int64_t(sh.hkv) * sh.d : kv_row, stream, t.ev);
         if (e == hipSuccess) t.commit();
     }
     if (e != hipSuccess) return device_error("append_rope launch", e);
+    return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                            const void* q_in, void* q_out, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, int64_t num_pool_pages,
+                            void* hip_stream) {
+    ca::clear_error();
+    return append_impl(ctx, desc, plan, q_in, q_out, k_new, v_new, k_cache, v_cache, num_pool_pages,
+                       hip_stream, -1, -1);
+}
+
+ca_status ca_append_kv_rope_packed(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                                   const void* qkv, void* q_out, void* k_cache, void* v_cache,
+                                   int64_t num_pool_pages, void* hip_stream) {
+    ca::clear_error();
+    if (!desc || !qkv) { ca::set_error("ca_append_kv_rope_packed: null argument"); return CA_ERR_INVALID_ARG; }
+    const int64_t d = desc->head_dim, hq = desc->num_q_heads, hkv = desc->num_kv_heads;
+    const int64_t eb = desc->dtype == CA_BF16 ? 2 : 4;
+    const int64_t row = (hq + 2 * hkv) * d;
+    const char* base = static_cast<const char*>(qkv);
+    return append_impl(ctx, desc, plan, base, q_out, base + hq * d * eb, base + (hq + hkv) * d * eb,
+                       k_cache, v_cache, num_pool_pages, hip_stream, row, row);
+}
+
+ca_status ca_qkv_projection(ca_ctx* ctx, const ca_attn_desc* desc, int32_t num_tokens,
+                            int32_t hidden, const void* x, const void* w, void* qkv,
+                            void* hip_stream) {
+    ca::clear_error();
+    if (!ctx || !desc) { ca::set_error("ca_qkv_projection: null argument"); return CA_ERR_INVALID_ARG; }
+    if (desc->dtype != CA_BF16) { ca::set_error("ca_qkv_projection: bf16 only"); return CA_ERR_UNSUPPORTED; }
+    if (num_tokens < 0 || hidden <= 0 || desc->num_q_heads <= 0 || desc->num_kv_heads <= 0 ||
+        desc->head_dim <= 0 || hidden % 8 != 0) {
+        ca::set_error("ca_qkv_projection: need num_tokens >= 0, hidden > 0 and a multiple of 8, heads > 0");
+        return CA_ERR_INVALID_ARG;
+    }
+    if (num_tokens == 0) return CA_OK;
+    if (!x || !w || !qkv) { ca::set_error("ca_qkv_projection: null buffer"); return CA_ERR_INVALID_ARG; }
+    if (!aligned16({x, w, qkv})) {
+        ca::set_error("ca_qkv_projection: device buffers must be 16-byte aligned");
+        return CA_ERR_INVALID_ARG;
+    }
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const int64_t N = static_cast<int64_t>(desc->num_q_heads + 2 * desc->num_kv_heads) * desc->head_dim;
+    std::string err;
+    Timed t(ctx->prof, "qkv_projection", CA_PROFILE_PROJECTION);
+    if (t.ev.start) (void)hipEventRecord(t.ev.start, stream);
+    if (!ca::linear_bf16(ctx->linear, num_tokens, hidden, N, x, w, qkv, stream, &err)) {
+        ca::set_error("ca_qkv_projection: " + err);
+        return CA_ERR_DEVICE;
+    }
+    if (t.ev.stop && hipEventRecord(t.ev.stop, stream) == hipSuccess) t.commit();
     return CA_OK;
 }
 
@@ -884,8 +950,8 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
 ca_status ca_profile_enable(ca_ctx* ctx, int enable) {
     ca::clear_error();
     if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
-    if (enable < 0 || enable > 31) { ca::set_error("ca_profile_enable: unknown flags"); return CA_ERR_INVALID_ARG; }
-    ctx->prof.mask = (enable & CA_PROFILE_ALL) ? 0x1e : enable;
+    if (enable < 0 || enable > 63) { ca::set_error("ca_profile_enable: unknown flags"); return CA_ERR_INVALID_ARG; }
+    ctx->prof.mask = (enable & CA_PROFILE_ALL) ? 0x3e : enable;
     return CA_OK;
 }
 

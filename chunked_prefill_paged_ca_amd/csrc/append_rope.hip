@@ -11,7 +11,8 @@
 //     theta^(-2i/d) are a host-computed fp64 table;
 //   * every q/k/v load is a 16-byte vector load, all issued before the first store (a thread
 //     writes back exactly the elements it read, so q_out may alias q_in), and unconditional so
-//     that they are in flight together;
+//     that they are in flight together; q, k and v rows are read with their own row strides, so
+//     they may be the column ranges of one packed projection output;
 //   * the d/2 pair angles are formed in fp64 once per token, shared through LDS, and each
 //     rotated element is computed in fp64 and rounded once to the storage type.
 
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
     const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_page,
     const double* __restrict__ inv_freq, const T* q_in, T* q_out, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ k_cache, T* __restrict__ v_cache, int hq,
-    int hkv, int d, int P) {
+    int hkv, int d, int P, int64_t q_row, int64_t kv_row) {
 #pragma clang fp contract(off)
     constexpr int N = Vec<T>::N;
     __shared__ double s_cos[64];
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
     // they are all in flight together instead of each waiting at the end of its own branch.
     // The frequency load is issued first: waiting for it does not wait for the q/k/v loads.
     const double freq = inv_freq[tid < half ? tid : half - 1];
-    Vec<T> vv = load16(v_new + static_cast<int64_t>(t) * hkv * d + (tid < v_units ? tid : v_units - 1) * N);
+    Vec<T> vv = load16(v_new + t * kv_row + (tid < v_units ? tid : v_units - 1) * N);
 
     Vec<T> a[kUnits], b[kUnits];
     int i0[kUnits];
@@ -96,8 +97,8 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
             const int u = u0 < units ? u0 : units - 1;
             const int h = u / per_head;
             i0[j] = (u - h * per_head) * N;
-            const T* src = h < hq ? q_in + (static_cast<int64_t>(t) * hq + h) * d
-                                  : k_new + (static_cast<int64_t>(t) * hkv + (h - hq)) * d;
+            const T* src = h < hq ? q_in + t * q_row + static_cast<int64_t>(h) * d
+                                  : k_new + t * kv_row + static_cast<int64_t>(h - hq) * d;
             a[j] = load16(src + i0[j]);
             b[j] = load16(src + i0[j] + half);
         }
@@ -151,7 +152,7 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
     // V goes unrotated into its page: dim e of the slot lands in the run of 16-dim block e / 16
     // and 4-slot group slot / 4, at (e % 16) * 4 + slot % 4 (a vector unit stays in one block)
     for (int vu = tid; vu < v_units; vu += kThreads) {
-        if (vu != tid) vv = load16(v_new + static_cast<int64_t>(t) * hkv * d + vu * N);
+        if (vu != tid) vv = load16(v_new + t * kv_row + vu * N);
         const int g = (vu * N) / d;
         const int e0 = vu * N - g * d;
         T* vp = v_cache + (static_cast<int64_t>(page) * hkv + g) * P * d +
@@ -165,8 +166,8 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
 
 hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
                               const void* q_in, void* q_out, const void* k_new, const void* v_new,
-                              void* k_cache, void* v_cache, hipStream_t stream,
-                              const LaunchEvents& ev) {
+                              void* k_cache, void* v_cache, int64_t q_row, int64_t kv_row,
+                              hipStream_t stream, const LaunchEvents& ev) {
     if (p.num_tokens <= 0) return hipSuccess;
     const dim3 grid(p.num_tokens), block(kThreads);
     if (sh.dtype == CA_FP32) {
@@ -174,13 +175,14 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* i
                            inv_freq, static_cast<const float*>(q_in), static_cast<float*>(q_out),
                            static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                            static_cast<float*>(k_cache), static_cast<float*>(v_cache), sh.hq,
-                           sh.hkv, sh.d, p.page_size);
+                           sh.hkv, sh.d, p.page_size, q_row, kv_row);
     } else {
         hipExtLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, ev.start, ev.stop, 0, p.row_pos,
                            p.row_page, inv_freq, static_cast<const uint16_t*>(q_in),
                            static_cast<uint16_t*>(q_out), static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
-                           static_cast<uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, p.page_size);
+                           static_cast<uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, p.page_size, q_row,
+                           kv_row);
     }
     return hipGetLastError();
 }

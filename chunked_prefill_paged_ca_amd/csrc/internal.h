@@ -71,10 +71,18 @@ struct LaunchEvents {
 
 // ---- launchers (each enqueues on `stream`; returns hipSuccess or the launch error) ----
 // inv_freq: [d / 2] fp64 table theta^(-2i/d) in device memory.
+// The QKV projection (linear.cpp): out[T][N] = x[T][K] . w[N][K]^T, bf16 with fp32
+// accumulation, through hipBLASLt.  *L is created on first use and cached per shape.
+struct Linear;
+void linear_release(Linear* L);
+bool linear_bf16(Linear*& L, int64_t T, int64_t K, int64_t N, const void* x, const void* w,
+                 void* out, hipStream_t stream, std::string* err);
+
+// q_row, kv_row: elements between consecutive token rows of q_in and of k_new / v_new.
 hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
                               const void* q_in, void* q_out, const void* k_new, const void* v_new,
-                              void* k_cache, void* v_cache, hipStream_t stream,
-                              const LaunchEvents& ev);
+                              void* k_cache, void* v_cache, int64_t q_row, int64_t kv_row,
+                              hipStream_t stream, const LaunchEvents& ev);
 
 // Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
 // partial: fp32 workspace of num_tokens * hq * nsplit * (d + 2) floats.

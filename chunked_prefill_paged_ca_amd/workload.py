@@ -365,3 +365,12 @@ def make_serve_scenario(seed: int = 3, *, n: int = 14, rounds: int = 60, pool_pa
                          arrival=arrival.astype(np.int32), prompt_len=prompt.astype(np.int32),
                          num_cached=cached.astype(np.int32), max_new=max_new.astype(np.int32),
                          rounds=rounds)
+
+
+def projection_inputs(T: int, hidden: int, n_out: int, seed: int, dtype: str = "bf16"):
+    """Seeded hidden states x [T][hidden] ~ N(0, 1) and projection weights w [n_out][hidden] ~
+    N(0, 1/hidden) (so each output is O(1)), both rounded to the storage type."""
+    rng = np.random.default_rng([seed, 5])
+    x = rng.standard_normal((T, hidden), dtype=np.float32)
+    w = rng.standard_normal((n_out, hidden), dtype=np.float32) * np.float32(1.0 / math.sqrt(hidden))
+    return round_to_storage(x, dtype), round_to_storage(w, dtype)

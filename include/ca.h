@@ -12,6 +12,7 @@
  *   [CP] blog.vllbc.top/visual-reading/chunked-prefill-pd-disaggregation/  "Chunked Prefill 与 PD 分离"
  *   [SF] magicnetworld.com/tech/articles/2026-10-02-chunked-prefill-stall-free-scheduling/
  *        "分块预填充与 Stall-free 调度"
+ *   [SA] bowenzhou.top/papers/2023/Sarathi  "Sarathi：让解码搭上 prefill 的顺风车"
  *
  * Conventions shared by every entry point:
  *   - The caller owns every buffer.  Host arrays are plain pointers; device buffers are device
@@ -198,11 +199,39 @@ enum {
     CA_PROFILE_UPLOAD = 2,
     CA_PROFILE_APPEND = 4,
     CA_PROFILE_ATTENTION = 8,
-    CA_PROFILE_MERGE = 16
+    CA_PROFILE_MERGE = 16,
+    CA_PROFILE_PROJECTION = 32 /* "qkv_projection" */
 };
 
 ca_status ca_profile_enable(ca_ctx* ctx, int enable);
 ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int32_t* count);
+
+/*
+ * ca_qkv_projection -- the step's q, k and v from its hidden states, as one matrix product over
+ * the whole mixed token array ([SA] "Decode-maximal batching：顺车的账本": the linear layers of the
+ * decode tokens and of the prefill chunk run as one GEMM, so each weight is read once for all of
+ * them; attention stays separate).
+ *   qkv[T][Hq + 2 Hkv][d] = x[T][hidden] . w^T, where w is [(Hq + 2 Hkv) d][hidden] (one row per
+ *   output feature, rows ordered q heads, then k heads, then v heads) and T = num_tokens (the
+ *   plan's row order: decode rows, then chunk rows).  bf16 operands and result, fp32
+ *   accumulation; a library GEMM (hipBLASLt), planned once per token count and cached in ctx.
+ * Device buffers x, w, qkv (16-byte aligned).  Errors: CA_ERR_INVALID_ARG (null pointer, sizes,
+ * hidden not a multiple of 8), CA_ERR_UNSUPPORTED (dtype not bf16), CA_ERR_DEVICE (a hipBLASLt or
+ * HIP error).
+ */
+ca_status ca_qkv_projection(ca_ctx* ctx, const ca_attn_desc* desc, int32_t num_tokens,
+                            int32_t hidden, const void* x, const void* w, void* qkv,
+                            void* hip_stream);
+
+/*
+ * ca_append_kv_rope_packed -- ca_append_kv_rope reading q, k_new and v_new in place from the
+ * packed projection output qkv[T][Hq + 2 Hkv][d] (q heads, k heads, v heads of each row), with
+ * no copy in between.  q_out [T][Hq][d] receives the rotated q and must not overlap qkv; the
+ * caches, plan and errors are those of ca_append_kv_rope.
+ */
+ca_status ca_append_kv_rope_packed(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                                   const void* qkv, void* q_out, void* k_cache, void* v_cache,
+                                   int64_t num_pool_pages, void* hip_stream);
 
 /*
  * ---- Multi-step driver: ca_sched (host only, no device work) ----

@@ -236,6 +236,20 @@ class Session:
 
 
 # ---------------------------------------------------------------------------------------------
+# QKV projection
+# ---------------------------------------------------------------------------------------------
+
+def linear(x: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
+    """out[T][N] = x[T][K] . w[N][K]^T in fp64, rounded once to the storage type.
+
+    bowenzhou.top "Sarathi：让解码搭上 prefill 的顺风车", section "Decode-maximal batching：顺车的账本":
+    the linear layers of a mixed batch are one matrix product over all its tokens (decode rows
+    and chunk rows alike); this is that product for the q, k, v projection.
+    """
+    return round_to(np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T, dtype)
+
+
+# ---------------------------------------------------------------------------------------------
 # Multi-step serving loop
 # ---------------------------------------------------------------------------------------------
 

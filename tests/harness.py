@@ -115,17 +115,26 @@ def ulp_distance(a: np.ndarray, b: np.ndarray, dt: str) -> np.ndarray:
     return np.abs(np.asarray(a, dtype=np.float64) - b) / np.exp2(e - mant)
 
 
-def gpu_step(ctx, wl, plan, q_raw, k_raw, v_raw, k_cache, v_cache, want_lse=True, stream=None):
-    """One step through the C ABI: append + RoPE, then mixed attention.  Returns device tensors."""
+def gpu_step(ctx, wl, plan, q_raw, k_raw, v_raw, k_cache, v_cache, want_lse=True, stream=None,
+             packed=False):
+    """One step through the C ABI: append + RoPE, then mixed attention.  Returns device tensors.
+    packed: hand q, k, v over as one packed [T][Hq + 2 Hkv][d] array (ca_append_kv_rope_packed)."""
     import torch
     from chunked_prefill_paged_ca_amd import make_desc
     desc = make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
-    q_in = to_device(q_raw, wl.dtype)
-    k_in = to_device(k_raw, wl.dtype)
-    v_in = to_device(v_raw, wl.dtype)
-    q_out = torch.empty_like(q_in)
-    ctx.append_kv_rope(desc, plan, q_in, q_out, k_in, v_in, k_cache, v_cache, wl.num_pool_pages,
-                       stream=stream)
+    if packed:
+        qkv = to_device(np.concatenate([q_raw, k_raw, v_raw], axis=1), wl.dtype)
+        q_out = torch.empty((qkv.shape[0], wl.num_q_heads, wl.head_dim), dtype=qkv.dtype, device=qkv.device)
+        ctx.append_kv_rope_packed(desc, plan, qkv, q_out, k_cache, v_cache, wl.num_pool_pages,
+                                  stream=stream)
+        q_in = q_out
+    else:
+        q_in = to_device(q_raw, wl.dtype)
+        k_in = to_device(k_raw, wl.dtype)
+        v_in = to_device(v_raw, wl.dtype)
+        q_out = torch.empty_like(q_in)
+        ctx.append_kv_rope(desc, plan, q_in, q_out, k_in, v_in, k_cache, v_cache, wl.num_pool_pages,
+                           stream=stream)
     o = torch.empty_like(q_out)
     lse = (torch.empty((plan.num_tokens, wl.num_q_heads), dtype=torch.float32, device=q_in.device)
            if want_lse else None)

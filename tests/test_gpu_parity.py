@@ -38,7 +38,7 @@ def _log(msg):
 
 
 def run_and_check(ctx, oracle, wl, steps=None, rows_per_seq=None, track=None, pool=None,
-                  check_cache=True, label=""):
+                  check_cache=True, label="", packed=False):
     """Run `steps` steps on GPU and oracle; compare everything compared in the module docstring.
 
     rows_per_seq -- if set, attend-check only this many rows per sequence (sampled, incl. last).
@@ -66,7 +66,7 @@ def run_and_check(ctx, oracle, wl, steps=None, rows_per_seq=None, track=None, po
         for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
             assert np.array_equal(a[k], ref_plan[k]), (label, step, k)
         q, k, v = cur.take(ref_plan["req_ids"], np.diff(ref_plan["qo_indptr"]))
-        q_out, o, lse = H.gpu_step(ctx, wl, plan, q, k, v, k_cache, v_cache)
+        q_out, o, lse = H.gpu_step(ctx, wl, plan, q, k, v, k_cache, v_cache, packed=packed)
         torch.cuda.synchronize()
         rows = None
         if rows_per_seq is not None:
@@ -128,13 +128,14 @@ def test_tiny_chunked_matches_oracle_and_one_shot(env, dt):
     assert np.abs(chunk_o - one_o).max() <= TOL_O[dt]
 
 
-@pytest.mark.parametrize("variant", ["base", "peaky"])
+@pytest.mark.parametrize("variant", ["base", "peaky", "packed"])
 def test_mistral_mixed_full(env, variant):
-    """Config 2 at full size: 80 decodes + P(300 on 1200) + Q(132 on 2048), every row checked."""
+    """Config 2 at full size: 80 decodes + P(300 on 1200) + Q(132 on 2048), every row checked
+    (packed: q, k, v handed over as one packed projection-shaped array)."""
     from chunked_prefill_paged_ca_amd.workload import make_config
     ctx, oracle = env
     wl = make_config(2, peaky=(variant == "peaky"))
-    res, _, _ = run_and_check(ctx, oracle, wl, label=f"mistral-{variant}")
+    res, _, _ = run_and_check(ctx, oracle, wl, label=f"mistral-{variant}", packed=(variant == "packed"))
     p = res[0][0]
     assert list(np.diff(p["qo_indptr"])[-2:]) == [300, 132] and p["num_tokens"] == 512
 
@@ -202,6 +203,73 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.array_equal(gk, gk1) and np.array_equal(gv, gv1)
     chunk_o = np.concatenate([go for p, go, gl, ref in res])
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
+
+
+@pytest.mark.parametrize("T", [1, 80, 512, 523])
+def test_qkv_projection_matches_oracle(env, T):
+    """The Mistral-7B q/k/v projection (hidden 4096 -> (32 + 2 x 8) x 128 features) over T
+    tokens against the exact product rounded once.  The GPU sums K = 4096 exact bf16 products in
+    fp32, whose error is at most K 2^-24 sum_k |x_k w_k| (the standard bound for a K-term
+    floating-point sum); the bar is that bound plus one bf16 unit in the last place of the exact
+    value.  Away from cancellation this means "equal or the neighbouring bf16 value"; an output
+    near zero may be further off in ulps of its own tiny magnitude."""
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import projection_inputs
+    from tests import harness as H
+    ctx, oracle = env
+    Hq, Hkv, d, hidden = 32, 8, 128, 4096
+    N = (Hq + 2 * Hkv) * d
+    x, w = projection_inputs(T, hidden, N, seed=11 + T)
+    desc = ca.make_desc(Hq, Hkv, d, 16, "bf16")
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    ctx.qkv_projection(desc, T, hidden, H.to_device(x, "bf16"), H.to_device(w, "bf16"), out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.linear(x, w, "bf16")
+    u = H.ulp_distance(got, ref, "bf16")
+    sum_bound = hidden * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T)
+    allowed = sum_bound + np.abs(ref) * 2.0 ** -7 + 2.0 ** -133
+    _log(f"[projection T={T}] max ulp {u.max():.0f}, outputs not equal {(u > 0).mean():.5f}, "
+         f"worst |err|/allowed {(np.abs(got - ref) / allowed).max():.3f}")
+    assert np.all(np.abs(got - ref) <= allowed)
+    assert (u > 1).mean() <= 1e-4
+
+
+def test_projected_step_matches_oracle(env):
+    """The Mistral-7B step fed from hidden states: projection, packed append, attention, against
+    the oracle's projection (rounded once) -> RoPE -> attention.  The projections may differ in
+    the last bf16 bit, so the bar here is on the attention output (2e-2) and lse (1e-2)."""
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import make_config, projection_inputs
+    from tests import harness as H
+    ctx, oracle = env
+    wl = make_config(2)
+    Hq, Hkv, d, hidden = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 4096
+    N = (Hq + 2 * Hkv) * d
+    kc, vc = H.alloc_pool(wl)
+    H.write_history(wl, kc, vc)
+    sess = oracle.Session(wl)
+    ref_plan = sess.plan()
+    plan = H.lib_plan(wl, wl.num_computed, wl.num_prompt_left)
+    T = plan.num_tokens
+    x, w = projection_inputs(T, hidden, N, seed=29)
+    desc = ca.make_desc(Hq, Hkv, d, wl.page_size, wl.dtype)
+    qkv = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    ctx.qkv_projection(desc, T, hidden, H.to_device(x, "bf16"), H.to_device(w, "bf16"), qkv)
+    q_rot = torch.empty((T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    ctx.append_kv_rope_packed(desc, plan, qkv, q_rot, kc, vc, wl.num_pool_pages)
+    o = torch.empty_like(q_rot)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, lse)
+    torch.cuda.synchronize()
+    ref_qkv = oracle.linear(x, w, "bf16").reshape(T, Hq + 2 * Hkv, d)
+    ref = sess.step(ref_plan, ref_qkv[:, :Hq], ref_qkv[:, Hq:Hq + Hkv], ref_qkv[:, Hq + Hkv:])
+    err = np.abs(o.float().cpu().numpy() - ref["o"]).max()
+    lerr = np.abs(lse.cpu().numpy() - ref["lse"]).max()
+    _log(f"[projected step] T={T} max|do|={err:.3e} max|dlse|={lerr:.3e}")
+    assert err <= TOL_O["bf16"] and lerr <= 1e-2
 
 
 def test_serving_loop_matches_oracle(env):

@@ -4,6 +4,8 @@ Pins used (none re-types the oracle's own formula):
   * the pages' worked example of a 512-token budget (tests/golden/worked_example_512.json), also
     with chunk sizes aligned to 32 as the pages' tile-quantisation section describes, and a
     downward brute-force search for aligned chunk sizes;
+  * the QKV projection: a triple-loop brute force, identity and row-selection weights, and a
+    tie that shows one rounding of the exact sum;
   * the serving loop: the worked example over two rounds (P becomes a decode, Q gets 431), the
     pages' rounds-to-first-token example (tests/golden/rounds_to_first_token.json), and pool /
     preemption invariants over random arrivals;
@@ -232,6 +234,42 @@ def test_sched_invariants_random(oracle_mod):
             if r["state"] == m.FINISHED:
                 assert r["generated"] == r["max_new"]
     assert preempted_total > 0  # the random pools are small enough to exercise preemption
+
+
+# ------------------------------------------------------------------------------------------
+# QKV projection
+# ------------------------------------------------------------------------------------------
+
+def test_linear_brute_force(oracle_mod):
+    rng = np.random.default_rng(3)
+    for T, K, N in ((1, 1, 1), (3, 5, 4), (7, 16, 9)):
+        x = oracle_mod.round_to(rng.standard_normal((T, K)), "bf16")
+        w = oracle_mod.round_to(rng.standard_normal((N, K)), "bf16")
+        ref = np.zeros((T, N))
+        for t in range(T):
+            for n in range(N):
+                acc = 0.0
+                for k in range(K):
+                    acc += x[t, k] * w[n, k]
+                ref[t, n] = acc
+        assert np.array_equal(oracle_mod.linear(x, w, "bf16"), oracle_mod.round_to(ref, "bf16"))
+        assert np.array_equal(oracle_mod.linear(x, w, "fp32"), oracle_mod.round_to(ref, "fp32"))
+
+
+def test_linear_identity_and_selection(oracle_mod):
+    rng = np.random.default_rng(4)
+    x = oracle_mod.round_to(rng.standard_normal((6, 8)), "bf16")
+    assert np.array_equal(oracle_mod.linear(x, np.eye(8), "bf16"), x)
+    perm = rng.permutation(8)
+    assert np.array_equal(oracle_mod.linear(x, np.eye(8)[perm], "bf16"), x[:, perm])
+
+
+def test_linear_single_rounding(oracle_mod):
+    # 1 + 2^-8 is a tie between the bf16 neighbours 1 and 1 + 2^-7: nearest-even gives 1, and
+    # 1 + 2^-8 + 2^-20 (a sum that a per-term rounding would lose) rounds up
+    x = np.array([[1.0, 2.0 ** -8, 2.0 ** -20]])
+    assert oracle_mod.linear(x[:, :2], np.ones((1, 2)), "bf16")[0, 0] == 1.0
+    assert oracle_mod.linear(x, np.ones((1, 3)), "bf16")[0, 0] == 1.0 + 2.0 ** -7
 
 
 def _check_plan_invariants(p, nc, left, tables, tau, max_chunk, P):
