@@ -8,10 +8,13 @@ over a 64K-page pool.  Inputs are resident in HBM before the timed region starts
 
 Prints ONE JSON line.  `value` is tokens per second of whole steps over the timed region.
 `roofline` places the dominant kernel -- the attention launch, which runs the decode rows and
-the prefill-chunk rows side by side and is bound by reading the K/V pages -- against the 8 TB/s
-HBM peak, using algorithmic bytes and the launch's own duration (HIP events attached to that
-launch on the bench's stream, every step of the timed region).  `traffic` is the HBM bytes the
-counters measured for that launch (profiles/), used only while the kernel sources are unchanged.
+the prefill-chunk rows side by side -- against the peak of the resource its algorithmic work
+needs longest: reading the K/V pages at 8 TB/s HBM (the default workload and every
+decode-heavy one), or the chunk rows' flops at 2.5 PFLOP/s bf16 MFMA (long prefill chunks),
+using the launch's own duration (HIP events attached to that launch on the bench's stream,
+every step of the timed region).  `traffic` is the HBM bytes the counters measured for that
+launch (profiles/), used only for the workload they were taken on and while the kernel sources
+are unchanged.
 `parts` times the decode and chunk work as two separate launches in a second, untimed pass, for
 their own HBM and bf16 MFMA fractions.  `cpu_baseline` times the CPU oracle on the same step.
 """
@@ -35,15 +38,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stored_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or None."""
+def stored_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or None: the reading
+    counts only for the workload it was taken on and while the kernel sources are unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     from chunked_prefill_paged_ca_amd.profiling import kernel_sources_sha256
-    if t.get("sources_sha256") != kernel_sources_sha256():
+    if t.get("workload") != workload or t.get("sources_sha256") != kernel_sources_sha256():
         return None
     return int(t["hbm_bytes_per_launch"])
 
@@ -149,9 +153,16 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
 
+    # The launch's bound is the resource its algorithmic work needs longest: K/V bytes at the HBM
+    # peak, or the chunk rows' flops at the bf16 MFMA peak (long prefill chunks).
     attn_bytes = dec_w.bytes + chk_w.bytes
-    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    traffic = stored_traffic()
+    t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = chk_w.flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        achieved, peak, unit, bound = chk_w.flops / (attn_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = attn_bytes / (attn_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    traffic = stored_traffic(wl.name)
     out = {
         "metric": "mixed chunked-prefill+decode attn tokens/s; % HBM peak and % MFMA peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -160,10 +171,11 @@ def main():
         "config": {"workload": wl.name, "tokens_per_step": T, "decodes": nd,
                    "token_budget": wl.token_budget, "page_size": wl.page_size,
                    "pool_pages": wl.num_pool_pages, "step": "plan + append_kv_rope + mixed_attention"},
-        "roofline": {"bound": "hbm", "kernel": "attention (decode + chunk rows, one launch)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "roofline": {"bound": bound, "kernel": "attention (decode + chunk rows, one launch)",
+                     "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
                      "alg_bytes_per_launch": int(attn_bytes),
+                     "alg_flops_per_launch": int(chk_w.flops),
                      "launch_ms": round(attn_ms, 5)},
     }
 

@@ -7,7 +7,9 @@
 // accumulation -- a plain library GEMM, done by hipBLASLt.  hipBLASLt is column-major: with the
 // row-major arrays read as their transposes this is D(N x T) = op_T(w as K x N) . x(K x T), the
 // "TN" form.  Layouts and the chosen algorithm are cached per token count (the serving loop sees
-// a few distinct T again and again).
+// a few distinct T again and again).  The first call for a token count times up to kCandidates
+// of the algorithms hipBLASLt proposes (on the caller's buffers, synchronising the stream) and
+// keeps the fastest; the output is then written by that algorithm.
 
 #include <hipblaslt/hipblaslt.h>
 
@@ -35,6 +37,7 @@ struct Linear {
 namespace {
 
 constexpr size_t kWorkspace = size_t(32) << 20;
+constexpr int kCandidates = 16;
 
 std::string blas_error(const char* what, hipblasStatus_t st) {
     return std::string(what) + ": hipBLASLt status " + std::to_string(static_cast<int>(st));
@@ -93,10 +96,10 @@ bool linear_bf16(Linear*& L, int64_t T, int64_t K, int64_t N, const void* x, con
         const uint64_t cap = L->ws_bytes;
         if (st == HIPBLAS_STATUS_SUCCESS)
             st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
-        hipblasLtMatmulHeuristicResult_t res[1];
+        hipblasLtMatmulHeuristicResult_t res[kCandidates];
         int got = 0;
         if (st == HIPBLAS_STATUS_SUCCESS)
-            st = hipblasLtMatmulAlgoGetHeuristic(L->handle, L->desc, s.a, s.b, s.d, s.d, pref, 1, res, &got);
+            st = hipblasLtMatmulAlgoGetHeuristic(L->handle, L->desc, s.a, s.b, s.d, s.d, pref, kCandidates, res, &got);
         if (pref) hipblasLtMatmulPreferenceDestroy(pref);
         if (st != HIPBLAS_STATUS_SUCCESS || got < 1) {
             *err = st != HIPBLAS_STATUS_SUCCESS ? blas_error("hipBLASLt plan", st)
@@ -108,6 +111,35 @@ bool linear_bf16(Linear*& L, int64_t T, int64_t K, int64_t N, const void* x, con
         }
         s.algo = res[0].algo;
         s.ws = res[0].workspaceSize;
+        if (got > 1) {
+            hipEvent_t e0 = nullptr, e1 = nullptr;
+            if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+                const float alpha = 1.0f, beta = 0.0f;
+                float best = 1e30f;
+                for (int i = 0; i < got; ++i) {
+                    if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > L->ws_bytes) continue;
+                    bool ok = true;
+                    for (int r = 0; r < 2 && ok; ++r)  // warm-up
+                        ok = hipblasLtMatmul(L->handle, L->desc, &alpha, w, s.a, x, s.b, &beta, out, s.d, out, s.d,
+                                             &res[i].algo, L->ws, res[i].workspaceSize, stream) == HIPBLAS_STATUS_SUCCESS;
+                    if (!ok) continue;
+                    (void)hipEventRecord(e0, stream);
+                    for (int r = 0; r < 5 && ok; ++r)
+                        ok = hipblasLtMatmul(L->handle, L->desc, &alpha, w, s.a, x, s.b, &beta, out, s.d, out, s.d,
+                                             &res[i].algo, L->ws, res[i].workspaceSize, stream) == HIPBLAS_STATUS_SUCCESS;
+                    (void)hipEventRecord(e1, stream);
+                    float ms = 0.0f;
+                    if (!ok || hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) continue;
+                    if (ms < best) {
+                        best = ms;
+                        s.algo = res[i].algo;
+                        s.ws = res[i].workspaceSize;
+                    }
+                }
+            }
+            if (e0) (void)hipEventDestroy(e0);
+            if (e1) (void)hipEventDestroy(e1);
+        }
         it = L->shapes.emplace(T, s).first;
     }
     const float alpha = 1.0f, beta = 0.0f;

@@ -3,9 +3,10 @@
     python -m chunked_prefill_paged_ca_amd.profiling stats <kernel_stats.csv> <title> <command>
         -> markdown table of per-kernel dispatch durations on stdout
     python -m chunked_prefill_paged_ca_amd.profiling traffic <fetch counter_collection.csv>
-           <write counter_collection.csv> <copy MiB> <command>
+           <write counter_collection.csv> <copy MiB> <command> <workload>
         -> JSON: FETCH_SIZE / WRITE_SIZE per attention launch, scaled by what the same counters
-           read for a device-to-device copy of known size, on stdout
+           read for a device-to-device copy of known size, on stdout; <workload> is the name of
+           the workload the counters were taken on (a reading holds for that workload only)
 
 Neither touches the GPU; they read the CSV files rocprofv3 wrote.
 """
@@ -61,9 +62,9 @@ def _per_dispatch(path: str, counter: str):
     return {d: (names[d], v) for d, v in acc.items()}
 
 
-def traffic(fetch_csv: str, write_csv: str, copy_mib: int, cmd: str) -> dict:
+def traffic(fetch_csv: str, write_csv: str, copy_mib: int, cmd: str, workload: str) -> dict:
     copy_bytes = copy_mib * (1 << 20)
-    res = {"command": cmd, "copy_reference_bytes": copy_bytes}
+    res = {"command": cmd, "workload": workload, "copy_reference_bytes": copy_bytes}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         per = _per_dispatch(path, counter)  # KiB per dispatch
         attn = [v for n, v in per.values() if "mixed_kernel" in n]
@@ -84,8 +85,8 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, cmd: str) -> dict:
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         sys.stdout.write(stats_md(argv[1], argv[2], argv[3]))
-    elif len(argv) >= 5 and argv[0] == "traffic":
-        print(json.dumps(traffic(argv[1], argv[2], int(argv[3]), argv[4]), indent=1))
+    elif len(argv) >= 6 and argv[0] == "traffic":
+        print(json.dumps(traffic(argv[1], argv[2], int(argv[3]), argv[4], argv[5]), indent=1))
     else:
         print(__doc__, file=sys.stderr)
         return 2
