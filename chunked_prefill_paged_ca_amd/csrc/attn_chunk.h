@@ -83,6 +83,10 @@ __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __res
     }
 }
 
+// One LDS stage holds two 32-key blocks (64 keys); each block keeps the four-run layout above.
+template <int D>
+constexpr int kStageHalves = 2 * 64 * D;
+
 // items: two int4 per item: {seq, kv head, first column (row * G + head), partial slot or -1},
 //                           {key begin, key end, 0, 0}   (seq -1: grid padding)
 template <int D>
@@ -92,11 +96,13 @@ __device__ __forceinline__ void chunk_item(
     const uint16_t* __restrict__ v_cache, int hq, int hkv, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) uint16_t stage0[64 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t stage1[64 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t stage2[64 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t stage3[64 * D];
-    __shared__ int s_pages[kMaxItemPages];  // the item's page ids, so a block's ids are an LDS read
+    __shared__ __attribute__((aligned(16))) uint16_t stage0[kStageHalves<D>];
+    __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageHalves<D>];
+    __shared__ __attribute__((aligned(16))) uint16_t stage2[kStageHalves<D>];
+    __shared__ __attribute__((aligned(16))) uint16_t stage3[kStageHalves<D>];
+    // the item's page ids, so a block's ids are an LDS read (two spare entries: a block's pair
+    // is read as one 8-byte load, also past the last page, and the spare half then ignored)
+    __shared__ __attribute__((aligned(16))) int s_pages[kMaxItemPages + 2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,10 +125,13 @@ __device__ __forceinline__ void chunk_item(
     const int lp0 = kb >> 4;
     const int nlp = min(((ke + 31) >> 4) - lp0, np - lp0);  // <= kMaxItemPages (host-checked)
     for (int i = tid; i < nlp; i += 64 * kWaves) s_pages[i] = pages[lp0 + i];
+    // key0 is a multiple of 32 (item ranges start on 32-key blocks), so lp is even and the
+    // pair is one aligned 8-byte read
     auto page_pair = [&](int key0, int* pa, int* pb) {
         const int lp = (key0 >> 4) - lp0;
-        *pa = s_pages[lp];
-        *pb = (lp0 + lp + 1 < np) ? s_pages[lp + 1] : *pa;  // a missing page is masked, never used
+        const int2 ids = *reinterpret_cast<const int2*>(s_pages + lp);
+        *pa = ids.x;
+        *pb = (lp0 + lp + 1 < np) ? ids.y : ids.x;  // a missing page is masked, never used
     };
 
     // this wave's columns: tile nt, lane column c -> column cb + 32 w + 16 nt + c
@@ -143,6 +152,9 @@ __device__ __forceinline__ void chunk_item(
     }
 #pragma unroll
     for (int o_ = 32; o_ >= 1; o_ >>= 1) wmin = min(wmin, __shfl_xor(wmin, o_, 64));
+    // A wave whose 32 columns all lie past the chunk (the last column block of a chunk) only
+    // helps with the copies and barriers; it skips the LDS reads, MFMAs and softmax.
+    const bool active = wmin != 0x7fffffff;
 
     // Per column: running max m (log2 units), weight sum l (this lane's keys; summed over the
     // lane groups at the end) and the O^T accumulator.  m starts at a finite floor far below any
@@ -159,21 +171,20 @@ __device__ __forceinline__ void chunk_item(
         for (int mt = 0; mt < D / 16; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // One 32-key block held in LDS stage `stg`.  Blocks wholly inside every column's visible
-    // range (the common case) skip the causal mask; the mask test is wave-uniform.
-    auto consume = [&](const uint16_t* stg, int key0) {
-        // All of the block's K fragments are requested before the first MFMA, and all of its V
-        // fragments right after the last QK MFMA, so the LDS latency is paid once per operand
-        // (under the MFMAs, then under the softmax) instead of once per pair of reads.
-        bf16x8 kf[2][D / 32];
+    // The block loop is software-pipelined by one operand: block i's K fragments are read from
+    // LDS while block i-1's PV MFMAs run, so the QK MFMAs of block i start as soon as the block
+    // begins.  Per block: QK (K fragments already in registers) -> V fragment reads -> softmax
+    // -> barrier (publishes block i+1, frees block i's stage) -> refill DMA -> block i+1's K
+    // reads -> PV of block i.
+    auto read_k = [&](bf16x8 (&kf)[2][D / 32], const uint16_t* stg) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk)
                 // tile t = page t: row c = slot c, dims 32 kk + 8 q .. = 8-dim block 4 kk + q
                 kf[t][kk] = lds_frag(stg + 16 * D * t + 512 * kk + 8 * lane);
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs that use them
-        floatx4 st[kTiles][2];
+    };
+    auto qk = [&](const bf16x8 (&kf)[2][D / 32], floatx4 (&st)[kTiles][2]) {
 #pragma unroll
         for (int nt = 0; nt < kTiles; ++nt) st[nt][0] = st[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -182,17 +193,21 @@ __device__ __forceinline__ void chunk_item(
             for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
                 for (int nt = 0; nt < kTiles; ++nt) st[nt][t] = mfma16x16x32(kf[t][kk], qf[nt][kk], st[nt][t]);
-        // a fragment's two halves (pages a and b) sit 16 D halves apart: read as one pair, kept
-        // apart from the other fragments' reads so the pair is what gets merged into one
-        // two-address LDS read, straight into the fragment's registers
-        bf16x8 vf[D / 16];
+    };
+    // a V fragment's two halves (pages a and b) sit 16 D halves apart: read as one pair, kept
+    // apart from the other fragments' reads so the pair is what gets merged into one
+    // two-address LDS read, straight into the fragment's registers
+    auto read_v = [&](bf16x8 (&vf)[D / 16], const uint16_t* stg) {
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
             vf[mt] = lds_frag_pair(stg + 32 * D + 256 * mt + 4 * lane, stg + 48 * D + 256 * mt + 4 * lane);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    // Online softmax of one block's scores into P^T fragments.  Blocks wholly inside every
+    // column's visible range (the common case) skip the causal mask; the test is wave-uniform.
+    auto softmax = [&](floatx4 (&st)[kTiles][2], int key0, bf16x8 (&pf)[kTiles]) {
         const bool full = key0 + 31 <= wmin;
-        bf16x8 pf[kTiles];
 #pragma unroll
         for (int nt = 0; nt < kTiles; ++nt) {
             float sc[8];
@@ -236,7 +251,9 @@ __device__ __forceinline__ void chunk_item(
             }
             pf[nt] = pack_frag(pr);
         }
-        // O^T += V^T P^T; each V fragment serves both tiles
+    };
+    // O^T += V^T P^T; each V fragment serves both tiles
+    auto pv = [&](const bf16x8 (&vf)[D / 16], const bf16x8 (&pf)[kTiles]) {
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt)
 #pragma unroll
@@ -256,59 +273,115 @@ __device__ __forceinline__ void chunk_item(
         __syncthreads();
     };
 
-    // Four LDS stages, loop unrolled by four so each step names its stages at compile time:
-    // blocks i+1 .. i+3 are in flight (DMA) while block i is consumed, which covers an L2/MALL
-    // or HBM round trip with three blocks of MFMA work.  Each step waits only for its own block
-    // (the DMA count of the blocks issued after it may stay outstanding), and one barrier both
-    // publishes that block and frees the stage the step is about to refill.
-    constexpr int U = 8 * D / (64 * kWaves);  // DMA instructions per wave per block
+    // Four LDS stages of two 32-key blocks each, loop unrolled by four so each step names its
+    // stages at compile time: up to three stages (192 keys) are in flight (DMA) while one is
+    // consumed, which covers an L2/MALL or HBM round trip with several blocks of MFMA work.
+    // One wait and one barrier per stage (not per block): the wait covers only the stage about
+    // to be read (the DMA count of the stages issued after it may stay outstanding), and the
+    // barrier both publishes that stage and frees the one about to be refilled.
+    constexpr int U = 8 * D / (64 * kWaves);  // DMA instructions per wave per 32-key block
     const int nblk = (ke - kb + 31) >> 5;
+    const int nst = (nblk + 1) >> 1;
     __syncthreads();  // page ids in LDS
-    int pa, pb;
-    page_pair(kb, &pa, &pb);
-    dma_block<D>(stage0, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-    if (nblk > 1) {
-        page_pair(kb + 32, &pa, &pb);
-        dma_block<D>(stage1, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-    }
-    if (nblk > 2) {
-        page_pair(kb + 64, &pa, &pb);
-        dma_block<D>(stage2, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-    }
-    // Wait until at most `later` blocks' DMAs of this wave are still outstanding, then an
-    // execution barrier.  __syncthreads() would also be a release fence, which makes the
-    // compiler drain every outstanding DMA first; here visibility is already explicit: the
-    // step's own DMA is waited for above, and every LDS read of the stage about to be refilled
-    // has returned (its MFMA consumed it) before a wave can reach the barrier.  The signal
-    // fence keeps the compiler from moving LDS accesses across it.
-    auto wait_block = [&](int later) {
-        if (later >= 2) __builtin_amdgcn_s_waitcnt((2 * U) | (0x7 << 4) | (0xf << 8));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(U | (0x7 << 4) | (0xf << 8));
-        else __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+    int pa, pb, pc, pd;
+    // copy stage si (its one or two blocks) into `slot`
+    auto dma_stage = [&](uint16_t* slot, int si) {
+        page_pair(kb + 64 * si, &pa, &pb);
+        dma_block<D>(slot, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+        if (2 * si + 1 < nblk) {
+            page_pair(kb + 64 * si + 32, &pc, &pd);
+            dma_block<D>(slot + 64 * D, k_cache, v_cache, pc, pd, g, hkv, w, lane);
+        }
+    };
+    dma_stage(stage0, 0);
+    if (nst > 1) dma_stage(stage1, 1);
+    if (nst > 2) dma_stage(stage2, 2);
+    // Wait until at most `later` blocks' DMAs of this wave are still outstanding and every LDS
+    // read of this wave has returned, then an execution barrier.  __syncthreads() would also be
+    // a release fence, which makes the compiler drain every outstanding DMA first; here
+    // visibility is explicit: the waited-for stage's DMA is complete in every wave, and every
+    // wave's reads of the stage about to be refilled have returned, when the barrier opens.  The
+    // signal fence keeps the compiler from moving LDS accesses across it.
+    auto wait_stage = [&](int later) {
+        switch (later) {
+            case 0: __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(U | (0x7 << 4)); break;
+            case 2: __builtin_amdgcn_s_waitcnt((2 * U) | (0x7 << 4)); break;
+            case 3: __builtin_amdgcn_s_waitcnt((3 * U) | (0x7 << 4)); break;
+            default: __builtin_amdgcn_s_waitcnt((4 * U) | (0x7 << 4)); break;
+        }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    auto step = [&](uint16_t* cur, uint16_t* refill, int bi) {
-        const int key0 = kb + 32 * bi;
-        const int issued_after = min(2, nblk - 1 - bi);  // blocks bi+1, bi+2 already requested
-        wait_block(issued_after);
-        zero_v_tail(cur, key0);
-        if (bi + 3 < nblk) {
-            page_pair(key0 + 96, &pa, &pb);
-            dma_block<D>(refill, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-        }
-        consume(cur, key0);
+    // At step si's wait, stages 0 .. si+3 have been requested (blocks below min(nblk, 2si+8))
+    // and stage si+1 (blocks 2si+2, 2si+3) must be complete: the blocks requested after it may
+    // stay outstanding.
+    auto later_blocks = [&](int si) { return max(0, min(nblk, 2 * si + 8) - (2 * si + 4)); };
+    auto zero_stage_tail = [&](uint16_t* slot, int si) {
+        zero_v_tail(slot, kb + 64 * si);
+        zero_v_tail(slot + 64 * D, kb + 64 * si + 32);
     };
-    for (int bi = 0; bi < nblk; bi += 4) {
-        step(stage0, stage3, bi);
-        if (bi + 1 >= nblk) break;
-        step(stage1, stage0, bi + 1);
-        if (bi + 2 >= nblk) break;
-        step(stage2, stage1, bi + 2);
-        if (bi + 3 >= nblk) break;
-        step(stage3, stage2, bi + 3);
-    }
+    wait_stage(max(0, min(nblk, 6) - 2));  // stage 0 landed
+    zero_stage_tail(stage0, 0);
+    if (nst > 3) dma_stage(stage3, 3);
+
+    // Stage si sits in `cur`, with its first block's K fragments already in kf; `nxt` holds
+    // stage si+1; `cur` is refilled with stage si+4 once every wave is past its reads.  Per
+    // block: QK -> V reads -> softmax -> (the next block's K reads) -> PV, so each block's K
+    // reads go out under the previous block's PV MFMAs.  A wave whose columns all lie past the
+    // chunk (ACT false: the last column block of a chunk) only helps with the copies and
+    // barriers.
+    bf16x8 kf[2][D / 32];
+    auto step = [&](uint16_t* cur, uint16_t* nxt, int si, auto act) {
+        constexpr bool ACT = decltype(act)::value;
+        const int key0 = kb + 64 * si;
+        const bool two = 2 * si + 1 < nblk;
+        floatx4 st[kTiles][2];
+        bf16x8 vf[D / 16];
+        bf16x8 pf[kTiles];
+        if constexpr (ACT) {
+            qk(kf, st);
+            read_v(vf, cur);
+            softmax(st, key0, pf);
+            if (two) {
+                read_k(kf, cur + 64 * D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            pv(vf, pf);
+            if (two) {
+                qk(kf, st);
+                read_v(vf, cur + 64 * D);
+                softmax(st, key0 + 32, pf);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the softmax completes before the barrier
+        if (si + 1 < nst) {
+            wait_stage(later_blocks(si));  // stage si+1 landed; stages si+2, si+3 may still fly
+            zero_stage_tail(nxt, si + 1);
+            if (si + 4 < nst) dma_stage(cur, si + 4);
+            if constexpr (ACT) read_k(kf, nxt);
+            __builtin_amdgcn_sched_barrier(0);  // the next block's K reads go out ahead of PV
+        }
+        if constexpr (ACT) {
+            if (two) pv(vf, pf);
+        }
+    };
+    auto run = [&](auto act) {
+        if constexpr (decltype(act)::value) read_k(kf, stage0);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int si = 0; si < nst; si += 4) {
+            step(stage0, stage1, si, act);
+            if (si + 1 >= nst) break;
+            step(stage1, stage2, si + 1, act);
+            if (si + 2 >= nst) break;
+            step(stage2, stage3, si + 2, act);
+            if (si + 3 >= nst) break;
+            step(stage3, stage0, si + 3, act);
+        }
+    };
+    if (active) run(std::true_type{});
+    else run(std::false_type{});
 
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {

@@ -10,6 +10,14 @@ Llama-13B prompt of 8192 tokens (MHA, 40 heads, d 128, bf16):
     python -m chunked_prefill_paged_ca_amd.tile_sweep prompt [c ...]
         the whole prompt at token budget c, with chunk_align 0 and 32: the summed kernel time of
         all steps (append + attention + merge)
+    python -m chunked_prefill_paged_ca_amd.tile_sweep sweep [c ...]
+        the whole prompt at chunk size c against the one-shot prefill (c = 8192): attention time
+        summed over the K = 8192/c steps, the K/V bytes it must read (the history is read again
+        at every chunk) and the flops, each against its roofline
+
+The sweep follows the chunk-size trade-off of [SS] "为什么总 FLOPs 近似不变，显存流量却增加":
+the flops of the whole prompt do not depend on c, the K/V bytes read grow as c shrinks, so small
+chunks are bound by HBM and large ones by MFMA.
 
 Prints one markdown table per mode.  Needs the GPU library; uses random K/V (the timing does
 not depend on the values).
@@ -22,6 +30,9 @@ import numpy as np
 
 DEFAULT_SINGLE = [224, 255, 256, 257, 288, 511, 512, 513]
 DEFAULT_PROMPT = [256, 257, 512, 513]
+DEFAULT_SWEEP = [64, 128, 256, 512, 2048, 8192]
+HBM = 8.0e12
+MFMA = 2.5e15
 
 
 def _setup():
@@ -115,13 +126,55 @@ def prompt(cs, aligns=(0, 32)):
     return "\n".join(rows) + "\n"
 
 
+def sweep(cs, reps=3):
+    from chunked_prefill_paged_ca_amd import accounting as acc
+    torch, ca, wl, k, v, desc = _setup()
+    L, H, d = 8192, wl.num_kv_heads, wl.head_dim
+    rows = ["| c | steps | attention + merge us | K/V bytes read GB | flops GF | TB/s | TF/s | "
+            "roofline us (8 TB/s, 2.5 PF) | fraction of roofline | append + upload us |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for c in cs:
+        ctx = ca.create(0)
+        nc, steps, att, other, nbytes, flops = 0, 0, 0.0, 0.0, 0.0, 0.0
+        t_roof = 0.0
+        while nc < L:
+            plan = ca.plan_batch([nc], [L - nc], wl.block_tables, c, 0, 16, wl.num_pool_pages)
+            T = plan.num_tokens
+            _, chk = acc.plan_work([T], [nc + T], 0, wl.num_q_heads, H, d, 16)
+            q, kn, vn = _inputs(torch, wl, T)
+            _run_step(torch, ca, ctx, wl, k, v, desc, plan, q, kn, vn)  # warm this shape
+            torch.cuda.synchronize()
+            ctx.profile_read()
+            ctx.profile_enable(True)
+            for _ in range(reps):
+                _run_step(torch, ca, ctx, wl, k, v, desc, plan, q, kn, vn)
+            torch.cuda.synchronize()
+            ctx.profile_enable(False)
+            per = _kernel_us(ctx.profile_read())
+            att += sum(sum(per.get(n, [])) for n in ("attention", "chunk", "decode", "merge")) / reps
+            other += sum(sum(per.get(n, [])) for n in ("append_rope", "upload")) / reps
+            nbytes += chk.bytes
+            flops += chk.flops
+            t_roof += max(chk.bytes / HBM, chk.flops / MFMA)
+            nc += T
+            steps += 1
+        ctx.close()
+        rows.append(f"| {c} | {steps} | {att:.0f} | {nbytes / 1e9:.2f} | {flops / 1e9:.0f} | "
+                    f"{nbytes / att / 1e6:.2f} | {flops / att / 1e6:.0f} | {t_roof * 1e6:.0f} | "
+                    f"{t_roof * 1e6 / att:.2f} | {other:.0f} |")
+        print(rows[-1], file=sys.stderr, flush=True)
+    return "\n".join(rows) + "\n"
+
+
 def main(argv):
-    if not argv or argv[0] not in ("single", "prompt"):
+    if not argv or argv[0] not in ("single", "prompt", "sweep"):
         print(__doc__, file=sys.stderr)
         return 2
     cs = [int(x) for x in argv[1:]]
     if argv[0] == "single":
         sys.stdout.write(single(cs or DEFAULT_SINGLE))
+    elif argv[0] == "sweep":
+        sys.stdout.write(sweep(cs or DEFAULT_SWEEP))
     else:
         sys.stdout.write(prompt(cs or DEFAULT_PROMPT))
     return 0

@@ -181,7 +181,7 @@ def test_llama70b_share_sampled(env):
     run_and_check(ctx, oracle, wl, rows_per_seq=24, track=track, pool=(kc, vc), label="70b-share")
 
 
-@pytest.mark.parametrize("c,align", [(512, 0), (2048, 0), (257, 32)])
+@pytest.mark.parametrize("c,align", [(64, 0), (512, 0), (2048, 0), (257, 32)])
 def test_sweep_chunked_vs_one_shot(env, c, align):
     """Config 3: one 8192-token prompt at token budget c (chunks snapped to multiples of `align`
     when set: 257 with 32 gives 32 chunks of 256) against the oracle (sampled rows each step),
