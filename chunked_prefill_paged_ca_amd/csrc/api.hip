@@ -459,7 +459,7 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
     // fits there within that time, splitting a row block only adds its partials' round trip
     // through HBM and the merge: keep each block whole, as long as its workgroup still ends well
     // inside the decode time.  Measured on the part: one 32-key block of a 256-column workgroup
-    // takes ~1.75 us at d = 128, and the decode rows stream ~5.5 TB/s.
+    // takes ~1.3 us at d = 128, and the decode rows stream ~5.5 TB/s.
     const bool fused = plan->num_decodes > 0 && plan->num_seqs > plan->num_decodes && !ctx->split_attention;
     if (fused) {
         int64_t dec_keys = 0;
@@ -468,7 +468,7 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
             dec_keys += (np - 1) * plan->page_size + plan->kv_last_page_len[s];
         }
         const double dec_us = static_cast<double>(dec_keys) * sh.hkv * sh.d * 4 / 5.5e6;  // K + V bf16
-        const double block_us = sh.d == 128 ? 1.75 : 0.9;
+        const double block_us = sh.d == 128 ? 1.3 : 0.67;
         const double chunk_cus = ctx->num_cus * (1.0 - kMixedDecodeShare);
         if (static_cast<double>(work) / 32 * block_us <= 0.75 * chunk_cus * dec_us) {
             int32_t longest = 0;

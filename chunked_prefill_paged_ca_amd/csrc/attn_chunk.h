@@ -14,10 +14,11 @@
 // (row, q head) pair of the kv head's group, numbered row * G + head, so any group size packs the
 // MFMA tiles without padding.  A workgroup is 8 wavefronts of 32 columns (two waves per SIMD:
 // one wave's softmax overlaps the other's MFMAs), and one K/V tile in LDS serves all 256
-// columns.  Per 32-key block (two pages): the workgroup copies the two K pages and two V pages
-// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), kept three blocks
-// ahead of the block being consumed (four LDS stages); each wave then runs S^T = K Q^T and
-// O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with an online softmax per column.  The pages keep
+// columns.  Per 32-key block (two pages) the workgroup copies the two K pages and two V pages
+// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers); the blocks are
+// copied and published four at a time (a 128-key LDS stage, one barrier each), the next stage
+// in flight while one is consumed.  Each wave runs S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_16x16x32_bf16 with an online softmax per column.  The pages keep
 // their cache layout in LDS, where every fragment read is a bank-conflict-free contiguous run.
 // Only blocks that cross a row's diagonal need the mask; keys past a column's position get
 // weight 0, and V slots past the sequence end are zeroed in LDS before they reach the MFMA.
@@ -83,9 +84,19 @@ __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __res
     }
 }
 
-// One LDS stage holds two 32-key blocks (64 keys); each block keeps the four-run layout above.
+// One LDS stage holds kSub 32-key blocks; each block keeps the four-run layout above.  kStages
+// stages rotate: one is consumed while the others are in flight.  Measured on the part: the
+// workgroup barrier, not the copy, is what the stage size trades against -- with one barrier
+// per 32, 64, 96 and 128 keys the Yi-34B chunk took 588, 551, 523 and 502 us (192, 192, 96 and
+// 64 KB in flight) -- so the stages are as large as LDS allows two of (2 x 64 KB at d = 128).
+constexpr int kSub = 4;
+constexpr int kStages = 2;
 template <int D>
-constexpr int kStageHalves = 2 * 64 * D;
+constexpr int kStageHalves = kSub * 64 * D;
+
+// s_waitcnt immediate: wait until at most n vector memory operations are outstanding and
+// every LDS read has returned (expcnt not waited for)
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xf) | (0x7 << 4) | ((n >> 4) << 14); }
 
 // items: two int4 per item: {seq, kv head, first column (row * G + head), partial slot or -1},
 //                           {key begin, key end, 0, 0}   (seq -1: grid padding)
@@ -273,29 +284,36 @@ __device__ __forceinline__ void chunk_item(
         __syncthreads();
     };
 
-    // Four LDS stages of two 32-key blocks each, loop unrolled by four so each step names its
-    // stages at compile time: up to three stages (192 keys) are in flight (DMA) while one is
-    // consumed, which covers an L2/MALL or HBM round trip with several blocks of MFMA work.
-    // One wait and one barrier per stage (not per block): the wait covers only the stage about
-    // to be read (the DMA count of the stages issued after it may stay outstanding), and the
-    // barrier both publishes that stage and frees the one about to be refilled.
+    // kStages LDS stages of kSub 32-key blocks each, loop unrolled by kStages so each step
+    // names its stages at compile time: while one stage is consumed the others are in flight
+    // (DMA), which covers an L2/MALL or HBM round trip with several blocks of MFMA work.  One
+    // wait and one barrier per stage (not per block): the wait covers only the stage about to be
+    // read (the DMA count of the stages issued after it may stay outstanding), and the barrier
+    // both publishes that stage and frees the one about to be refilled.
+    static_assert(kStages >= 2 && kStages <= 4 && kSub >= 1 && kSub * (kStages - 2) <= 8, "stage shape");
     constexpr int U = 8 * D / (64 * kWaves);  // DMA instructions per wave per 32-key block
+    constexpr int SK = 32 * kSub;             // keys per stage
     const int nblk = (ke - kb + 31) >> 5;
-    const int nst = (nblk + 1) >> 1;
+    const int nst = (nblk + kSub - 1) / kSub;
     __syncthreads();  // page ids in LDS
-    int pa, pb, pc, pd;
-    // copy stage si (its one or two blocks) into `slot`
+    auto slot_of = [&](auto I) -> uint16_t* {
+        constexpr int i = decltype(I)::value % kStages;
+        if constexpr (i == 0) return stage0;
+        else if constexpr (i == 1) return stage1;
+        else if constexpr (i == 2) return stage2;
+        else return stage3;
+    };
+    // copy stage si (its first min(kSub, blocks left) blocks) into `slot`
     auto dma_stage = [&](uint16_t* slot, int si) {
-        page_pair(kb + 64 * si, &pa, &pb);
-        dma_block<D>(slot, k_cache, v_cache, pa, pb, g, hkv, w, lane);
-        if (2 * si + 1 < nblk) {
-            page_pair(kb + 64 * si + 32, &pc, &pd);
-            dma_block<D>(slot + 64 * D, k_cache, v_cache, pc, pd, g, hkv, w, lane);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            if (kSub * si + j < nblk) {
+                int pa, pb;
+                page_pair(kb + SK * si + 32 * j, &pa, &pb);
+                dma_block<D>(slot + 64 * D * j, k_cache, v_cache, pa, pb, g, hkv, w, lane);
+            }
         }
     };
-    dma_stage(stage0, 0);
-    if (nst > 1) dma_stage(stage1, 1);
-    if (nst > 2) dma_stage(stage2, 2);
     // Wait until at most `later` blocks' DMAs of this wave are still outstanding and every LDS
     // read of this wave has returned, then an execution barrier.  __syncthreads() would also be
     // a release fence, which makes the compiler drain every outstanding DMA first; here
@@ -304,80 +322,97 @@ __device__ __forceinline__ void chunk_item(
     // signal fence keeps the compiler from moving LDS accesses across it.
     auto wait_stage = [&](int later) {
         switch (later) {
-            case 0: __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4)); break;
-            case 1: __builtin_amdgcn_s_waitcnt(U | (0x7 << 4)); break;
-            case 2: __builtin_amdgcn_s_waitcnt((2 * U) | (0x7 << 4)); break;
-            case 3: __builtin_amdgcn_s_waitcnt((3 * U) | (0x7 << 4)); break;
-            default: __builtin_amdgcn_s_waitcnt((4 * U) | (0x7 << 4)); break;
+            case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(1 * U)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * U)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * U)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * U)); break;
+            case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5 * U)); break;
+            case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6 * U)); break;
+            case 7: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(7 * U)); break;
+            default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * U)); break;
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    // At step si's wait, stages 0 .. si+3 have been requested (blocks below min(nblk, 2si+8))
-    // and stage si+1 (blocks 2si+2, 2si+3) must be complete: the blocks requested after it may
-    // stay outstanding.
-    auto later_blocks = [&](int si) { return max(0, min(nblk, 2 * si + 8) - (2 * si + 4)); };
+    // At step si's wait, stages 0 .. si+kStages-1 have been requested (blocks below
+    // min(nblk, kSub (si + kStages))) and stage si+1 (blocks below kSub (si + 2)) must be
+    // complete: the blocks requested after it may stay outstanding.
+    auto later_blocks = [&](int si) { return max(0, min(nblk, kSub * (si + kStages)) - kSub * (si + 2)); };
     auto zero_stage_tail = [&](uint16_t* slot, int si) {
-        zero_v_tail(slot, kb + 64 * si);
-        zero_v_tail(slot + 64 * D, kb + 64 * si + 32);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) zero_v_tail(slot + 64 * D * j, kb + SK * si + 32 * j);
     };
-    wait_stage(max(0, min(nblk, 6) - 2));  // stage 0 landed
+    // prologue: stages 0 .. kStages-2 requested, stage 0 waited for, then the last slot filled
+#pragma unroll
+    for (int i = 0; i + 1 < kStages; ++i)
+        if (i < nst) dma_stage(i == 0 ? stage0 : i == 1 ? stage1 : stage2, i);
+    wait_stage(max(0, min(nblk, kSub * (kStages - 1)) - kSub));  // stage 0 landed
     zero_stage_tail(stage0, 0);
-    if (nst > 3) dma_stage(stage3, 3);
+    if (kStages - 1 < nst) dma_stage(slot_of(std::integral_constant<int, kStages - 1>{}), kStages - 1);
 
     // Stage si sits in `cur`, with its first block's K fragments already in kf; `nxt` holds
-    // stage si+1; `cur` is refilled with stage si+4 once every wave is past its reads.  Per
-    // block: QK -> V reads -> softmax -> (the next block's K reads) -> PV, so each block's K
+    // stage si+1; `cur` is refilled with stage si+kStages once every wave is past its reads.
+    // Per block: QK -> V reads -> softmax -> (the next block's K reads) -> PV, so each block's K
     // reads go out under the previous block's PV MFMAs.  A wave whose columns all lie past the
     // chunk (ACT false: the last column block of a chunk) only helps with the copies and
     // barriers.
     bf16x8 kf[2][D / 32];
     auto step = [&](uint16_t* cur, uint16_t* nxt, int si, auto act) {
         constexpr bool ACT = decltype(act)::value;
-        const int key0 = kb + 64 * si;
-        const bool two = 2 * si + 1 < nblk;
+        const int key0 = kb + SK * si;
+        const int nb = min(kSub, nblk - kSub * si);  // blocks in this stage
         floatx4 st[kTiles][2];
         bf16x8 vf[D / 16];
         bf16x8 pf[kTiles];
         if constexpr (ACT) {
-            qk(kf, st);
-            read_v(vf, cur);
-            softmax(st, key0, pf);
-            if (two) {
-                read_k(kf, cur + 64 * D);
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j + 1 < kSub; ++j) {
+                if (j < nb) {
+                    qk(kf, st);
+                    read_v(vf, cur + 64 * D * j);
+                    softmax(st, key0 + 32 * j, pf);
+                    if (j + 1 < nb) {
+                        read_k(kf, cur + 64 * D * (j + 1));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    pv(vf, pf);
+                }
             }
-            pv(vf, pf);
-            if (two) {
+            if (kSub - 1 < nb) {
                 qk(kf, st);
-                read_v(vf, cur + 64 * D);
-                softmax(st, key0 + 32, pf);
+                read_v(vf, cur + 64 * D * (kSub - 1));
+                softmax(st, key0 + 32 * (kSub - 1), pf);
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // the softmax completes before the barrier
         if (si + 1 < nst) {
-            wait_stage(later_blocks(si));  // stage si+1 landed; stages si+2, si+3 may still fly
+            wait_stage(later_blocks(si));  // stage si+1 landed; later stages may still fly
             zero_stage_tail(nxt, si + 1);
-            if (si + 4 < nst) dma_stage(cur, si + 4);
+            if (si + kStages < nst) dma_stage(cur, si + kStages);
             if constexpr (ACT) read_k(kf, nxt);
             __builtin_amdgcn_sched_barrier(0);  // the next block's K reads go out ahead of PV
         }
         if constexpr (ACT) {
-            if (two) pv(vf, pf);
+            if (kSub - 1 < nb) pv(vf, pf);
         }
     };
     auto run = [&](auto act) {
         if constexpr (decltype(act)::value) read_k(kf, stage0);
         __builtin_amdgcn_sched_barrier(0);
-        for (int si = 0; si < nst; si += 4) {
-            step(stage0, stage1, si, act);
+        for (int si = 0; si < nst; si += kStages) {
+            step(slot_of(std::integral_constant<int, 0>{}), slot_of(std::integral_constant<int, 1>{}), si, act);
             if (si + 1 >= nst) break;
-            step(stage1, stage2, si + 1, act);
-            if (si + 2 >= nst) break;
-            step(stage2, stage3, si + 2, act);
-            if (si + 3 >= nst) break;
-            step(stage3, stage0, si + 3, act);
+            step(slot_of(std::integral_constant<int, 1>{}), slot_of(std::integral_constant<int, 2>{}), si + 1, act);
+            if constexpr (kStages > 2) {
+                if (si + 2 >= nst) break;
+                step(slot_of(std::integral_constant<int, 2>{}), slot_of(std::integral_constant<int, 3>{}), si + 2, act);
+            }
+            if constexpr (kStages > 3) {
+                if (si + 3 >= nst) break;
+                step(slot_of(std::integral_constant<int, 3>{}), slot_of(std::integral_constant<int, 4>{}), si + 3, act);
+            }
         }
     };
     if (active) run(std::true_type{});
