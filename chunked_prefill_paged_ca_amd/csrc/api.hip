@@ -588,22 +588,38 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
             const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
             const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
             const int32_t ncols = q_len * G;
+            // Records go key range by key range (all column blocks of split 0, then of split 1,
+            // ...), so the workgroups that one XCD runs side by side read the same pages and
+            // share them in its L2; each column block's partial slots stay contiguous.
+            const int32_t nblocks = (ncols + cols_per_block - 1) / cols_per_block;
             for (int32_t g = 0; g < sh.hkv; ++g) {
-                for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+                int32_t max_split = 0;
+                const int32_t slot0 = cslots;
+                for (int32_t b = 0; b < nblocks; ++b) {
+                    const int32_t cb = b * cols_per_block;
                     const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
                     const int32_t key_end = kv_len - q_len + last / G + 1;  // last row's position + 1
                     const int32_t nsplit = (key_end + Lc - 1) / Lc;
-                    if (nsplit == 1) {
-                        clist.push_back(make_int4(s, g, cb, -1));
-                        clist.push_back(make_int4(0, key_end, 0, 0));
-                        continue;
+                    if (nsplit > max_split) max_split = nsplit;
+                    if (nsplit > 1) {
+                        groups.push_back(make_int4(s, g, cb, cslots));
+                        groups.push_back(make_int4(nsplit, plan->qo_indptr[s], q_len, 0));
+                        cslots += nsplit;
                     }
-                    groups.push_back(make_int4(s, g, cb, cslots));
-                    groups.push_back(make_int4(nsplit, plan->qo_indptr[s], q_len, 0));
-                    for (int32_t i = 0; i < nsplit; ++i) {
-                        const int32_t b = i * Lc, e = (b + Lc < key_end) ? b + Lc : key_end;
-                        clist.push_back(make_int4(s, g, cb, cslots++));
-                        clist.push_back(make_int4(b, e, 0, 0));
+                }
+                for (int32_t i = 0; i < max_split; ++i) {
+                    int32_t slot = slot0;
+                    for (int32_t b = 0; b < nblocks; ++b) {
+                        const int32_t cb = b * cols_per_block;
+                        const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+                        const int32_t key_end = kv_len - q_len + last / G + 1;
+                        const int32_t nsplit = (key_end + Lc - 1) / Lc;
+                        if (i < nsplit) {
+                            const int32_t kb = i * Lc, ke = (kb + Lc < key_end) ? kb + Lc : key_end;
+                            clist.push_back(make_int4(s, g, cb, nsplit == 1 ? -1 : slot + i));
+                            clist.push_back(make_int4(kb, ke, 0, 0));
+                        }
+                        if (nsplit > 1) slot += nsplit;
                     }
                 }
             }
