@@ -16,7 +16,9 @@ every step of the timed region).  `traffic` is the HBM bytes the counters measur
 launch (profiles/), used only for the workload they were taken on and while the kernel sources
 are unchanged.
 `parts` times the decode and chunk work as two separate launches in a second, untimed pass, for
-their own HBM and bf16 MFMA fractions.  `cpu_baseline` times the CPU oracle on the same step.
+their own HBM and bf16 MFMA fractions.  `measured_peaks` re-measures, after the timed region,
+what this device sustains (a 4 GiB read stream, a 1 GiB copy, an 8192^3 bf16 GEMM on random data) and
+places the roofline launch against the matching one.  `cpu_baseline` times the CPU oracle on the same step.
 """
 import argparse
 import json
@@ -83,6 +85,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip re-measuring the HBM and bf16 GEMM rates this device sustains")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, copy this many MiB device to device once (a "
                          "known-size reference for the HBM byte counters)")
@@ -205,6 +209,17 @@ def main():
                               "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                               "alg_flops_per_launch": int(chk_w.flops)}
         out["parts"] = parts
+
+    # ---- what this device sustains (after the timed region): the roofline above uses the
+    # datasheet peaks; these put the same launch against measured ones ----
+    if not args.no_peaks:
+        from chunked_prefill_paged_ca_amd import peaks
+        rd, cp, gm = peaks.hbm_read_gbs(), peaks.hbm_copy_gbs(), peaks.gemm_tflops("randn")
+        r = out["roofline"]
+        meas = rd if r["bound"] == "hbm" else gm
+        out["measured_peaks"] = {"hbm_read_GBs": round(rd, 1), "hbm_copy_GBs": round(cp, 1),
+                                 "bf16_gemm_8192_TFs": round(gm, 1),
+                                 "roofline_frac_of_measured": round(r["achieved"] / meas, 4)}
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4

@@ -1,7 +1,8 @@
 """Build the HIP library libca.so in-tree for gfx950 (hipcc; no JIT, no torch extension).
 
 Every kernel source and the host runtime are compiled into one shared library whose only
-interface is the C ABI of include/ca.h.
+interface is the C ABI of include/ca.h.  A second, separate library, libca_probe.so, holds the
+measurement probe of csrc/probe_mfma.hip (not part of the attention path).
 """
 import os
 import shutil
@@ -15,6 +16,8 @@ LIB = os.path.join(PKG, "libca.so")
 SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "linear.cpp", "append_rope.hip", "attn_generic.hip",
            "attn_mixed.hip", "merge.hip"]
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]  # the QKV projection's GEMM
+PROBE_LIB = os.path.join(PKG, "libca_probe.so")
+PROBE_SOURCE = "probe_mfma.hip"
 
 
 def hipcc() -> str:
@@ -57,6 +60,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
     os.replace(tmp, LIB)
+    probe = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip",
+             os.path.join(CSRC, PROBE_SOURCE), "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    pr = subprocess.run(probe, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if pr.returncode:
+        print(pr.stdout.decode(errors="replace"), flush=True)
+        raise RuntimeError(f"hipcc failed for {PROBE_SOURCE}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

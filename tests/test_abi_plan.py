@@ -25,6 +25,17 @@ def test_exports_every_header_symbol(L):
         assert hasattr(L, s), s
 
 
+def test_probe_library_exports_its_entry_point(L):
+    """The measurement probe is its own library (not part of the ca_* ABI); it loads without a
+    GPU and exports its one C entry point."""
+    import ctypes
+    from chunked_prefill_paged_ca_amd import peaks
+    probe = ctypes.CDLL(peaks.PROBE_LIB)
+    for sym in ("ca_probe_mfma_rate", "ca_probe_read_rate"):
+        assert hasattr(probe, sym)
+        assert not hasattr(L, sym)
+
+
 def test_status_strings(L):
     for s in range(6):
         assert binding.status_string(s)
