@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--time-every", type=int, default=1,
+                    help="attach the timing events to the attention launch of every N-th step of "
+                         "the timed region (1: every step)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip re-measuring the HBM and bf16 GEMM rates this device sustains")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -127,10 +130,12 @@ def main():
                                  wl.head_dim, wl.page_size)
     stream = torch.cuda.current_stream()
 
-    def run_steps(ctx, n):
-        for _ in range(n):
+    def run_steps(ctx, n, time_every=0):
+        for i in range(n):
             plan = batch.plan()
             ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages, stream=stream)
+            if time_every:
+                ctx.profile_enable(ca.PROFILE_ATTENTION if i % time_every == 0 else False)
             ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, lse, stream=stream)
 
     def kernel_means(recs):
@@ -144,10 +149,9 @@ def main():
     run_steps(ctx, args.warmup)
     torch.cuda.synchronize()
     ctx.profile_read()
-    ctx.profile_enable(ca.PROFILE_ATTENTION)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(ctx, args.steps)
+    run_steps(ctx, args.steps, time_every=max(1, args.time_every))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ctx.profile_enable(False)
