@@ -10,7 +10,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
+#include <map>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -89,7 +91,7 @@ struct Staging {
 
     hipError_t init() {
         for (int i = 0; i < kSlots / kGroup; ++i) {
-            hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+            hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming | hipEventDisableSystemFence);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -133,6 +135,12 @@ struct Staging {
                               static_cast<const uint4*>(dev[slot]), static_cast<uint4*>(dst), n);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        return mark_read(slot, stream);
+    }
+    // After the launch that reads `slot` has been enqueued on `stream` (the upload kernel, or an
+    // append launch that copies the slot itself).
+    hipError_t mark_read(int slot, hipStream_t stream) {
+        hipError_t e = hipSuccess;
         if (slot % kGroup == kGroup - 1) {
             e = hipEventRecord(ev[slot / kGroup], stream);
             if (e != hipSuccess) return e;
@@ -253,7 +261,17 @@ struct ca_ctx {
     Staging staging;
     DevBuf meta_buf;        // one upload per step: plan metadata, then the work lists
     DevPlan dplan{};
-    const double* inv_freq = nullptr;  // [d / 2] rotary inverse frequencies, in meta_buf
+    const double* inv_freq = nullptr;  // [d / 2] rotary inverse frequencies of the current shape
+    // one device table of inverse frequencies per (head dim, rotary base), filled once and kept
+    // (a table may still be read by an earlier launch when another shape comes along)
+    std::map<std::pair<int32_t, double>, void*> freq_tables;
+    // Set by prepare(..., defer = true): the step's metadata sits in staging slot `defer_slot`
+    // (defer_bytes) and has not been copied to meta_buf yet; hrow_pos / hrow_page are its per-row
+    // arrays as the device sees the staging.  The next append launch copies it.
+    int defer_slot = -1;
+    size_t defer_bytes = 0;
+    const int32_t* hrow_pos = nullptr;
+    const int32_t* hrow_page = nullptr;
     DevBuf partial_buf;     // fp32 split-KV partials of the generic path
     WorkKey work_key{};     // what meta_buf holds (generation 0: nothing)
     DevWork dwork{};
@@ -522,8 +540,33 @@ int32_t xcd_order(const std::vector<int4>& in, std::vector<int4>& out) {
 //   [decode items | first item of each decode wave | decode merges | chunk items | chunk merges]
 // keyed by (plan generation, shape, split sizes), so the append and the attention of one step
 // share it and a repeated call with the same plan uploads nothing.
+// The rotary inverse frequencies theta^(-2i/d) of this shape, fp64, as a device table (built on
+// the host once per (d, theta) and kept for the context's lifetime).
+ca_status ensure_freq(ca_ctx* ctx, const Shape& sh) {
+    const std::pair<int32_t, double> key(sh.d, static_cast<double>(sh.theta));
+    auto it = ctx->freq_tables.find(key);
+    if (it == ctx->freq_tables.end()) {
+        std::vector<double> f(static_cast<size_t>(sh.d / 2));
+        for (int32_t i = 0; i < sh.d / 2; ++i)
+            f[static_cast<size_t>(i)] = std::pow(static_cast<double>(sh.theta), -2.0 * static_cast<double>(i) / static_cast<double>(sh.d));
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, f.size() * sizeof(double));
+        if (e != hipSuccess) return device_error("rotary table allocation", e);
+        e = hipMemcpy(p, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return device_error("rotary table copy", e);
+        }
+        it = ctx->freq_tables.emplace(key, p).first;
+    }
+    ctx->inv_freq = static_cast<const double*>(it->second);
+    return CA_OK;
+}
+
+// defer: leave the metadata in its staging slot (ctx->defer_slot) for the append launch that
+// follows to copy; otherwise copy it now with the upload kernel.
 ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool defer = false) {
     const int G = sh.hq / sh.hkv;
     int32_t dec_wgs = 0;
     const bool mfma = sh.dtype == CA_BF16 && G <= 16;
@@ -532,6 +575,10 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
                 mfma ? chunk_split_keys(ctx, plan, sh, ctx->csplit_override) : -1, sh.theta};
     if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
     ca_status st = validate_plan_arrays(plan, pool);
+    if (st != CA_OK) return st;
+    ctx->work_key = WorkKey{};  // meta_buf is about to change; nothing matches until it is whole
+    ctx->defer_slot = -1;
+    st = ensure_freq(ctx, sh);
     if (st != CA_OK) return st;
 
     std::vector<int4> items, merges, citems, groups;
@@ -633,8 +680,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     const int32_t ns = plan->num_seqs;
     const int32_t T = plan->num_tokens;
     const size_t plan_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages + 3 * static_cast<size_t>(T);
-    const size_t off_freq = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
-    const size_t off_items = off_freq + (static_cast<size_t>(sh.d / 2) * sizeof(double) + 15) / 16 * 16;
+    const size_t off_items = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
     const size_t n_items = items.size() / 2, n_merges = merges.size();
     const size_t wave_words = (wave_items.size() + 3) / 4 * 4;
     const size_t off_out = off_items + items.size() * sizeof(int4);
@@ -669,21 +715,27 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
             hpage[q0 + i] = plan->kv_page_indices[p0 + pos / plan->page_size];
         }
     }
-    // rotary inverse frequencies theta^(-2i/d), fp64
-    double* hfreq = reinterpret_cast<double*>(h + off_freq);
-    for (int32_t i = 0; i < sh.d / 2; ++i)
-        hfreq[i] = std::pow(sh.theta, -2.0 * static_cast<double>(i) / static_cast<double>(sh.d));
     std::memcpy(h + off_items, items.data(), items.size() * sizeof(int4));
     std::memcpy(h + off_out, wave_items.data(), wave_items.size() * sizeof(int32_t));
     std::memcpy(h + off_merge, merges.data(), n_merges * sizeof(int4));
     std::memcpy(h + off_citem, citems.data(), citems.size() * sizeof(int4));
     std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
-    {
+    const size_t row_pos_off = (static_cast<size_t>(2) * (ns + 1) + ns + plan->num_pages + T) * sizeof(int32_t);
+    if (defer) {
+        ctx->defer_slot = slot;
+        ctx->defer_bytes = bytes;
+        const char* hd = static_cast<const char*>(ctx->staging.dev[slot]);
+        ctx->hrow_pos = reinterpret_cast<const int32_t*>(hd + row_pos_off);
+        ctx->hrow_page = ctx->hrow_pos + T;
+    } else {
         Timed t(ctx->prof, "upload", CA_PROFILE_UPLOAD);
         e = ctx->staging.upload(slot, ctx->meta_buf.ptr, bytes, stream, t.ev);
         if (e == hipSuccess) t.commit();
+        if (e != hipSuccess) {
+            ctx->work_key = WorkKey{};
+            return device_error("metadata upload", e);
+        }
     }
-    if (e != hipSuccess) return device_error("metadata upload", e);
 
     const char* d = static_cast<const char*>(ctx->meta_buf.ptr);
     const int32_t* dp = reinterpret_cast<const int32_t*>(d);
@@ -694,7 +746,6 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     ctx->dplan.row_seq = dp + 2 * (ns + 1) + ns + plan->num_pages;
     ctx->dplan.row_pos = ctx->dplan.row_seq + T;
     ctx->dplan.row_page = ctx->dplan.row_pos + T;
-    ctx->inv_freq = reinterpret_cast<const double*>(d + off_freq);
     ctx->dplan.num_seqs = ns;
     ctx->dplan.num_decodes = plan->num_decodes;
     ctx->dplan.num_tokens = plan->num_tokens;
@@ -773,6 +824,7 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->chk_acc_buf.release();
     ctx->chk_ml_buf.release();
     ctx->prof.release();
+    for (auto& kv : ctx->freq_tables) (void)hipFree(kv.second);
     ca::linear_release(ctx->linear);
     delete ctx;
     return CA_OK;
@@ -807,17 +859,31 @@ ca_status append_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    st = prepare(ctx, plan, sh, num_pool_pages, stream);
+    st = prepare(ctx, plan, sh, num_pool_pages, stream, /*defer=*/true);
     if (st != CA_OK) return st;
+    // A fresh plan's metadata is still in its staging slot: this launch also copies it to device
+    // memory (for the attention launch after it), and reads its own per-row values from the
+    // staging.  A plan already on the device (append called again) takes the device copy.
+    const int slot = ctx->defer_slot;
+    const bool copy = slot >= 0;
     hipError_t e;
     {
         Timed t(ctx->prof, "append_rope", CA_PROFILE_APPEND);
-        e = ca::launch_append_rope(ctx->dplan, sh, ctx->inv_freq, q_in, q_out, k_new, v_new, k_cache,
-                                   v_cache, q_row < 0 ? int64_t(sh.hq) * sh.d : q_row,
-                                   kv_row < 0 ? int64_t(sh.hkv) * sh.d : kv_row, stream, t.ev);
+        e = ca::launch_append_rope(ctx->dplan, sh, copy ? ctx->hrow_pos : ctx->dplan.row_pos,
+                                   copy ? ctx->hrow_page : ctx->dplan.row_page, ctx->inv_freq, q_in,
+                                   q_out, k_new, v_new, k_cache, v_cache,
+                                   q_row < 0 ? int64_t(sh.hq) * sh.d : q_row,
+                                   kv_row < 0 ? int64_t(sh.hkv) * sh.d : kv_row,
+                                   copy ? ctx->staging.dev[slot] : nullptr, copy ? ctx->meta_buf.ptr : nullptr,
+                                   copy ? static_cast<int64_t>(ctx->defer_bytes / 16) : 0, stream, t.ev);
         if (e == hipSuccess) t.commit();
     }
-    if (e != hipSuccess) return device_error("append_rope launch", e);
+    ctx->defer_slot = -1;
+    if (e == hipSuccess && copy) e = ctx->staging.mark_read(slot, stream);
+    if (e != hipSuccess) {
+        if (copy) ctx->work_key = WorkKey{};  // the metadata never reached the device
+        return device_error("append_rope launch", e);
+    }
     return CA_OK;
 }
 

@@ -9,6 +9,10 @@
 //   * the token's position and destination page come from per-row arrays the host fills with
 //     the plan (no sequence -> indptr -> page-id chain), and the inverse frequencies
 //     theta^(-2i/d) are a host-computed fp64 table;
+//   * when the step's metadata has not reached device memory yet, extra workgroups after the
+//     token workgroups copy it there from the pinned host staging (for the attention launch that
+//     follows in stream order), and the token workgroups read their two per-row values straight
+//     from that staging: the copy overlaps the append instead of running before it;
 //   * every q/k/v load is a 16-byte vector load, all issued before the first store (a thread
 //     writes back exactly the elements it read, so q_out may alias q_in), and unconditional so
 //     that they are in flight together; q, k and v rows are read with their own row strides, so
@@ -62,18 +66,26 @@ __device__ __forceinline__ float narrow<float>(double x) { return static_cast<fl
 template <>
 __device__ __forceinline__ uint16_t narrow<uint16_t>(double x) { return double_to_bf16_bits(x); }
 
+// Workgroups [num_tokens, gridDim.x) copy meta_n16 16-byte units from meta_src to meta_dst.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) append_rope_kernel(
     const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_page,
     const double* __restrict__ inv_freq, const T* q_in, T* q_out, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ k_cache, T* __restrict__ v_cache, int hq,
-    int hkv, int d, int P, int64_t q_row, int64_t kv_row) {
+    int hkv, int d, int P, int64_t q_row, int64_t kv_row, int num_tokens,
+    const uint4* __restrict__ meta_src, uint4* __restrict__ meta_dst, int64_t meta_n16) {
 #pragma clang fp contract(off)
     constexpr int N = Vec<T>::N;
     __shared__ double s_cos[64];
     __shared__ double s_sin[64];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    if (t >= num_tokens) {  // metadata copy workgroup (uniform branch)
+        const int64_t stride = static_cast<int64_t>(gridDim.x - num_tokens) * kThreads;
+        for (int64_t i = static_cast<int64_t>(t - num_tokens) * kThreads + tid; i < meta_n16; i += stride)
+            meta_dst[i] = meta_src[i];
+        return;
+    }
     const int half = d >> 1;
     const int per_head = half / N;  // vector units per head (each covers N pairs)
     const int units = (hq + hkv) * per_head;
@@ -164,25 +176,33 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
 
 }  // namespace
 
-hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
-                              const void* q_in, void* q_out, const void* k_new, const void* v_new,
-                              void* k_cache, void* v_cache, int64_t q_row, int64_t kv_row,
-                              hipStream_t stream, const LaunchEvents& ev) {
+hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* row_pos,
+                              const int32_t* row_page, const double* inv_freq, const void* q_in,
+                              void* q_out, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, int64_t q_row, int64_t kv_row, const void* meta_src,
+                              void* meta_dst, int64_t meta_n16, hipStream_t stream,
+                              const LaunchEvents& ev) {
     if (p.num_tokens <= 0) return hipSuccess;
-    const dim3 grid(p.num_tokens), block(kThreads);
+    // one 16-byte unit per copy thread: the staging is read over PCIe, where many small reads in
+    // flight at once are what keeps the copy short
+    const int64_t copy_wgs64 = meta_n16 > 0 ? (meta_n16 + kThreads - 1) / kThreads : 0;
+    const int copy_wgs = static_cast<int>(copy_wgs64 < 256 ? copy_wgs64 : 256);
+    const dim3 grid(p.num_tokens + copy_wgs), block(kThreads);
+    const uint4* msrc = static_cast<const uint4*>(meta_src);
+    uint4* mdst = static_cast<uint4*>(meta_dst);
     if (sh.dtype == CA_FP32) {
-        hipExtLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, ev.start, ev.stop, 0, p.row_pos, p.row_page,
+        hipExtLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos, row_page,
                            inv_freq, static_cast<const float*>(q_in), static_cast<float*>(q_out),
                            static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                            static_cast<float*>(k_cache), static_cast<float*>(v_cache), sh.hq,
-                           sh.hkv, sh.d, p.page_size, q_row, kv_row);
+                           sh.hkv, sh.d, p.page_size, q_row, kv_row, p.num_tokens, msrc, mdst, meta_n16);
     } else {
-        hipExtLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, ev.start, ev.stop, 0, p.row_pos,
-                           p.row_page, inv_freq, static_cast<const uint16_t*>(q_in),
+        hipExtLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos,
+                           row_page, inv_freq, static_cast<const uint16_t*>(q_in),
                            static_cast<uint16_t*>(q_out), static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
                            static_cast<uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, p.page_size, q_row,
-                           kv_row);
+                           kv_row, p.num_tokens, msrc, mdst, meta_n16);
     }
     return hipGetLastError();
 }

@@ -79,10 +79,15 @@ bool linear_bf16(Linear*& L, int64_t T, int64_t K, int64_t N, const void* x, con
                  void* out, hipStream_t stream, std::string* err);
 
 // q_row, kv_row: elements between consecutive token rows of q_in and of k_new / v_new.
-hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const double* inv_freq,
-                              const void* q_in, void* q_out, const void* k_new, const void* v_new,
-                              void* k_cache, void* v_cache, int64_t q_row, int64_t kv_row,
-                              hipStream_t stream, const LaunchEvents& ev);
+// row_pos, row_page: [num_tokens] per-row position and destination page (device memory or the
+// device-mapped host staging).  meta_n16 > 0: the same launch also copies meta_n16 16-byte units
+// from meta_src (device-mapped host staging) to meta_dst (device memory).
+hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* row_pos,
+                              const int32_t* row_page, const double* inv_freq, const void* q_in,
+                              void* q_out, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, int64_t q_row, int64_t kv_row, const void* meta_src,
+                              void* meta_dst, int64_t meta_n16, hipStream_t stream,
+                              const LaunchEvents& ev);
 
 // Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
 // partial: fp32 workspace of num_tokens * hq * nsplit * (d + 2) floats.

@@ -179,7 +179,9 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
  * start/stop HIP event pair attached to the dispatch itself (hipExtLaunchKernel), so the
  * figures are device time of that launch alone and timing adds no packet to the stream.  ca_profile_read waits for the recorded events, copies up to `cap` records
  * (oldest first), sets *count to the number copied and forgets every record read or not.
- * Names are static strings: "upload" (the step's metadata, host staging -> device), "append_rope",
+ * Names are static strings: "upload" (the step's metadata, host staging -> device, when an
+ * attention call is the first to see a plan; after ca_append_kv_rope the append launch has
+ * copied it, inside "append_rope"), "append_rope",
  * "attention" (decode and prefill-chunk rows in one launch; with CA_SPLIT_ATTENTION=1 in the
  * environment at ca_create they are two launches named "chunk" and "decode"), "merge" (both
  * kinds of split merge in one launch) and "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between reads; later ones are
