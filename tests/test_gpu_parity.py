@@ -402,6 +402,32 @@ def test_edge_cases(env):
         assert np.array_equal(res[0][1], res2[0][1]) and np.array_equal(res[0][2], res2[0][2])
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 64), (32, 2, 128), (8, 8, 64)])
+def test_chunk_kernel_shapes(env, hq, hkv, d):
+    """Chunk rows through many 128-key LDS stages for the group sizes and head dims the MFMA path
+    takes -- G = 16 (its limit) at d = 64 and 128, G = 1 at d = 64 -- beside a decode in the same
+    launch: a 100-row chunk on 700 cached keys (25 key blocks: six full stages and a partial
+    one; at G = 16 its last column block holds 64 columns, so six of its eight waves only copy),
+    a 37-row chunk from position 0, and a 1501-key decode."""
+    from chunked_prefill_paged_ca_amd.workload import Workload
+    ctx, oracle = env
+    nc = np.array([1500, 0, 700], np.int32)
+    left = np.array([0, 37, 100], np.int32)
+    stream = np.array([1, 37, 100], np.int32)
+    pool = 256
+    perm = np.random.default_rng(21).permutation(pool).astype(np.int32)
+    tabs, it = [], 0
+    for r in range(3):
+        n = -(-int(nc[r] + stream[r]) // 16)
+        tabs.append(perm[it:it + n]); it += n
+    wl = Workload(name="chunk-shapes", config=0, seed=78, num_q_heads=hq, num_kv_heads=hkv,
+                  head_dim=d, page_size=16, dtype="bf16", token_budget=256, max_chunk=0,
+                  num_pool_pages=pool, num_computed=nc, num_prompt_left=left, block_tables=tabs,
+                  stream_len=stream)
+    res, _, _ = run_and_check(ctx, oracle, wl, rows_per_seq=24, label=f"chunk-shapes-{hq}/{hkv}/{d}")
+    assert res[0][0]["num_decodes"] == 1 and res[0][0]["num_tokens"] == 138
+
+
 def test_empty_step_is_noop(env):
     import torch
     import chunked_prefill_paged_ca_amd as ca
