@@ -155,8 +155,11 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ctx.profile_enable(False)
-    km0 = kernel_means(ctx.profile_read())
-    attn_ms = km0["attention"] if "attention" in km0 else km0["generic"]  # fp32 storage: plain kernel
+    recs0 = ctx.profile_read()
+    km0 = kernel_means(recs0)
+    attn_name = "attention" if "attention" in km0 else "generic"  # fp32 storage: plain kernel
+    attn_ms = km0[attn_name]
+    attn_all = np.array([ms for n, ms in recs0 if n == attn_name])
     ctx.close()
     ms_per_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
@@ -184,7 +187,9 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "alg_bytes_per_launch": int(attn_bytes),
                      "alg_flops_per_launch": int(chk_w.flops),
-                     "launch_ms": round(attn_ms, 5)},
+                     "launch_ms": round(attn_ms, 5),
+                     "launch_ms_p10_p50_p90": [round(float(np.percentile(attn_all, x)), 5) for x in (10, 50, 90)],
+                     "launches_timed": int(attn_all.size)},
     }
 
     # ---- second pass (not timed for `value`): decode and chunk as separate launches ----
