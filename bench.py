@@ -11,10 +11,10 @@ Prints ONE JSON line.  `value` is tokens per second of whole steps over the time
 the prefill-chunk rows side by side -- against the peak of the resource its algorithmic work
 needs longest: reading the K/V pages at 8 TB/s HBM (the default workload and every
 decode-heavy one), or the chunk rows' flops at 2.5 PFLOP/s bf16 MFMA (long prefill chunks),
-using the launch's own duration (HIP events attached to that launch on the bench's stream,
-every step of the timed region).  `traffic` is the HBM bytes the counters measured for that
-launch (profiles/), used only for the workload they were taken on and while the kernel sources
-are unchanged.
+using the launch's own duration (HIP events attached to that launch on the bench's stream, on
+every tenth step of the timed region by default: each timed launch adds ~2 us to its step).
+`traffic` is the HBM bytes the counters measured for that launch (profiles/), used only for the
+workload they were taken on and while the kernel sources are unchanged.
 `parts` times the decode and chunk work as two separate launches in a second, untimed pass, for
 their own HBM and bf16 MFMA fractions.  `measured_peaks` re-measures, after the timed region,
 what this device sustains (a 4 GiB read stream, a 1 GiB copy, an 8192^3 bf16 GEMM on random data) and
@@ -80,14 +80,15 @@ def cpu_baseline(wl, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
-    ap.add_argument("--time-every", type=int, default=1,
+    ap.add_argument("--time-every", type=int, default=10,
                     help="attach the timing events to the attention launch of every N-th step of "
-                         "the timed region (1: every step)")
+                         "the timed region (1: every step; each timed launch adds ~2 us to its "
+                         "step, so the default times one step in ten)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip re-measuring the HBM and bf16 GEMM rates this device sustains")
     ap.add_argument("--copy-mib", type=int, default=0,

@@ -186,6 +186,7 @@ struct DevWork {
     const int4* chunk_groups = nullptr;  // two int4 per multi-split row block
     int32_t num_dec_items = 0, num_dec_waves = 0, num_merges = 0, num_slots = 0;
     int32_t dec_wgs = 0;  // decode workgroups of the attention launch
+    int32_t dec_wpg = 0;  // decode wavefronts per decode workgroup
     int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0;
 };
 
@@ -255,6 +256,14 @@ struct Timed {
     }
 };
 
+// Decode wavefronts per decode workgroup (one workgroup per CU, so one decode wave per SIMD).
+// Measured on the part (same box, attention launch): the Mistral-7B and LLaMA2-70B steps take
+// the same time with 4 or 8 decode waves per CU (the HBM stream rate does not depend on it); the
+// chunk-heavy Yi-34B step is 4 % faster with 4.  A per-wave timeline also showed that a SIMD's
+// older wave gets most of the SIMD's share of the memory pipe (equal shares ended 40 % apart
+// with 8 waves per CU).
+constexpr int32_t kDecodeWavesPerWg = 4;
+
 struct ca_ctx {
     int device = 0;
     Profiler prof;
@@ -282,6 +291,7 @@ struct ca_ctx {
     int32_t num_cus = 0;
     int32_t attn_wgs_per_cu[2] = {0, 0};  // d = 64, d = 128 (queried on first use)
     int32_t dec_wgs_override = 0;  // CA_DECODE_WGS: decode workgroups of a mixed launch, 0 = auto
+    int32_t dec_wpg = kDecodeWavesPerWg;  // CA_DECODE_WAVES: decode wavefronts per workgroup
     bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
     ca::Linear* linear = nullptr;  // hipBLASLt state of ca_qkv_projection (created on first use)
@@ -436,9 +446,9 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t
         n = (n + 7) / 8 * 8;
         if (n > slots) n = slots;
     }
-    const int64_t W = static_cast<int64_t>(n) * ca::attention_decode_waves_per_wg();
+    const int32_t per_wg = ctx->dec_wpg;
+    const int64_t W = static_cast<int64_t>(n) * per_wg;
     const int32_t shares = static_cast<int32_t>(W < blocks ? W : blocks);
-    const int32_t per_wg = ca::attention_decode_waves_per_wg();
     *wgs = shares > 0 ? (shares + per_wg - 1) / per_wg : 0;
     if (mixed) *wgs = (*wgs + 7) / 8 * 8;  // keep the chunk workgroups' XCD order
     return shares;
@@ -760,6 +770,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     w.num_dec_items = static_cast<int32_t>(n_items);
     w.num_dec_waves = wave_items.empty() ? 0 : static_cast<int32_t>(wave_items.size()) - 1;
     w.dec_wgs = dec_wgs;
+    w.dec_wpg = ctx->dec_wpg;
     w.num_merges = static_cast<int32_t>(n_merges);
     w.num_slots = slots;
     w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
@@ -796,6 +807,10 @@ ca_status ca_create(int device, ca_ctx** out) {
     ctx->device = device;
     if (const char* env = std::getenv("CA_DECODE_WGS")) ctx->dec_wgs_override = std::atoi(env);
     if (const char* env = std::getenv("CA_SPLIT_ATTENTION")) ctx->split_attention = std::atoi(env) != 0;
+    if (const char* env = std::getenv("CA_DECODE_WAVES")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v <= ca::attention_decode_waves_per_wg()) ctx->dec_wpg = v;
+    }
     e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess || ctx->num_cus <= 0) {
         delete ctx;
@@ -987,21 +1002,21 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         // of the same kernel, each over the whole device, to time them separately.
         if (!ctx->split_attention) {
             Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION);
-            e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_items, w.dec_wave_items,
+            e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
                                      w.num_dec_waves, w.chunk_items, w.num_chunk_items, q, k_cache,
                                      v_cache, dacc, dml, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
         } else {
             if (w.num_chunk_items > 0) {
                 Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION);
-                e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_items, w.dec_wave_items, 0,
+                e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_wpg, w.dec_items, w.dec_wave_items, 0,
                                          w.chunk_items, w.num_chunk_items, q, k_cache, v_cache,
                                          dacc, dml, cacc, cml, o, lse, stream, t.ev);
                 if (e == hipSuccess) t.commit();
             }
             if (e == hipSuccess && w.num_dec_waves > 0) {
                 Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION);
-                e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_items, w.dec_wave_items,
+                e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
                                          w.num_dec_waves, w.chunk_items, 0, q, k_cache, v_cache,
                                          dacc, dml, cacc, cml, o, lse, stream, t.ev);
                 if (e == hipSuccess) t.commit();

@@ -8,8 +8,8 @@
 // of work can run on the chip at the same time instead of one after the other.
 //
 // The grid is [dec_wgs decode workgroups][chunk workgroups].  Workgroups are dispatched in index
-// order, so the decode workgroups (8 wavefronts each, every wave streaming its equal share of the
-// decode K/V blocks, attn_decode.h) start first and stay resident on dec_wgs CUs until their
+// order, so the decode workgroups (dec_wpg wavefronts each, every wave streaming its equal share
+// of the decode K/V blocks, attn_decode.h) start first and stay resident on dec_wgs CUs until their
 // shares are done; the chunk workgroups (attn_chunk.h) run on the remaining CUs from the start
 // and take over the decode CUs as those drain.  Decode reaches the HBM bandwidth on a fraction of
 // the CUs, so the chunk work fills CUs the decode stream does not need.  Either part may be
@@ -29,8 +29,9 @@ constexpr int kDecodeWaves = kThreads / 64;
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
-    DevPlan p, int dec_wgs, const int4* __restrict__ dec_items, const int32_t* __restrict__ wave_items,
-    int num_waves, const int4* __restrict__ chunk_items, const uint16_t* __restrict__ qg,
+    DevPlan p, int dec_wgs, int dec_wpg, const int4* __restrict__ dec_items,
+    const int32_t* __restrict__ wave_items, int num_waves, const int4* __restrict__ chunk_items,
+    const uint16_t* __restrict__ qg,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
     float scale_log2, float* __restrict__ dec_acc, float2* __restrict__ dec_ml,
     float* __restrict__ chunk_acc, float2* __restrict__ chunk_ml, uint16_t* __restrict__ o,
@@ -40,7 +41,9 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
         // scalar registers and is read with scalar loads, which do not share the vector-load
         // counter the K/V prefetch relies on
         const int lane = threadIdx.x & 63;
-        const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + (threadIdx.x >> 6));
+        const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (wi >= dec_wpg) return;
+        const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * dec_wpg + wi);
         if (w >= num_waves) return;
         const ConstPtr<int32_t> bounds = as_const(wave_items);
         const ConstPtr<int32_t> recs = as_const(reinterpret_cast<const int32_t*>(dec_items));
@@ -61,14 +64,16 @@ int chunk_cols_per_block() { return chunk::kCols; }
 int chunk_max_split_keys() { return 16 * (chunk::kMaxItemPages - 2); }
 int attention_decode_waves_per_wg() { return kDecodeWaves; }
 
-hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, const int4* dec_items,
-                            const int32_t* wave_items, int num_waves, const int4* chunk_items,
+hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int dec_wpg,
+                            const int4* dec_items, const int32_t* wave_items, int num_waves,
+                            const int4* chunk_items,
                             int num_chunk_items, const void* q, const void* k_cache,
                             const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
                             float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev) {
     if (num_waves <= 0) dec_wgs = 0;
-    if (dec_wgs * kDecodeWaves < num_waves) return hipErrorInvalidValue;
+    if (dec_wgs > 0 && (dec_wpg < 1 || dec_wpg > kDecodeWaves || dec_wgs * dec_wpg < num_waves))
+        return hipErrorInvalidValue;
     const int grid = dec_wgs + num_chunk_items;
     if (grid <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
@@ -78,12 +83,12 @@ hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, cons
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
         hipExtLaunchKernelGGL(mixed_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
-                              ev.stop, 0, p, dec_wgs, dec_items, wave_items, num_waves,
+                              ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
                               chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     else
         hipExtLaunchKernelGGL(mixed_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
-                              ev.stop, 0, p, dec_wgs, dec_items, wave_items, num_waves,
+                              ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
                               chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     return hipGetLastError();

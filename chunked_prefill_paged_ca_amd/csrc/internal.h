@@ -106,19 +106,20 @@ namespace ca {
 // workgroups followed by num_chunk_items chunk workgroups (attn_mixed.hip).
 //   decode: dec_items holds two int4 per item, {kv head, key begin, key end, partial slot or -1
 //     (the item covers the whole row: output written directly)}, {row, offset of the row's page
-//     ids in kv_page_indices, page count, 0}; decode wave w (of dec_wgs *
-//     attention_decode_waves_per_wg()) runs items [wave_items[w], wave_items[w + 1]) for
-//     w < num_waves.  Partials: dec_acc [slots][G][d] fp32, dec_ml [slots][G] (max in log2
-//     units, sum).
+//     ids in kv_page_indices, page count, 0}.  Decode workgroups run dec_wpg
+//     wavefronts each (1 .. attention_decode_waves_per_wg()), and decode wave w (of dec_wgs *
+//     dec_wpg) runs items [wave_items[w], wave_items[w + 1]) for w < num_waves.  Partials:
+//     dec_acc [slots][G][d] fp32, dec_ml [slots][G] (max in log2 units, sum).
 //   chunk: a query column is one (row, q head) pair of a kv head's group, numbered row * G +
 //     head.  chunk_items: two int4 per workgroup, {seq, kv head, first column, partial slot or
 //     -1}, {key begin, key end, 0, 0} (seq -1: padding).  Partials: chunk_acc
 //     [slot][chunk_cols_per_block()][d] fp32 and chunk_ml [slot][cols].
-hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, const int4* dec_items,
-                            const int32_t* wave_items, int num_waves, const int4* chunk_items,
+hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int dec_wpg,
+                            const int4* dec_items, const int32_t* wave_items, int num_waves,
+                            const int4* chunk_items,
                             int num_chunk_items, const void* q, const void* k_cache,
-                            const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
-                            float2* chunk_ml, void* o, float* lse, hipStream_t stream,
+                            const void* v_cache, float* dec_acc, float2* dec_ml,
+                            float* chunk_acc, float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev);
 int chunk_cols_per_block();
 int attention_decode_waves_per_wg();
