@@ -295,6 +295,7 @@ struct ca_ctx {
     bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
     ca::Linear* linear = nullptr;  // hipBLASLt state of ca_qkv_projection (created on first use)
+    bool projection_library = false;  // CA_PROJECTION_LIBRARY=1: the library GEMM for every T
 };
 
 namespace {
@@ -817,6 +818,7 @@ ca_status ca_create(int device, ca_ctx** out) {
         return device_error("hipDeviceGetAttribute(multiprocessor count)", e != hipSuccess ? e : hipErrorInvalidValue);
     }
     if (const char* env = std::getenv("CA_CHUNK_SPLIT")) ctx->csplit_override = std::atoi(env);
+    if (const char* env = std::getenv("CA_PROJECTION_LIBRARY")) ctx->projection_library = std::atoi(env) != 0;
     e = ctx->staging.init();
     if (e != hipSuccess) {
         ctx->staging.release();
@@ -951,6 +953,14 @@ ca_status ca_qkv_projection(ca_ctx* ctx, const ca_attn_desc* desc, int32_t num_t
     const int64_t N = static_cast<int64_t>(desc->num_q_heads + 2 * desc->num_kv_heads) * desc->head_dim;
     std::string err;
     Timed t(ctx->prof, "qkv_projection", CA_PROFILE_PROJECTION);
+    // few tokens: the weight-streaming kernel (bound by reading the weights once); otherwise,
+    // or with CA_PROJECTION_LIBRARY=1, the library GEMM
+    if (!ctx->projection_library && ca::skinny_projection_fits(num_tokens, hidden, N)) {
+        const hipError_t e = ca::launch_skinny_projection(num_tokens, hidden, N, x, w, qkv, stream, t.ev);
+        if (e != hipSuccess) return device_error("ca_qkv_projection", e);
+        t.commit();
+        return CA_OK;
+    }
     if (t.ev.start) (void)hipEventRecord(t.ev.start, stream);
     if (!ca::linear_bf16(ctx->linear, num_tokens, hidden, N, x, w, qkv, stream, &err)) {
         ca::set_error("ca_qkv_projection: " + err);

@@ -77,6 +77,13 @@ struct Linear;
 void linear_release(Linear* L);
 bool linear_bf16(Linear*& L, int64_t T, int64_t K, int64_t N, const void* x, const void* w,
                  void* out, hipStream_t stream, std::string* err);
+// The same product for few tokens (linear_skinny.hip): a kernel that streams the weights once
+// through the matrix cores.  It takes T in [1, kSkinnyMaxTokens], K a multiple of 2048 and N a
+// multiple of 32 (skinny_projection_fits); x [T][K], w [N][K], out [T][N], 16-byte aligned.
+constexpr int64_t kSkinnyMaxTokens = 16;
+bool skinny_projection_fits(int64_t T, int64_t K, int64_t N);
+hipError_t launch_skinny_projection(int64_t T, int64_t K, int64_t N, const void* x, const void* w,
+                                    void* out, hipStream_t stream, const LaunchEvents& ev);
 
 // q_row, kv_row: elements between consecutive token rows of q_in and of k_new / v_new.
 // row_pos, row_page: [num_tokens] per-row position and destination page (device memory or the

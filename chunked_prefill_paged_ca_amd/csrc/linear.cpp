@@ -4,7 +4,8 @@
 // in a mixed batch the linear layers of the decode tokens and of the prefill chunk run as one
 // matrix product, so every weight is read from memory once for all of them (attention stays
 // separate).  The product here is out[T][N] = x[T][K] . w[N][K]^T with bf16 operands and fp32
-// accumulation -- a plain library GEMM, done by hipBLASLt.  hipBLASLt is column-major: with the
+// accumulation -- a plain library GEMM, done by hipBLASLt (up to 16 tokens the weight-streaming
+// kernel of linear_skinny.hip runs instead).  hipBLASLt is column-major: with the
 // row-major arrays read as their transposes this is D(N x T) = op_T(w as K x N) . x(K x T), the
 // "TN" form.  Layouts and the chosen algorithm are cached per token count (the serving loop sees
 // a few distinct T again and again).  The first call for a token count times up to kCandidates

@@ -10,9 +10,11 @@ through ca_qkv_projection for T tokens.  Eight weight copies are used in turn (4
 the 256 MB last-level cache), so every call reads its weights from HBM as a real multi-layer
 step does.  Times are HIP events around each call (CA_PROFILE_PROJECTION), mean of 40 calls.
 
-Prints a markdown table: time, TFLOP/s, GB/s (algorithmic bytes: weights + x + out), the bound
-the roofline gives at that T (HBM at 8 TB/s or bf16 MFMA at 2.5 PFLOP/s) and the fraction of it
-reached, and the time per token.
+Prints a markdown table: the path the library takes at that T (the weight-streaming kernel for
+T <= 16, the hipBLASLt GEMM above), time, TFLOP/s, GB/s (algorithmic bytes: weights + x + out),
+the bound the roofline gives at that T (HBM at 8 TB/s or bf16 MFMA at 2.5 PFLOP/s) and the
+fraction of it reached, the time per token, and the hipBLASLt GEMM's time at the same T
+(a second context created with CA_PROJECTION_LIBRARY=1).
 """
 from __future__ import annotations
 
@@ -37,30 +39,42 @@ def main(argv):
     x = torch.randn((max(Ts), hidden), device="cuda").to(torch.bfloat16)
     out = torch.empty((max(Ts), N), dtype=torch.bfloat16, device="cuda")
     desc = ca.make_desc(Hq, Hkv, d, 16, "bf16")
+    import os
     ctx = ca.create(0)
-    rows = ["| T | us per call | TFLOP/s | GB/s | roofline bound | fraction of bound | us per token |",
-            "|---|---|---|---|---|---|---|"]
-    for T in Ts:
+    os.environ["CA_PROJECTION_LIBRARY"] = "1"
+    ctx_lib = ca.create(0)
+    del os.environ["CA_PROJECTION_LIBRARY"]
+
+    def time_calls(c, T):
         for i in range(2 * copies):  # plan this T and warm the library
-            ctx.qkv_projection(desc, T, hidden, x, ws[i % copies], out)
+            c.qkv_projection(desc, T, hidden, x, ws[i % copies], out)
         torch.cuda.synchronize()
-        ctx.profile_read()
-        ctx.profile_enable(ca.PROFILE_PROJECTION)
+        c.profile_read()
+        c.profile_enable(ca.PROFILE_PROJECTION)
         reps = 40
         for i in range(reps):
-            ctx.qkv_projection(desc, T, hidden, x, ws[i % copies], out)
+            c.qkv_projection(desc, T, hidden, x, ws[i % copies], out)
         torch.cuda.synchronize()
-        ctx.profile_enable(False)
-        us = float(np.mean([ms for _, ms in ctx.profile_read()])) * 1e3
+        c.profile_enable(False)
+        return float(np.mean([ms for _, ms in c.profile_read()])) * 1e3
+
+    rows = ["| T | path | us per call | TFLOP/s | GB/s | roofline bound | fraction of bound | us per token "
+            "| hipBLASLt us |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for T in Ts:
+        us = time_calls(ctx, T)
+        us_lib = time_calls(ctx_lib, T)
+        path = "streaming kernel" if T <= 16 and hidden % 2048 == 0 and N % 32 == 0 else "hipBLASLt"
         flops = 2.0 * T * hidden * N
         nbytes = 2.0 * (N * hidden + T * hidden + T * N)
         t_hbm, t_mfma = nbytes / HBM, flops / MFMA
         bound = "HBM" if t_hbm >= t_mfma else "MFMA"
         frac = max(t_hbm, t_mfma) / (us * 1e-6)
-        rows.append(f"| {T} | {us:.1f} | {flops / us / 1e6:.0f} | {nbytes / us / 1e3:.0f} | {bound} | "
-                    f"{frac:.2f} | {us / T:.3f} |")
+        rows.append(f"| {T} | {path} | {us:.1f} | {flops / us / 1e6:.0f} | {nbytes / us / 1e3:.0f} | "
+                    f"{bound} | {frac:.2f} | {us / T:.3f} | {us_lib:.1f} |")
         print(rows[-1], file=sys.stderr, flush=True)
     ctx.close()
+    ctx_lib.close()
     print(f"# QKV projection, Mistral-7B shapes (4096 -> 6144, bf16), weights read from HBM\n\n"
           f"Command (repository root, one MI355X): `python3 -m chunked_prefill_paged_ca_amd.linear_bench`\n")
     print("\n".join(rows))

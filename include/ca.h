@@ -177,15 +177,16 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
 /*
  * Kernel timing (the tracing layer).  When enabled, every launch the library makes carries a
  * start/stop HIP event pair attached to the dispatch itself (hipExtLaunchKernel), so the
- * figures are device time of that launch alone and timing adds no packet to the stream.  ca_profile_read waits for the recorded events, copies up to `cap` records
- * (oldest first), sets *count to the number copied and forgets every record read or not.
+ * figures are device time of that launch alone and timing adds no packet to the stream.
+ * ca_profile_read waits for the recorded events, copies up to `cap` records (oldest first),
+ * sets *count to the number copied and forgets every record read or not.
  * Names are static strings: "upload" (the step's metadata, host staging -> device, when an
  * attention call is the first to see a plan; after ca_append_kv_rope the append launch has
  * copied it, inside "append_rope"), "append_rope",
  * "attention" (decode and prefill-chunk rows in one launch; with CA_SPLIT_ATTENTION=1 in the
  * environment at ca_create they are two launches named "chunk" and "decode"), "merge" (both
- * kinds of split merge in one launch) and "generic" (the plain fp32 kernel with its merge).  At most 65536 launches are kept between reads; later ones are
- * not recorded.
+ * kinds of split merge in one launch) and "generic" (the plain fp32 kernel with its merge).
+ * At most 65536 launches are kept between reads; later ones are not recorded.
  */
 typedef struct {
     const char* kernel;
@@ -216,7 +217,10 @@ ca_status ca_profile_read(ca_ctx* ctx, ca_profile_record* out, int32_t cap, int3
  *   qkv[T][Hq + 2 Hkv][d] = x[T][hidden] . w^T, where w is [(Hq + 2 Hkv) d][hidden] (one row per
  *   output feature, rows ordered q heads, then k heads, then v heads) and T = num_tokens (the
  *   plan's row order: decode rows, then chunk rows).  bf16 operands and result, fp32
- *   accumulation; a library GEMM (hipBLASLt), planned once per token count and cached in ctx.
+ *   accumulation.  Up to 16 tokens (hidden a multiple of 2048) a kernel of this library streams
+ *   the weights once through the matrix cores; otherwise, or with CA_PROJECTION_LIBRARY=1 in the
+ *   environment at ca_create, a library GEMM (hipBLASLt), planned once per token count and cached
+ *   in ctx.
  * Device buffers x, w, qkv (16-byte aligned).  Errors: CA_ERR_INVALID_ARG (null pointer, sizes,
  * hidden not a multiple of 8), CA_ERR_UNSUPPORTED (dtype not bf16), CA_ERR_DEVICE (a hipBLASLt or
  * HIP error).

@@ -205,10 +205,11 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
-@pytest.mark.parametrize("T", [1, 80, 512, 523])
+@pytest.mark.parametrize("T", [1, 7, 16, 17, 80, 512, 523])
 def test_qkv_projection_matches_oracle(env, T):
     """The Mistral-7B q/k/v projection (hidden 4096 -> (32 + 2 x 8) x 128 features) over T
-    tokens against the exact product rounded once.  The GPU sums K = 4096 exact bf16 products in
+    tokens against the exact product rounded once.  T <= 16 runs the weight-streaming kernel
+    (7: a ragged token tile), larger T the library GEMM.  The GPU sums K = 4096 exact bf16 products in
     fp32, whose error is at most K 2^-24 sum_k |x_k w_k| (the standard bound for a K-term
     floating-point sum); the bar is that bound plus one bf16 unit in the last place of the exact
     value.  Away from cancellation this means "equal or the neighbouring bf16 value"; an output
