@@ -205,11 +205,13 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
-@pytest.mark.parametrize("T", [1, 7, 16, 17, 80, 512, 523])
-def test_qkv_projection_matches_oracle(env, T):
+@pytest.mark.parametrize("T,library", [(1, False), (7, False), (16, False), (17, False), (80, False),
+                                       (512, False), (523, False), (1, True)])
+def test_qkv_projection_matches_oracle(env, T, library):
     """The Mistral-7B q/k/v projection (hidden 4096 -> (32 + 2 x 8) x 128 features) over T
     tokens against the exact product rounded once.  T <= 16 runs the weight-streaming kernel
-    (7: a ragged token tile), larger T the library GEMM.  The GPU sums K = 4096 exact bf16 products in
+    (7: a ragged token tile), larger T -- and T = 1 in a context created with
+    CA_PROJECTION_LIBRARY=1 -- the library GEMM.  The GPU sums K = 4096 exact bf16 products in
     fp32, whose error is at most K 2^-24 sum_k |x_k w_k| (the standard bound for a K-term
     floating-point sum); the bar is that bound plus one bf16 unit in the last place of the exact
     value.  Away from cancellation this means "equal or the neighbouring bf16 value"; an output
@@ -224,8 +226,19 @@ def test_qkv_projection_matches_oracle(env, T):
     x, w = projection_inputs(T, hidden, N, seed=11 + T)
     desc = ca.make_desc(Hq, Hkv, d, 16, "bf16")
     out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-    ctx.qkv_projection(desc, T, hidden, H.to_device(x, "bf16"), H.to_device(w, "bf16"), out)
+    if library:
+        import os
+        os.environ["CA_PROJECTION_LIBRARY"] = "1"
+        try:
+            pctx = ca.create(0)
+        finally:
+            del os.environ["CA_PROJECTION_LIBRARY"]
+    else:
+        pctx = ctx
+    pctx.qkv_projection(desc, T, hidden, H.to_device(x, "bf16"), H.to_device(w, "bf16"), out)
     torch.cuda.synchronize()
+    if library:
+        pctx.close()
     got = out.float().cpu().numpy().astype(np.float64)
     ref = oracle.linear(x, w, "bf16")
     u = H.ulp_distance(got, ref, "bf16")
@@ -335,18 +348,19 @@ def test_serving_loop_matches_oracle(env):
     assert added == sc.n and preempted > 0 and states.count(ca.CA_REQ_FINISHED) >= sc.n - 2
 
 
-@pytest.mark.parametrize("mode", ["split", "few-decode-wgs", "decode-only"])
+@pytest.mark.parametrize("mode", ["split", "few-decode-wgs", "eight-decode-waves", "decode-only"])
 def test_attention_launch_layouts(env, mode):
     """The Mistral-7B step through the other layouts of the attention launch: decode and chunk
     rows as two launches (CA_SPLIT_ATTENTION=1), a mixed launch with only 8 decode workgroups (so
-    every decode wave runs many items, crossing many (row, kv head) boundaries), and a step with
-    decodes only (no chunk workgroups at all)."""
+    every decode wave runs many items, crossing many (row, kv head) boundaries), 8 decode waves
+    per workgroup instead of 4 (CA_DECODE_WAVES=8), and a step with decodes only (no chunk
+    workgroups at all)."""
     import os
     import chunked_prefill_paged_ca_amd as ca
     from chunked_prefill_paged_ca_amd.workload import Workload, make_config
     _, oracle = env
     setting = {"split": ("CA_SPLIT_ATTENTION", "1"), "few-decode-wgs": ("CA_DECODE_WGS", "8"),
-               "decode-only": None}[mode]
+               "eight-decode-waves": ("CA_DECODE_WAVES", "8"), "decode-only": None}[mode]
     if setting:
         os.environ[setting[0]] = setting[1]
     try:
