@@ -7,8 +7,12 @@
         -> JSON: FETCH_SIZE / WRITE_SIZE per attention launch, scaled by what the same counters
            read for a device-to-device copy of known size, on stdout; <workload> is the name of
            the workload the counters were taken on (a reading holds for that workload only)
+    python -m chunked_prefill_paged_ca_amd.profiling parts <SQ counter_collection.csv>
+           <fetch counter_collection.csv> <write counter_collection.csv> <parts_run output> <command>
+        -> markdown: MFMA utilisation, executed bf16 MFMA flops and HBM bytes of the decode-only
+           and chunk-only attention launches of parts_run.py, on stdout
 
-Neither touches the GPU; they read the CSV files rocprofv3 wrote.
+None touches the GPU; they read the CSV files rocprofv3 wrote.
 """
 from __future__ import annotations
 
@@ -18,6 +22,8 @@ import json
 import os
 import sys
 from collections import defaultdict
+
+import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ATTENTION_SOURCES = ("attn_mixed.hip", "attn_decode.h", "attn_chunk.h", "mfma.h", "internal.h")
@@ -82,8 +88,84 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, cmd: str, workload: s
     return res
 
 
+def _instances(path: str):
+    """{dispatch id: (kernel name, {counter: [values of its instances]})}."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        name, vals = out.setdefault(d, (r["Kernel_Name"], defaultdict(list)))
+        vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def parts(sq_csv: str, fetch_csv: str, write_csv: str, timing: dict, cmd: str) -> str:
+    """Counters of the decode-only and chunk-only attention launches of parts_run.py.
+
+    The attention dispatches alternate in launch order (timing["attention_launch_order"]).
+    rocprofv3 writes each counter summed over its instances (SIMDs, shader engines, XCDs), so
+    GRBM_GUI_ACTIVE / 8 is one XCD's active cycles and MFMA utilisation -- rocprofv3's MfmaUtil --
+    is SQ_VALU_MFMA_BUSY_CYCLES / SIMDs over that; executed bf16 MFMA flops are SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; HBM bytes are
+    FETCH_SIZE and WRITE_SIZE scaled by what the same counters read for the reference copy
+    (timing["copy_mib"] MiB read and written)."""
+    order = timing["attention_launch_order"]
+    copy_bytes = timing["copy_mib"] * (1 << 20)
+
+    def attention(per):
+        ids = sorted(d for d, (n, _) in per.items() if "mixed_kernel" in n)
+        return {kind: [per[d][1] for i, d in enumerate(ids) if order[i % len(order)] == kind] for kind in order}
+
+    def scaled(path, counter):
+        per = _instances(path)
+        copies = [sum(v[counter]) for n, v in per.values() if "copy" in n.lower() and counter in v]
+        if not copies:
+            raise SystemExit(f"{path}: no reference copy with {counter}")
+        factor = max(copies) * 1024.0 / copy_bytes
+        return {k: float(np.mean([sum(v[counter]) for v in vs])) * 1024.0 / factor
+                for k, vs in attention(per).items()}, factor
+
+    sq = attention(_instances(sq_csv))
+    fetch, ff = scaled(fetch_csv, "FETCH_SIZE")
+    write, wf = scaled(write_csv, "WRITE_SIZE")
+    ms = timing["kernel_ms"]
+    rows = []
+    for kind in order:
+        vs = sq[kind]
+        util = float(np.mean([sum(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / SIMDS / (sum(v["GRBM_GUI_ACTIVE"]) / XCDS)
+                              for v in vs]))
+        mops = float(np.mean([sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) for v in vs])) * 512
+        t = ms[kind] * 1e-3
+        rows.append((kind, ms[kind] * 1e3, util, mops, mops / t / 1e12, fetch[kind], write[kind],
+                     (fetch[kind] + write[kind]) / t / 1e9, len(vs)))
+    out = [f"# Decode-only and chunk-only attention launches: {timing['workload']}", "",
+           "Command (run from the repository root on one MI355X; TMPDIR=/tmp):", "", f"    {cmd}", "",
+           f"Event time per launch from parts_run ({timing['steps']} timed steps); counters averaged "
+           f"over every launch of each kind ({rows[0][-1]} each).  FETCH_SIZE reads {ff:.3g} and "
+           f"WRITE_SIZE {wf:.3g} counter KiB per real KiB on the reference copy; bytes below are "
+           "scaled by those factors.", "",
+           "| launch | event us | MFMA busy (MfmaUtil) | executed bf16 MFMA flops | executed TF/s | HBM read MB | "
+           "HBM written MB | HBM GB/s |", "|---|---|---|---|---|---|---|---|"]
+    for kind, us, util, mops, tf, rd, wr, gbs, _ in rows:
+        out.append(f"| {kind} | {us:.1f} | {100 * util:.1f} % | {mops / 1e9:.1f} G | {tf:.0f} | "
+                   f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {gbs:.0f} |")
+    ca = timing["chunk_alg_flops"]
+    out += ["", f"Algorithmic work: decode rows {timing['decode_alg_bytes'] / 1e6:.1f} MB "
+            f"({timing['decode_alg_bytes'] / (ms['decode'] * 1e-3) / 1e9:.0f} GB/s over the decode launch, "
+            f"{timing['decode_alg_bytes'] / (ms['decode'] * 1e-3) / 8e12 * 100:.1f} % of 8 TB/s); chunk rows "
+            f"{ca / 1e9:.1f} GFLOP ({ca / (ms['chunk'] * 1e-3) / 1e12:.0f} TF/s over the chunk launch, "
+            f"{ca / (ms['chunk'] * 1e-3) / 2.5e15 * 100:.1f} % of 2.5 PFLOP/s) and "
+            f"{timing['chunk_alg_bytes'] / 1e6:.1f} MB of unique K/V and q."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
-    if len(argv) >= 4 and argv[0] == "stats":
+    if len(argv) >= 6 and argv[0] == "parts":
+        timing = json.loads(open(argv[4]).read().strip().splitlines()[-1])
+        sys.stdout.write(parts(argv[1], argv[2], argv[3], timing, argv[5]))
+    elif len(argv) >= 4 and argv[0] == "stats":
         sys.stdout.write(stats_md(argv[1], argv[2], argv[3]))
     elif len(argv) >= 6 and argv[0] == "traffic":
         print(json.dumps(traffic(argv[1], argv[2], int(argv[3]), argv[4], argv[5]), indent=1))
