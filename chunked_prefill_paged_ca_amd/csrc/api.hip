@@ -473,6 +473,8 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
         return L < ca::chunk_max_split_keys() ? L : ca::chunk_max_split_keys() / 32 * 32;
     }
     int64_t work = 0;  // sum over column blocks of visible keys (x kv heads)
+    int64_t blocks = 0;  // column blocks (x kv heads): the chunk workgroups if no row block is split
+    int32_t widest = 0;  // most keys one column block sees
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
         const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
         const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
@@ -480,8 +482,28 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
         const int32_t ncols = q_len * G;
         for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
             const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
-            work += static_cast<int64_t>(kv_len - q_len + last / G + 1) * sh.hkv;
+            const int32_t keys = kv_len - q_len + last / G + 1;
+            work += static_cast<int64_t>(keys) * sh.hkv;
+            blocks += sh.hkv;
+            if (keys > widest) widest = keys;
         }
+    }
+    // When the chunk rows have the device to themselves (no decode rows in the launch), unsplit
+    // row blocks that already fill most of it in one round, with key ranges of about the same
+    // length, stay whole: splitting them only adds partials, a longer merge and each extra
+    // workgroup's pipeline fill.  Measured on the part (Yi-34B chunk alone: 212 blocks of ~16 K
+    // keys on 256 CUs): whole blocks 424-470 us with a 5 us merge, against 461-495 us with a
+    // 31 us merge when cut into ~1 K workgroups.  Beside decode rows the chunk workgroups start
+    // on a quarter of the CUs and take over the rest as the decode drains, and there the smaller
+    // pieces rebalance onto the freed CUs: same fused time within the box-to-box spread.
+    const bool beside_decode = plan->num_decodes > 0 && !ctx->split_attention;
+    if (!beside_decode) {
+        const int32_t known = ctx->attn_wgs_per_cu[sh.d == 128 ? 1 : 0];
+        const int64_t slots = static_cast<int64_t>(ctx->num_cus) * (known > 0 ? known : 1);
+        const int64_t cap = ca::chunk_max_split_keys() / 32 * 32;
+        const bool one_round = blocks > 0 && 4 * blocks >= 3 * slots && blocks <= slots;
+        const bool even = 4 * static_cast<int64_t>(widest) * blocks <= 5 * work;  // widest <= 1.25 x mean
+        if (one_round && even && widest <= cap) return ((widest + 31) / 32) * 32;
     }
     const int64_t target = 1024;  // workgroups (one per CU at a time; several rounds)
     int64_t L = (work + target - 1) / target;

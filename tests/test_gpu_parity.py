@@ -168,6 +168,25 @@ def test_yi_share_sampled(env):
     run_and_check(ctx, oracle, wl, rows_per_seq=48, track=dec + [128], label="yi-share")
 
 
+def test_yi_chunk_alone_whole_blocks(env):
+    """The Yi-34B share's 1920-row chunk on 14336 cached keys with no decode rows beside it: its
+    53 x 4 column blocks fill the device in one round with key ranges within 25 % of each other,
+    so each block runs its whole key range in one workgroup (no split, no merge); sampled rows
+    against the oracle."""
+    from chunked_prefill_paged_ca_amd.workload import Workload, make_config
+    ctx, oracle = env
+    wl = make_config(4)
+    keep = [r for r in range(wl.n) if not wl.is_decode(r)]
+    uids = np.arange(wl.n) if wl.uids is None else wl.uids
+    wl = Workload(**{**wl.__dict__, "num_computed": wl.num_computed[keep],
+                     "num_prompt_left": wl.num_prompt_left[keep],
+                     "block_tables": [wl.block_tables[r] for r in keep],
+                     "stream_len": wl.stream_len[keep], "uids": uids[keep]})
+    res, _, _ = run_and_check(ctx, oracle, wl, rows_per_seq=64, label="yi-chunk-alone")
+    p = res[0][0]
+    assert p["num_decodes"] == 0 and p["num_tokens"] == 1920
+
+
 def test_llama70b_share_sampled(env):
     """Config 5 at full size on a fragmented 128K-page pool: 256 decodes + 3 chunks, sampled
     requests (the rest of the pool holds device-drawn random values)."""
