@@ -417,16 +417,57 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
     return CA_OK;
 }
 
-// Share of the CUs the decode rows get when they share the attention launch with chunk rows.
-// Measured on the 256-CU part (Mistral-7B, Yi-34B and LLaMA2-70B mixed steps): decode keeps its
-// HBM rate on 3/4 of the CUs; fewer starve it, more starve the chunk work.
-constexpr double kMixedDecodeShare = 0.75;
+// Share of the CUs the decode rows get when they share the attention launch with chunk rows:
+// each part in proportion to the CU-time it needs -- the decode stream the whole device for
+// dec_us (its K/V bytes at kDecodeStreamBps), the chunk rows kChunkBlockUs per 32-key block of a
+// column block -- within [kMinDecodeShare, kMaxDecodeShare].  Measured on the part (4 decode waves
+// per workgroup, sweeps of the decode workgroups on several boxes): the Mistral-7B step is
+// fastest at 3/4 of the CUs and the LLaMA2-70B step at 5/8-3/4 (both decode-heavy: the proportion
+// is ~0.8 and clamps to 3/4), the chunk-heavy Yi-34B step at 5/16-3/8 (proportion ~0.26), where it
+// ran 580-588 us against 595-642 us at 3/4 and fell off a cliff below 5/16 (the decode stream
+// becomes the tail).
+constexpr double kMaxDecodeShare = 0.75;
+constexpr double kMinDecodeShare = 0.3125;
+constexpr double kDecodeStreamBps = 5.5e12;  // decode K/V read rate the estimates assume
+double chunk_block_us(const Shape& sh) { return sh.d == 128 ? 1.3 : 0.67; }
+
+// Decode K/V stream time (us) and chunk CU-time (CU-us) of a plan, as the launch-shaping rules
+// estimate them.
+void mixed_work(const ca_plan* plan, const Shape& sh, double* dec_us, double* chunk_cu_us) {
+    const int32_t G = sh.hq / sh.hkv;
+    const int32_t cols = ca::chunk_cols_per_block();
+    int64_t dec_keys = 0, chunk_keys = 0;
+    for (int32_t s = 0; s < plan->num_seqs; ++s) {
+        const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+        const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+        if (s < plan->num_decodes) {
+            dec_keys += kv_len;
+            continue;
+        }
+        const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+        for (int32_t cb = 0; cb < q_len * G; cb += cols) {
+            const int32_t last = (cb + cols < q_len * G ? cb + cols : q_len * G) - 1;
+            chunk_keys += kv_len - q_len + last / G + 1;
+        }
+    }
+    *dec_us = static_cast<double>(dec_keys) * sh.hkv * sh.d * 4 / kDecodeStreamBps * 1e6;  // K + V, bf16
+    *chunk_cu_us = static_cast<double>(chunk_keys) * sh.hkv / 32 * chunk_block_us(sh);
+}
+
+double mixed_decode_share(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh) {
+    double dec_us = 0, chunk_cu_us = 0;
+    mixed_work(plan, sh, &dec_us, &chunk_cu_us);
+    const double dec_cu_us = dec_us * ctx->num_cus;
+    if (dec_cu_us <= 0) return kMaxDecodeShare;
+    const double f = dec_cu_us / (dec_cu_us + chunk_cu_us);
+    return f < kMinDecodeShare ? kMinDecodeShare : (f > kMaxDecodeShare ? kMaxDecodeShare : f);
+}
 
 // Decode workgroups of the attention launch and decode shares.  The 32-key blocks of every
 // (decode row, kv head), laid end to end, are cut into one equal share per decode wavefront, so a
 // single round of waves streams the whole decode K/V with no tail.  Alone (no chunk rows, or the
 // two parts launched separately) decode takes every workgroup slot of the device; in a mixed
-// launch it takes kMixedDecodeShare of them (rounded to whole XCD rounds of 8) and the chunk
+// launch it takes mixed_decode_share of them (rounded to whole XCD rounds of 8) and the chunk
 // workgroups run beside it.  CA_DECODE_WGS sets the count of a mixed launch instead.  Returns
 // the share count; *wgs gets the decode workgroups.
 int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t* wgs) {
@@ -443,7 +484,8 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t
     const bool mixed = plan->num_seqs > plan->num_decodes && !ctx->split_attention;
     int32_t n = slots;
     if (mixed) {
-        n = ctx->dec_wgs_override > 0 ? ctx->dec_wgs_override : static_cast<int32_t>(slots * kMixedDecodeShare);
+        n = ctx->dec_wgs_override > 0 ? ctx->dec_wgs_override
+                                      : static_cast<int32_t>(slots * mixed_decode_share(ctx, plan, sh));
         n = (n + 7) / 8 * 8;
         if (n > slots) n = slots;
     }
@@ -512,26 +554,20 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
     // workgroups run beside them on the CUs the decode rows leave free.  If all the chunk work
     // fits there within that time, splitting a row block only adds its partials' round trip
     // through HBM and the merge: keep each block whole, as long as its workgroup still ends well
-    // inside the decode time.  Measured on the part: one 32-key block of a 256-column workgroup
-    // takes ~1.3 us at d = 128, and the decode rows stream ~5.5 TB/s.
+    // inside the decode time.  (The estimates are mixed_work's.)
     const bool fused = plan->num_decodes > 0 && plan->num_seqs > plan->num_decodes && !ctx->split_attention;
     if (fused) {
-        int64_t dec_keys = 0;
-        for (int32_t s = 0; s < plan->num_decodes; ++s) {
-            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
-            dec_keys += (np - 1) * plan->page_size + plan->kv_last_page_len[s];
-        }
-        const double dec_us = static_cast<double>(dec_keys) * sh.hkv * sh.d * 4 / 5.5e6;  // K + V bf16
-        const double block_us = sh.d == 128 ? 1.3 : 0.67;
-        const double chunk_cus = ctx->num_cus * (1.0 - kMixedDecodeShare);
-        if (static_cast<double>(work) / 32 * block_us <= 0.75 * chunk_cus * dec_us) {
+        double dec_us = 0, chunk_cu_us = 0;
+        mixed_work(plan, sh, &dec_us, &chunk_cu_us);
+        const double chunk_cus = ctx->num_cus * (1.0 - mixed_decode_share(ctx, plan, sh));
+        if (chunk_cu_us <= 0.75 * chunk_cus * dec_us) {
             int32_t longest = 0;
             for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
                 const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
                 const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
                 if (kv_len > longest) longest = kv_len;
             }
-            const int64_t whole = static_cast<int64_t>(0.9 * dec_us / block_us) * 32;
+            const int64_t whole = static_cast<int64_t>(0.9 * dec_us / chunk_block_us(sh)) * 32;
             const int64_t keep = longest < whole ? longest : whole;
             if (keep > L) L = keep;
         }
