@@ -5,7 +5,7 @@
 // and acc_s (sum of 2^(score - m_s) v).  With M = max_s m_s over splits that saw a key,
 //   o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,   lse = (M + log2 sum_s 2^(m_s - M) l_s) ln 2,
 // which is the softmax over the union of the splits' keys.  (Not a step of the pages: it is how
-// this build parallelises one row over many keys; see the causal attention of
+// the library parallelises one row over many keys; see the causal attention of
 // pinghaoyang.com.cn "Sarathi-Serve 完全拆解", section "分块不等于截断上下文", for what is merged.)
 //
 // Sixteen lanes per output column (row, q head), four columns per wavefront; a lane owns d / 16

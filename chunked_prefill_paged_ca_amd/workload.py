@@ -151,13 +151,22 @@ def _log_uniform_int(rng, lo: int, hi: int, size: int) -> np.ndarray:
 def make_config(config: int, seed: Optional[int] = None, *, chunk: int = 512,
                 one_shot: bool = False, peaky: bool = False, kv_value: Optional[float] = None,
                 dtype: Optional[str] = None) -> Workload:
-    """Build configuration `config` (1..5) with a fixed seed (default: the config number).
+    """Build one of the five workloads with a fixed seed (default: its number):
+      1  tiny fp32 batch: 2/2/64, a 64-token prompt in chunks of 16 beside 3 decodes;
+      2  Mistral-7B layer: 32/8/128 bf16, budget 512, 80 decodes + prefills P (300 on 1200) and
+         Q (132 of 900 on 2048);
+      3  Llama-13B prompt of 8192 tokens, MHA 40/40/128 bf16, in chunks of c;
+      4  Yi-34B one-GPU share: 28/4/128 bf16, budget 2048, 128 decodes + a 1920-token chunk on
+         14336 cached;
+      5  LLaMA2-70B one-GPU share: 64/8/128 bf16, budget 1536, 256 decodes + chunks 640@0,
+         512@6000, 128@30000 on a fragmented pool.
 
-    chunk     -- config 3 only: the chunk size c (token budget = c, K = ceil(8192 / c) steps).
-    one_shot  -- config 1 only: the whole 64-token prompt in one step, no decodes.
+    chunk     -- the Llama-13B prompt only: the chunk size c (token budget = c, K = ceil(8192 / c)
+                 steps).
+    one_shot  -- the tiny batch only: the whole 64-token prompt in one step, no decodes.
     peaky     -- multiply q by 4 (seed + 100 unless a seed is given).
     kv_value  -- make every V entry this constant.
-    dtype     -- override the storage type (e.g. run config 1 in bf16).
+    dtype     -- override the storage type (e.g. run the tiny batch in bf16).
     """
     if seed is None:
         seed = config + (100 if peaky else 0)
