@@ -547,16 +547,23 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
         const bool even = 4 * static_cast<int64_t>(widest) * blocks <= 5 * work;  // widest <= 1.25 x mean
         if (one_round && even && widest <= cap) return ((widest + 31) / 32) * 32;
     }
-    // Otherwise aim at ~1 K workgroups (one per CU at a time, several rounds), but with at least
-    // kMinSplitKeys keys each: a shorter split spends too much of its time filling the stage
-    // pipeline and writing its 128 KB of partials.  Measured on the part (Llama-13B 8192-token
-    // prompt, whole prompt at chunk size c): a floor of 1280 keys against 512 took c = 128 / 256 /
-    // 512 / 1024 from 2848 / 1878 / 1418 / 1092 us to 2580 / 1628 / 1213 / 1023 us; 2048 was
-    // slower again for small c.
+    // Otherwise aim at ~1 K workgroups (one per CU at a time, several rounds), each with at least
+    // kMinSplitKeys keys as long as that still leaves one workgroup per CU (512 at least): a
+    // shorter split spends too much of its time filling the stage pipeline and writing its 128 KB
+    // of partials, while too few workgroups leave CUs idle.  Measured on the part (Llama-13B
+    // 8192-token prompt, whole prompt at chunk size c): the 1280-key floor against 512 took c =
+    // 128 / 256 / 512 / 1024 from 2848 / 1878 / 1418 / 1092 us to 2580 / 1628 / 1213 / 1023 us
+    // (2048 was slower again for small c); applied without the one-per-CU bound it made the
+    // Mistral-7B chunks launched alone (64 row blocks of ~1.8 K keys) 27 -> 45 us.
     constexpr int64_t kMinSplitKeys = 1280;
     const int64_t target = 1024;
+    const int32_t known_cu = ctx->attn_wgs_per_cu[sh.d == 128 ? 1 : 0];
+    const int64_t wg_slots = static_cast<int64_t>(ctx->num_cus) * (known_cu > 0 ? known_cu : 1);
+    const int64_t per_slot = (work + wg_slots - 1) / wg_slots;
     int64_t L = (work + target - 1) / target;
-    if (L < kMinSplitKeys) L = kMinSplitKeys;
+    const int64_t floor_keys = per_slot < kMinSplitKeys ? per_slot : kMinSplitKeys;
+    if (L < floor_keys) L = floor_keys;
+    if (L < 512) L = 512;
     // When decode rows share the launch they set its length (their K/V stream), and the chunk
     // workgroups run beside them on the CUs the decode rows leave free.  If all the chunk work
     // fits there within that time, splitting a row block only adds its partials' round trip
