@@ -115,7 +115,18 @@ typedef struct {
 
 typedef struct ca_ctx ca_ctx;
 
-/* Create a context bound to HIP device `device`.  *out receives the handle. */
+/*
+ * Create a context bound to HIP device `device`.  *out receives the handle.
+ * The launch shape is chosen per call from the plan and the device's CU count.  For measurement,
+ * ca_create reads these overrides from the environment (unset = the default choice):
+ *   CA_DECODE_WGS=n         decode workgroups of the fused attention launch;
+ *   CA_DECODE_WAVES=n       waves per decode workgroup, 1..8 (default 4);
+ *   CA_CHUNK_SPLIT=n        keys per prefill-chunk split (rounded up to 32 and to at least
+ *                           1/64 of the longest chunk row's keys);
+ *   CA_SPLIT_ATTENTION=1    decode and prefill-chunk rows as two launches instead of one;
+ *   CA_PROJECTION_LIBRARY=1 ca_qkv_projection always through hipBLASLt.
+ * Errors: CA_ERR_INVALID_ARG (null out, no such device), CA_ERR_DEVICE (a HIP error).
+ */
 ca_status ca_create(int device, ca_ctx** out);
 /* Free the context's workspace (waits for nothing: the caller must have synchronised the
  * streams it used with this context). */
