@@ -10,19 +10,28 @@ Prints ONE JSON line.  `value` is tokens per second of whole steps over the time
 `roofline` places the dominant kernel -- the attention launch, which runs the decode rows and
 the prefill-chunk rows side by side -- against the peak of the resource its algorithmic work
 needs longest: reading the K/V pages at 8 TB/s HBM (the default workload and every
-decode-heavy one), or the chunk rows' flops at 2.5 PFLOP/s bf16 MFMA (long prefill chunks),
-using the launch's own duration (HIP events attached to that launch on the bench's stream, on
-every tenth step of the timed region by default: each timed launch adds ~2 us to its step).
+decode-heavy one), or the chunk rows' flops at 2.5 PFLOP/s bf16 MFMA (long prefill chunks).
+Its duration comes from HIP events attached to that launch itself on the bench's stream: every
+attention launch of the timed region carries them, and when the timed region has fewer than 50
+steps the same stream of steps continues, still timed, until 50 launches have been timed
+(mean and p10/p50/p90 over all of them).  `scrubbed` repeats 50 steps with a 512 MiB write
+before each (outside the events), so L2 and the MALL hold none of the step's data: cold-HBM
+launch times.
 `traffic` is the HBM bytes the counters measured for that launch (profiles/), used only for the
-workload they were taken on and while the kernel sources are unchanged.
+workload they were taken on and while the sources that shape the launch are unchanged.
 `parts` times the decode and chunk work as two separate launches in a second, untimed pass, for
-their own HBM and bf16 MFMA fractions.  `measured_peaks` re-measures, after the timed region,
-what this device sustains (a 4 GiB read stream, a 1 GiB copy, an 8192^3 bf16 GEMM on random data) and
-places the roofline launch against the matching one.  `cpu_baseline` times the CPU oracle on the same step.
+their own HBM and bf16 MFMA fractions.  `per_config` runs the other workloads the same way
+(Yi-34B and LLaMA2-70B one-GPU shares: whole steps; the Llama-13B 8192-token prompt: summed
+kernel time over all of its chunks at each chunk size, against the one-shot prompt).
+`measured_peaks` re-measures, after the timed region, what this device sustains (a 4 GiB read
+stream, a 1 GiB copy, an 8192^3 bf16 GEMM on random data) and places the roofline launch against
+the matching one.  `cpu_baseline` times the CPU oracle on the same step (all host threads, and
+one thread).
 """
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -34,6 +43,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_mistral7b_mixed_step.json")
+MIN_TIMED_LAUNCHES = 50
+SCRUB_MIB = 512
 
 
 def log(msg):
@@ -42,7 +53,7 @@ def log(msg):
 
 def stored_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, or None: the reading
-    counts only for the workload it was taken on and while the kernel sources are unchanged."""
+    counts only for the workload it was taken on and while the sources are unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -54,8 +65,20 @@ def stored_traffic(workload):
     return int(t["hbm_bytes_per_launch"])
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wl, min_seconds=10.0):
-    """The oracle as it stands on the whole step (every row), repeated for at least min_seconds."""
+    """The oracle as it stands on the whole step (every row): on every host thread, repeated for
+    at least min_seconds, and once on one thread."""
     import oracle
     from chunked_prefill_paged_ca_amd.workload import StreamCursor
     sess = oracle.Session(wl)
@@ -71,10 +94,255 @@ def cpu_baseline(wl, min_seconds=10.0):
         fresh.step(p, q, k, v, nthreads=threads)
         times.append(time.perf_counter() - t0)
     dt = float(np.mean(times))
+    fresh = sess.fork()
+    t0 = time.perf_counter()
+    fresh.step(p, q, k, v, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread": {"value": round(T / dt1, 2), "unit": "tokens/s", "seconds_per_step": round(dt1, 3)},
             "sample": f"the whole step: all {T} rows ({nd} decode rows + 2 prefill chunks), "
                       f"fp64 C oracle on {threads} threads, mean of {len(times)} runs "
-                      f"({sum(times):.1f} s of work, {dt:.2f} s per step)"}
+                      f"({sum(times):.1f} s of work, {dt:.2f} s per step); one_thread: one run"}
+
+
+def pct(a, ps=(10, 50, 90)):
+    return [round(float(np.percentile(a, x)), 5) for x in ps]
+
+
+def roofline_of(dec_w, chk_w, attn_ms):
+    """The launch's bound is the resource its algorithmic work needs longest: K/V bytes at the
+    HBM peak, or the chunk rows' flops at the bf16 MFMA peak (long prefill chunks)."""
+    attn_bytes = dec_w.bytes + chk_w.bytes
+    t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = chk_w.flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        achieved, peak, unit, bound = chk_w.flops / (attn_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = attn_bytes / (attn_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "alg_bytes_per_launch": int(attn_bytes),
+            "alg_flops_per_launch": int(chk_w.flops)}
+
+
+class Step:
+    """One workload laid out on the device: pool, inputs, outputs and the request batch."""
+
+    def __init__(self, wl, pool_fill="random"):
+        import torch
+        import chunked_prefill_paged_ca_amd as ca
+        from chunked_prefill_paged_ca_amd import accounting as acc
+        from chunked_prefill_paged_ca_amd.workload import StreamCursor
+        from tests import harness as H
+        self.ca, self.torch, self.wl = ca, torch, wl
+        if pool_fill == "random":
+            self.kc, self.vc = H.random_pool(wl, seed=wl.seed)
+        else:
+            self.kc, self.vc = H.alloc_pool(wl, fill=0.0)
+        self.desc = ca.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
+        self.batch = ca.RequestBatch(wl.num_computed, wl.num_prompt_left, wl.block_tables,
+                                     wl.token_budget, wl.max_chunk, wl.page_size, wl.num_pool_pages)
+        plan0 = self.batch.plan()
+        a = plan0.arrays()
+        q_lens = np.diff(a["qo_indptr"])
+        q_raw, k_raw, v_raw = StreamCursor(wl).take(a["req_ids"], q_lens)
+        self.q_in, self.k_in, self.v_in = (H.to_device(x, wl.dtype) for x in (q_raw, k_raw, v_raw))
+        self.q_rot = torch.empty_like(self.q_in)
+        self.o = torch.empty_like(self.q_in)
+        self.lse = torch.empty((plan0.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
+        self.T = plan0.num_tokens
+        self.nd = plan0.num_decodes
+        kv_lens = np.array([int(wl.num_computed[r]) + int(q) for r, q in zip(a["req_ids"], q_lens)])
+        self.dec_w, self.chk_w = acc.plan_work(q_lens, kv_lens, self.nd, wl.num_q_heads,
+                                               wl.num_kv_heads, wl.head_dim, wl.page_size)
+        self.stream = torch.cuda.current_stream()
+        self.scrub_buf = None
+
+    def run(self, ctx, n, time_attention=False, scrub=False):
+        """n whole steps (plan, append, attention); with time_attention every attention launch
+        carries timing events; with scrub a 512 MiB read precedes every step."""
+        wl = self.wl
+        if scrub and self.scrub_buf is None:
+            self.scrub_buf = self.torch.ones(SCRUB_MIB << 18, dtype=self.torch.float32, device="cuda")
+        for _ in range(n):
+            if scrub:
+                # a read of 512 MiB evicts the step's data from L2 and the MALL and leaves
+                # clean lines (a write would leave dirty ones for the next launch to write back)
+                self.scrub_sum = self.scrub_buf.sum()
+            plan = self.batch.plan()
+            ctx.append_kv_rope(self.desc, plan, self.q_in, self.q_rot, self.k_in, self.v_in, self.kc,
+                               self.vc, wl.num_pool_pages, stream=self.stream)
+            if time_attention:
+                ctx.profile_enable(self.ca.PROFILE_ATTENTION)
+            ctx.mixed_attention(self.desc, plan, self.q_rot, self.kc, self.vc, wl.num_pool_pages,
+                                self.o, self.lse, stream=self.stream)
+            if time_attention:
+                ctx.profile_enable(False)
+
+    def parts(self, warmup, steps):
+        """Decode and chunk rows as two launches over the whole device, each timed."""
+        ca, torch = self.ca, self.torch
+        os.environ["CA_SPLIT_ATTENTION"] = "1"
+        try:
+            ctx2 = ca.create(0)
+        finally:
+            del os.environ["CA_SPLIT_ATTENTION"]
+        self.run(ctx2, warmup)
+        torch.cuda.synchronize()
+        ctx2.profile_read()
+        ctx2.profile_enable(True)
+        self.run(ctx2, steps)
+        torch.cuda.synchronize()
+        ctx2.profile_enable(False)
+        km = kernel_means(ctx2.profile_read())
+        ctx2.close()
+        parts = {"kernel_ms": {k: round(v, 5) for k, v in km.items()}}
+        if "decode" in km:
+            bw = self.dec_w.bytes / (km["decode"] * 1e-3) / 1e9
+            parts["decode"] = {"bound": "hbm", "achieved": round(bw, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(bw / HBM_PEAK_GBS, 4),
+                               "alg_bytes_per_launch": int(self.dec_w.bytes)}
+        if "chunk" in km:
+            tf = self.chk_w.flops / (km["chunk"] * 1e-3) / 1e12
+            parts["chunk"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                              "alg_flops_per_launch": int(self.chk_w.flops)}
+        return parts
+
+    def release(self):
+        for name in ("kc", "vc", "q_in", "k_in", "v_in", "q_rot", "o", "lse", "scrub_buf"):
+            setattr(self, name, None)
+        self.torch.cuda.empty_cache()
+
+
+def kernel_means(recs):
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    return {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def attention_times(recs):
+    names = {n for n, _ in recs}
+    name = "attention" if "attention" in names else "generic"  # fp32 storage: plain kernel
+    return name, np.array([ms for n, ms in recs if n == name])
+
+
+def timed_steps(st, ctx, steps, warmup):
+    """Warm-up, then `steps` timed whole steps with every attention launch timed, continued (still
+    timed, outside the wall-clock region) until MIN_TIMED_LAUNCHES launches are timed."""
+    torch = st.torch
+    st.run(ctx, warmup)
+    torch.cuda.synchronize()
+    ctx.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.run(ctx, steps, time_attention=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    in_region = ctx.profile_read()
+    extra = []
+    if steps < MIN_TIMED_LAUNCHES:
+        st.run(ctx, MIN_TIMED_LAUNCHES - steps, time_attention=True)
+        torch.cuda.synchronize()
+        extra = ctx.profile_read()
+    name, region_ms = attention_times(in_region)
+    _, extra_ms = attention_times(extra) if extra else (name, np.zeros(0))
+    all_ms = np.concatenate([region_ms, extra_ms])
+    return elapsed, name, region_ms, all_ms
+
+
+def per_config_leg(n, steps=50, warmup=5):
+    """A one-GPU share workload (Yi-34B: n = 4, LLaMA2-70B: n = 5): whole steps as in the main
+    leg, plus the decode-only and chunk-only launches."""
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    wl = make_config(n)
+    st = Step(wl)
+    ctx = ca.create(0)
+    elapsed, name, region_ms, all_ms = timed_steps(st, ctx, steps, warmup)
+    ctx.close()
+    attn_ms = float(np.mean(all_ms))
+    out = {"workload": wl.name, "tokens_per_step": st.T, "decodes": st.nd,
+           "value": round(st.T * steps / elapsed, 1), "unit": "tokens/s",
+           "ms_per_step": round(elapsed * 1e3 / steps, 4), "steps": steps,
+           "roofline": {**roofline_of(st.dec_w, st.chk_w, attn_ms),
+                        "kernel": f"{name} (decode + chunk rows, one launch)",
+                        "launch_ms": round(attn_ms, 5), "launch_ms_p10_p50_p90": pct(all_ms),
+                        "launches_timed": int(all_ms.size)}}
+    out["parts"] = st.parts(warmup, 20)
+    st.release()
+    return out
+
+
+def sweep_leg(chunks=(64, 128, 256, 512, 2048, 8192), reps=3):
+    """The Llama-13B 8192-token prompt (MHA 40 x 128) prefilled in chunks of c (token budget c,
+    8192 / c steps, each step appending its chunk and attending over the history before it):
+    kernel time summed over all steps (median of `reps` passes), against the one-shot prompt
+    (c = 8192).  Bytes are each step's unique K/V + q; flops the causal pairs (the same at every
+    c); the bound is whichever needs longer at the peaks."""
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd import accounting as acc
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, make_config
+    from tests import harness as H
+    base = make_config(3, chunk=8192)
+    q_raw, k_raw, v_raw = StreamCursor(base).take([0], [8192])
+    q_all, k_all, v_all = (H.to_device(x, base.dtype) for x in (q_raw, k_raw, v_raw))
+    q_rot = torch.empty_like(q_all)
+    o = torch.empty_like(q_all)
+    kc, vc = H.alloc_pool(base, fill=0.0)
+    desc = ca.make_desc(base.num_q_heads, base.num_kv_heads, base.head_dim, base.page_size, base.dtype)
+    ctx = ca.create(0)
+    ctx.profile_enable(ca.PROFILE_ALL)
+    res = {}
+    for c in chunks:
+        wl = make_config(3, chunk=c)
+        work = acc.Work()
+        for i in range(wl.steps):
+            q = min(c, 8192 - i * c)
+            work += acc.chunk_work(i * c, q, wl.num_q_heads, wl.num_kv_heads, wl.head_dim)
+        totals, attn_totals = [], []
+        for _ in range(reps + 1):  # the first pass warms up
+            batch = ca.RequestBatch([0], [8192], wl.block_tables, c, 0, 16, wl.num_pool_pages)
+            ctx.profile_read()
+            done = 0
+            for i in range(wl.steps):
+                batch.update([done], [8192 - done])
+                plan = batch.plan()
+                t = plan.num_tokens
+                sl = slice(done, done + t)
+                ctx.append_kv_rope(desc, plan, q_all[sl], q_rot[sl], k_all[sl], v_all[sl], kc, vc,
+                                   wl.num_pool_pages)
+                ctx.mixed_attention(desc, plan, q_rot[sl], kc, vc, wl.num_pool_pages, o[sl])
+                done += t
+            torch.cuda.synchronize()
+            recs = ctx.profile_read()
+            totals.append(sum(ms for _, ms in recs))
+            attn_totals.append(sum(ms for n, ms in recs if n in ("attention", "merge", "upload")))
+        tot = float(np.median(totals[1:]))
+        att = float(np.median(attn_totals[1:]))
+        t_hbm = work.bytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = work.flops / (BF16_PEAK_TFLOPS * 1e12)
+        if t_mfma > t_hbm:
+            ach, peak, unit, bound = work.flops / (att * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        else:
+            ach, peak, unit, bound = work.bytes / (att * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        res[str(c)] = {"steps": wl.steps, "attention_merge_us": round(att * 1e3, 1),
+                       "with_append_us": round(tot * 1e3, 1), "bound": bound,
+                       "achieved": round(ach, 1), "unit": unit, "frac": round(ach / peak, 4),
+                       "alg_bytes": int(work.bytes), "alg_flops": int(work.flops)}
+    ctx.close()
+    del q_all, k_all, v_all, q_rot, o, kc, vc
+    torch.cuda.empty_cache()
+    one = res[str(chunks[-1])]["attention_merge_us"]
+    for c in chunks:
+        res[str(c)]["vs_one_shot"] = round(res[str(c)]["attention_merge_us"] / one, 3)
+    return {"workload": make_config(3).name.replace(" in chunks of c", ""),
+            "note": "summed kernel time of the whole prompt per chunk size c (median of "
+                    f"{reps} passes); attention_merge_us: the attention launches, their merges "
+                    "and metadata uploads; with_append_us: plus the append launches",
+            "chunks": res}
 
 
 def main():
@@ -85,10 +353,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
-    ap.add_argument("--time-every", type=int, default=10,
-                    help="attach the timing events to the attention launch of every N-th step of "
-                         "the timed region (1: every step; each timed launch adds ~2 us to its "
-                         "step, so the default times one step in ten)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the Yi-34B, LLaMA2-70B and Llama-13B sweep legs")
+    ap.add_argument("--no-scrub", action="store_true", help="skip the cold-HBM (scrubbed) pass")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip re-measuring the HBM and bf16 GEMM rates this device sustains")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -105,120 +372,65 @@ def main():
     from __graft_entry__ import ensure_built
     ensure_built()
     import chunked_prefill_paged_ca_amd as ca
-    from chunked_prefill_paged_ca_amd import accounting as acc
-    from chunked_prefill_paged_ca_amd.workload import StreamCursor, make_config
-    from tests import harness as H
+    from chunked_prefill_paged_ca_amd.workload import make_config
 
     torch.cuda.set_device(0)
     wl = make_config(args.config)
     log(f"workload: {wl.name}")
-    kc, vc = H.random_pool(wl, seed=wl.seed)
-    desc = ca.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
-    batch = ca.RequestBatch(wl.num_computed, wl.num_prompt_left, wl.block_tables, wl.token_budget,
-                            wl.max_chunk, wl.page_size, wl.num_pool_pages)
-    plan0 = batch.plan()
-    a = plan0.arrays()
-    q_lens = np.diff(a["qo_indptr"])
-    q_raw, k_raw, v_raw = StreamCursor(wl).take(a["req_ids"], q_lens)
-    q_in, k_in, v_in = (H.to_device(x, wl.dtype) for x in (q_raw, k_raw, v_raw))
-    q_rot = torch.empty_like(q_in)
-    o = torch.empty_like(q_in)
-    lse = torch.empty((plan0.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
-    T = plan0.num_tokens
-    nd = plan0.num_decodes
-    kv_lens = np.array([int(wl.num_computed[r]) + int(q) for r, q in zip(a["req_ids"], q_lens)])
-    dec_w, chk_w = acc.plan_work(q_lens, kv_lens, nd, wl.num_q_heads, wl.num_kv_heads,
-                                 wl.head_dim, wl.page_size)
-    stream = torch.cuda.current_stream()
+    st = Step(wl)
 
-    def run_steps(ctx, n, time_every=0):
-        for i in range(n):
-            plan = batch.plan()
-            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages, stream=stream)
-            if time_every:
-                ctx.profile_enable(ca.PROFILE_ATTENTION if i % time_every == 0 else False)
-            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, lse, stream=stream)
-
-    def kernel_means(recs):
-        per = {}
-        for name, ms in recs:
-            per.setdefault(name, []).append(ms)
-        return {k: float(np.mean(v)) for k, v in per.items()}
-
-    # ---- timed region: whole steps; the attention launch carries timing events ----
+    # ---- timed region: whole steps; every attention launch carries timing events ----
     ctx = ca.create(0)
-    run_steps(ctx, args.warmup)
-    torch.cuda.synchronize()
-    ctx.profile_read()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(ctx, args.steps, time_every=max(1, args.time_every))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ctx.profile_enable(False)
-    recs0 = ctx.profile_read()
-    km0 = kernel_means(recs0)
-    attn_name = "attention" if "attention" in km0 else "generic"  # fp32 storage: plain kernel
-    attn_ms = km0[attn_name]
-    attn_all = np.array([ms for n, ms in recs0 if n == attn_name])
-    ctx.close()
+    elapsed, attn_name, region_ms, all_ms = timed_steps(st, ctx, args.steps, args.warmup)
     ms_per_step = elapsed * 1e3 / args.steps
-    value = T * args.steps / elapsed
-
-    # The launch's bound is the resource its algorithmic work needs longest: K/V bytes at the HBM
-    # peak, or the chunk rows' flops at the bf16 MFMA peak (long prefill chunks).
-    attn_bytes = dec_w.bytes + chk_w.bytes
-    t_hbm = attn_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = chk_w.flops / (BF16_PEAK_TFLOPS * 1e12)
-    if t_mfma > t_hbm:
-        achieved, peak, unit, bound = chk_w.flops / (attn_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
-    else:
-        achieved, peak, unit, bound = attn_bytes / (attn_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-    traffic = stored_traffic(wl.name)
+    value = st.T * args.steps / elapsed
+    attn_ms = float(np.mean(all_ms))
+    launches = args.warmup + args.steps + max(0, MIN_TIMED_LAUNCHES - args.steps)
     out = {
         "metric": "mixed chunked-prefill+decode attn tokens/s; % HBM peak and % MFMA peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "tokens_per_step": T, "decodes": nd,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens_per_step": st.T, "decodes": st.nd,
                    "token_budget": wl.token_budget, "page_size": wl.page_size,
                    "pool_pages": wl.num_pool_pages, "step": "plan + append_kv_rope + mixed_attention"},
-        "roofline": {"bound": bound, "kernel": "attention (decode + chunk rows, one launch)",
-                     "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": int(attn_bytes),
-                     "alg_flops_per_launch": int(chk_w.flops),
+        "roofline": {**roofline_of(st.dec_w, st.chk_w, attn_ms),
+                     "kernel": f"{attn_name} (decode + chunk rows, one launch)",
+                     "traffic": stored_traffic(wl.name),
                      "launch_ms": round(attn_ms, 5),
-                     "launch_ms_p10_p50_p90": [round(float(np.percentile(attn_all, x)), 5) for x in (10, 50, 90)],
-                     "launches_timed": int(attn_all.size)},
+                     "launch_ms_p10_p50_p90": pct(all_ms),
+                     "launches_timed": int(all_ms.size),
+                     "launches_in_timed_region": int(region_ms.size),
+                     "launch_ms_timed_region_mean": round(float(np.mean(region_ms)), 5),
+                     "attention_launches_this_leg": launches},
     }
+    if not args.no_scrub:
+        st.run(ctx, MIN_TIMED_LAUNCHES, time_attention=True, scrub=True)
+        torch.cuda.synchronize()
+        _, cold = attention_times(ctx.profile_read())
+        cm = float(np.mean(cold))
+        out["roofline"]["scrubbed"] = {
+            "note": f"{SCRUB_MIB} MiB read before every step, outside the events",
+            "launch_ms": round(cm, 5), "launch_ms_p10_p50_p90": pct(cold),
+            "launches_timed": int(cold.size),
+            "frac": roofline_of(st.dec_w, st.chk_w, cm)["frac"]}
+    ctx.close()
 
     # ---- second pass (not timed for `value`): decode and chunk as separate launches ----
     if not args.no_parts:
-        os.environ["CA_SPLIT_ATTENTION"] = "1"
-        ctx2 = ca.create(0)
-        del os.environ["CA_SPLIT_ATTENTION"]
-        run_steps(ctx2, args.warmup)
-        torch.cuda.synchronize()
-        ctx2.profile_read()
-        ctx2.profile_enable(True)
-        run_steps(ctx2, args.steps)
-        torch.cuda.synchronize()
-        ctx2.profile_enable(False)
-        km = kernel_means(ctx2.profile_read())
-        ctx2.close()
-        parts = {"kernel_ms": {k: round(v, 5) for k, v in km.items()}}
-        if "decode" in km:
-            bw = dec_w.bytes / (km["decode"] * 1e-3) / 1e9
-            parts["decode"] = {"bound": "hbm", "achieved": round(bw, 1), "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": round(bw / HBM_PEAK_GBS, 4),
-                               "alg_bytes_per_launch": int(dec_w.bytes)}
-        if "chunk" in km:
-            tf = chk_w.flops / (km["chunk"] * 1e-3) / 1e12
-            parts["chunk"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                              "alg_flops_per_launch": int(chk_w.flops)}
-        out["parts"] = parts
+        out["parts"] = st.parts(args.warmup, max(args.steps, MIN_TIMED_LAUNCHES))
+    st.release()
+
+    # ---- the other workloads, one after the other ----
+    if not args.no_per_config and args.config == 2:
+        pc = {}
+        for n in (4, 5):
+            log(f"per-config leg: {make_config(n).name}")
+            pc[str(n)] = per_config_leg(n)
+        log("per-config leg: Llama-13B chunk-size sweep")
+        pc["3"] = sweep_leg()
+        out["per_config"] = pc
 
     # ---- what this device sustains (after the timed region): the roofline above uses the
     # datasheet peaks; these put the same launch against measured ones ----

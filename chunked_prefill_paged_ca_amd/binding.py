@@ -68,6 +68,7 @@ class CaProfileRecord(ctypes.Structure):
 
 PROFILE_ALL, PROFILE_UPLOAD, PROFILE_APPEND, PROFILE_ATTENTION, PROFILE_MERGE = 1, 2, 4, 8, 16
 PROFILE_PROJECTION = 32
+VALIDATE_WRITE_TARGETS = 1
 
 
 class CaError(RuntimeError):
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
                                                vp, vp, vp, vp, ctypes.c_int64, vp]
         L.ca_qkv_projection.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.c_int32, ctypes.c_int32,
                                         vp, vp, vp, vp]
+        L.ca_plan_validate.argtypes = [ctypes.POINTER(CaPlan), ctypes.c_int64, ctypes.c_int32]
         L.ca_profile_enable.argtypes = [vp, ctypes.c_int]
         L.ca_profile_read.argtypes = [vp, ctypes.POINTER(CaProfileRecord), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -114,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.ca_sched_free_pages.restype = ctypes.c_int64
         for fn in ("ca_create", "ca_destroy", "ca_plan_batch", "ca_append_kv_rope",
                    "ca_mixed_attention", "ca_append_kv_rope_packed", "ca_qkv_projection",
-                   "ca_profile_enable", "ca_profile_read", "ca_sched_create",
+                   "ca_plan_validate", "ca_profile_enable", "ca_profile_read", "ca_sched_create",
                    "ca_sched_destroy", "ca_sched_add", "ca_sched_step", "ca_sched_commit",
                    "ca_sched_get"):
             getattr(L, fn).restype = ctypes.c_int
@@ -173,6 +175,13 @@ class Plan:
                     "num_deferred_decodes", "page_size", "generation"):
             return getattr(self.c, name)
         raise AttributeError(name)
+
+    def validate(self, num_pool_pages: int, write_targets: bool = False):
+        """ca_plan_validate: raises CaError when the plan is inconsistent with the pool (or, with
+        write_targets, when two scheduled tokens would append to the same page slot)."""
+        _check(lib().ca_plan_validate(ctypes.byref(self.c), int(num_pool_pages),
+                                      VALIDATE_WRITE_TARGETS if write_targets else 0),
+               "ca_plan_validate")
 
     def arrays(self) -> dict:
         ns, npg = self.c.num_seqs, self.c.num_pages

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -89,15 +90,44 @@ struct Staging {
     bool pending[kSlots / kGroup] = {};
     int next = 0;
 
+    // Every slot is allocated here, at context creation, with kInitialBytes (enough for the
+    // metadata of a step of several thousand sequences and ~250 K pages), so that a steady
+    // stream of steps never allocates: a slot grows (doubling) only for a plan larger than that.
+    static constexpr size_t kInitialBytes = size_t(2) << 20;
     hipError_t init() {
         for (int i = 0; i < kSlots / kGroup; ++i) {
             hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming | hipEventDisableSystemFence);
             if (e != hipSuccess) return e;
         }
+        for (int i = 0; i < kSlots; ++i) {
+            hipError_t e = grow(i, kInitialBytes);
+            if (e != hipSuccess) return e;
+        }
         return hipSuccess;
     }
-    hipError_t acquire(size_t bytes, int* slot) {
+    hipError_t grow(int i, size_t want) {
+        if (host[i]) (void)hipHostFree(host[i]);
+        host[i] = nullptr;
+        dev[i] = nullptr;
+        cap[i] = 0;
+        hipError_t e = hipHostMalloc(&host[i], want, hipHostMallocMapped | hipHostMallocCoherent);
+        if (e != hipSuccess) { host[i] = nullptr; return e; }
+        e = hipHostGetDevicePointer(&dev[i], host[i], 0);
+        if (e != hipSuccess) {
+            (void)hipHostFree(host[i]);
+            host[i] = nullptr;
+            dev[i] = nullptr;
+            return e;
+        }
+        cap[i] = want;
+        return hipSuccess;
+    }
+    // The next slot of the ring, once the upload that last read it has completed.  With
+    // may_grow false a plan larger than the slot is refused (*slot = -1) instead of allocating.
+    hipError_t acquire(size_t bytes, int* slot, bool may_grow = true) {
+        *slot = -1;
         const int i = next;
+        if (cap[i] < bytes && !may_grow) return hipSuccess;
         next = (next + 1) % kSlots;
         const int g = i / kGroup;
         if (i % kGroup == 0 && pending[g]) {
@@ -106,21 +136,8 @@ struct Staging {
             pending[g] = false;
         }
         if (cap[i] < bytes) {
-            if (host[i]) (void)hipHostFree(host[i]);
-            host[i] = nullptr;
-            dev[i] = nullptr;
-            cap[i] = 0;
-            size_t want = bytes * 2 > (size_t(1) << 20) ? bytes * 2 : (size_t(1) << 20);  // see DevBuf
-            hipError_t e = hipHostMalloc(&host[i], want, hipHostMallocMapped | hipHostMallocCoherent);
-            if (e != hipSuccess) { host[i] = nullptr; return e; }
-            e = hipHostGetDevicePointer(&dev[i], host[i], 0);
-            if (e != hipSuccess) {
-                (void)hipHostFree(host[i]);
-                host[i] = nullptr;
-                dev[i] = nullptr;
-                return e;
-            }
-            cap[i] = want;
+            hipError_t e = grow(i, bytes * 2);  // doubling, see DevBuf
+            if (e != hipSuccess) return e;
         }
         *slot = i;
         return hipSuccess;
@@ -210,7 +227,20 @@ struct Profiler {
         // the caches around the timed launch, a few microseconds each time).
         hipEvent_t e = nullptr;
         if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
+        ++created;
         return e;
+    }
+    // Create events ahead of use (when timing is switched on), so that timed launches draw them
+    // from the pool instead of creating them between steps.
+    static constexpr size_t kReserve = 512;  // 256 timed launches between two reads
+    size_t created = 0;
+    void reserve() {
+        while (created < kReserve) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
+            pool.push_back(e);
+            ++created;
+        }
     }
     void release() {
         for (auto& r : pending) {
@@ -220,6 +250,7 @@ struct Profiler {
         for (auto e : pool) (void)hipEventDestroy(e);
         pending.clear();
         pool.clear();
+        created = 0;
     }
 };
 
@@ -296,6 +327,14 @@ struct ca_ctx {
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
     ca::Linear* linear = nullptr;  // hipBLASLt state of ca_qkv_projection (created on first use)
     bool projection_library = false;  // CA_PROJECTION_LIBRARY=1: the library GEMM for every T
+    // CA_DEBUG_VALIDATE=1: the append also checks that no two scheduled tokens write the same
+    // (page, slot) (a sort of the step's write targets on the host).
+    bool debug_validate = false;
+    int32_t work_max_page = -1;     // largest page id of the plan meta_buf holds
+    bool work_targets_checked = false;  // its write targets were checked
+    // host-side work lists of prepare(), kept so that a steady stream of steps reuses them
+    std::vector<int4> items, merges, citems, groups, clist;
+    std::vector<int32_t> wave_items;
 };
 
 namespace {
@@ -377,11 +416,22 @@ ca_status check_desc(const ca_attn_desc* d, const ca_plan* plan, Shape* sh) {
 }
 
 // Host-side consistency of the plan arrays against the pool (they are read by the kernels, so
-// every index is checked here before a launch).
-ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
+// every index is checked here before a launch).  *max_page receives the largest page id the plan
+// names.  With write_targets, the (page, slot) every scheduled token is appended to must also be
+// unique over the whole step: two sequences (or two positions of one sequence) that would write
+// the same slot are a block-table error the append kernel cannot see -- its workgroups would race
+// on that slot -- and the block table must stay consistent across appends (pinghaoyang.com.cn
+// "Sarathi-Serve 完全拆解", section "先验证数值与状态正确性").
+ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_targets,
+                               int32_t* max_page) {
     const int32_t ns = plan->num_seqs;
     const int32_t P = plan->page_size;
+    *max_page = -1;
     if (ns == 0) return CA_OK;
+    if (P <= 0) {
+        ca::set_error("plan page_size must be > 0");
+        return CA_ERR_INVALID_ARG;
+    }
     if (plan->qo_indptr[0] != 0 || plan->kv_page_indptr[0] != 0) {
         ca::set_error("indptr arrays must start at 0");
         return CA_ERR_INVALID_ARG;
@@ -408,12 +458,35 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool) {
         ca::set_error("indptr totals disagree with num_tokens / num_pages");
         return CA_ERR_INVALID_ARG;
     }
+    int32_t top = -1;
     for (int32_t j = 0; j < plan->num_pages; ++j) {
         if (plan->kv_page_indices[j] < 0 || plan->kv_page_indices[j] >= pool) {
             ca::set_error("page index " + std::to_string(plan->kv_page_indices[j]) + " outside the pool");
             return CA_ERR_INVALID_ARG;
         }
+        if (plan->kv_page_indices[j] > top) top = plan->kv_page_indices[j];
     }
+    if (write_targets) {
+        std::vector<std::pair<int64_t, int32_t>> t;  // (page * P + slot, sequence)
+        t.reserve(static_cast<size_t>(plan->num_tokens));
+        for (int32_t s = 0; s < ns; ++s) {
+            const int32_t q = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+            const int32_t p0 = plan->kv_page_indptr[s];
+            const int32_t kv_len = (plan->kv_page_indptr[s + 1] - p0 - 1) * P + plan->kv_last_page_len[s];
+            for (int32_t pos = kv_len - q; pos < kv_len; ++pos)
+                t.emplace_back(static_cast<int64_t>(plan->kv_page_indices[p0 + pos / P]) * P + pos % P, s);
+        }
+        std::sort(t.begin(), t.end());
+        for (size_t i = 1; i < t.size(); ++i) {
+            if (t[i].first == t[i - 1].first) {
+                ca::set_error("sequences " + std::to_string(t[i - 1].second) + " and " +
+                              std::to_string(t[i].second) + " both append to page " +
+                              std::to_string(t[i].first / P) + " slot " + std::to_string(t[i].first % P));
+                return CA_ERR_INVALID_ARG;
+            }
+        }
+    }
+    *max_page = top;
     return CA_OK;
 }
 
@@ -647,25 +720,50 @@ ca_status ensure_freq(ca_ctx* ctx, const Shape& sh) {
 }
 
 // defer: leave the metadata in its staging slot (ctx->defer_slot) for the append launch that
-// follows to copy; otherwise copy it now with the upload kernel.
+// follows to copy; otherwise copy it now with the upload kernel.  writes: the caller appends to
+// the cache (with CA_DEBUG_VALIDATE its write targets are checked).
 ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
-                  hipStream_t stream, bool defer = false) {
+                  hipStream_t stream, bool defer = false, bool writes = false) {
     const int G = sh.hq / sh.hkv;
     int32_t dec_wgs = 0;
     const bool mfma = sh.dtype == CA_BF16 && G <= 16;
     WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
                 mfma ? decode_shares(ctx, plan, sh, &dec_wgs) : -1,
                 mfma ? chunk_split_keys(ctx, plan, sh, ctx->csplit_override) : -1, sh.theta};
-    if (plan->generation != 0 && key == ctx->work_key) return CA_OK;
-    ca_status st = validate_plan_arrays(plan, pool);
+    const bool check_targets = writes && ctx->debug_validate;
+    if (plan->generation != 0 && key == ctx->work_key) {
+        // the plan was validated when it was first seen, but against that call's pool: its pages
+        // must also lie in this call's
+        if (ctx->work_max_page >= pool) {
+            ca::set_error("page index " + std::to_string(ctx->work_max_page) + " outside the pool");
+            return CA_ERR_INVALID_ARG;
+        }
+        if (check_targets && !ctx->work_targets_checked) {
+            int32_t top = -1;
+            ca_status st = validate_plan_arrays(plan, pool, true, &top);
+            if (st != CA_OK) return st;
+            ctx->work_targets_checked = true;
+        }
+        return CA_OK;
+    }
+    int32_t max_page = -1;
+    ca_status st = validate_plan_arrays(plan, pool, check_targets, &max_page);
     if (st != CA_OK) return st;
     ctx->work_key = WorkKey{};  // meta_buf is about to change; nothing matches until it is whole
     ctx->defer_slot = -1;
     st = ensure_freq(ctx, sh);
     if (st != CA_OK) return st;
 
-    std::vector<int4> items, merges, citems, groups;
-    std::vector<int32_t> wave_items;
+    std::vector<int4>& items = ctx->items;
+    std::vector<int4>& merges = ctx->merges;
+    std::vector<int4>& citems = ctx->citems;
+    std::vector<int4>& groups = ctx->groups;
+    std::vector<int32_t>& wave_items = ctx->wave_items;
+    items.clear();
+    merges.clear();
+    citems.clear();
+    groups.clear();
+    wave_items.clear();
     int32_t slots = 0, cslots = 0;
     if (mfma) {
         // decode: share w holds blocks [B w / W, B (w + 1) / W) of the B blocks of all
@@ -715,7 +813,8 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         // a column is one (row, q head) pair, numbered row * G + head
         const int32_t Lc = key.csplit;
         const int32_t cols_per_block = ca::chunk_cols_per_block();
-        std::vector<int4> clist;
+        std::vector<int4>& clist = ctx->clist;
+        clist.clear();
         for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
             const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
             const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
@@ -859,6 +958,8 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         if (e != hipSuccess) return device_error("partial allocation", e);
     }
     ctx->work_key = key;
+    ctx->work_max_page = max_page;
+    ctx->work_targets_checked = check_targets;
     return CA_OK;
 }
 
@@ -891,6 +992,7 @@ ca_status ca_create(int device, ca_ctx** out) {
     }
     if (const char* env = std::getenv("CA_CHUNK_SPLIT")) ctx->csplit_override = std::atoi(env);
     if (const char* env = std::getenv("CA_PROJECTION_LIBRARY")) ctx->projection_library = std::atoi(env) != 0;
+    if (const char* env = std::getenv("CA_DEBUG_VALIDATE")) ctx->debug_validate = std::atoi(env) != 0;
     e = ctx->staging.init();
     if (e != hipSuccess) {
         ctx->staging.release();
@@ -948,7 +1050,7 @@ ca_status append_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    st = prepare(ctx, plan, sh, num_pool_pages, stream, /*defer=*/true);
+    st = prepare(ctx, plan, sh, num_pool_pages, stream, /*defer=*/true, /*writes=*/true);
     if (st != CA_OK) return st;
     // A fresh plan's metadata is still in its staging slot: this launch also copies it to device
     // memory (for the attention launch after it), and reads its own per-row values from the
@@ -1129,11 +1231,26 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     return CA_OK;
 }
 
+ca_status ca_plan_validate(const ca_plan* plan, int64_t num_pool_pages, int32_t flags) {
+    ca::clear_error();
+    ca_status st = check_plan(plan);
+    if (st != CA_OK) return st;
+    if (num_pool_pages <= 0) { ca::set_error("num_pool_pages must be > 0"); return CA_ERR_INVALID_ARG; }
+    if (flags & ~CA_VALIDATE_WRITE_TARGETS) { ca::set_error("ca_plan_validate: unknown flags"); return CA_ERR_INVALID_ARG; }
+    int32_t top = -1;
+    return validate_plan_arrays(plan, num_pool_pages, (flags & CA_VALIDATE_WRITE_TARGETS) != 0, &top);
+}
+
 ca_status ca_profile_enable(ca_ctx* ctx, int enable) {
     ca::clear_error();
     if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
     if (enable < 0 || enable > 63) { ca::set_error("ca_profile_enable: unknown flags"); return CA_ERR_INVALID_ARG; }
     ctx->prof.mask = (enable & CA_PROFILE_ALL) ? 0x3e : enable;
+    if (ctx->prof.mask) {
+        DeviceGuard g(ctx->device);
+        if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
+        ctx->prof.reserve();
+    }
     return CA_OK;
 }
 

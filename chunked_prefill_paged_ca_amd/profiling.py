@@ -2,6 +2,8 @@
 
     python -m chunked_prefill_paged_ca_amd.profiling stats <kernel_stats.csv> <title> <command>
         -> markdown table of per-kernel dispatch durations on stdout
+    python -m chunked_prefill_paged_ca_amd.profiling trace <kernel_trace.csv> <title> <command>
+        -> markdown table of dispatch durations per (kernel, grid size) on stdout
     python -m chunked_prefill_paged_ca_amd.profiling traffic <fetch counter_collection.csv>
            <write counter_collection.csv> <copy MiB> <command> <workload>
         -> JSON: FETCH_SIZE / WRITE_SIZE per attention launch, scaled by what the same counters
@@ -26,11 +28,15 @@ from collections import defaultdict
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ATTENTION_SOURCES = ("attn_mixed.hip", "attn_decode.h", "attn_chunk.h", "mfma.h", "internal.h")
+# The attention kernel's sources and the host code that shapes its launch (decode shares, chunk
+# key splits and hence how many fp32 partials are written and merged).
+ATTENTION_SOURCES = ("attn_mixed.hip", "attn_decode.h", "attn_chunk.h", "mfma.h", "internal.h",
+                     "api.hip", "merge.hip")
 
 
 def kernel_sources_sha256() -> str:
-    """Hash of the attention kernel's sources: a stored counter reading is valid only for them."""
+    """Hash of the sources behind the attention launch: a stored counter reading is valid only
+    for them."""
     h = hashlib.sha256()
     for name in ATTENTION_SOURCES:
         with open(os.path.join(HERE, "csrc", name), "rb") as f:
@@ -52,6 +58,30 @@ def stats_md(path: str, title: str, cmd: str) -> str:
         out.append(f"| {short_name(r['Name'])[:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def trace_md(path: str, title: str, cmd: str) -> str:
+    """Per-dispatch durations from a rocprofv3 kernel_trace.csv, grouped by kernel AND grid size:
+    one bench run launches the same kernel for several workloads (different grids), and each
+    workload's launches are averaged on their own."""
+    rows = list(csv.DictReader(open(path)))
+    gcols = [c for c in ("Grid_Size_X", "Grid_Size") if rows and c in rows[0]]
+    groups = defaultdict(list)
+    first = {}
+    for i, r in enumerate(rows):
+        grid = int(r[gcols[0]]) if gcols else 0
+        key = (short_name(r["Kernel_Name"]), grid)
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        first.setdefault(key, i)
+    out = [f"# {title}", "", "Command (run from the repository root on one MI355X; TMPDIR=/tmp):", "",
+           f"    {cmd}", "", "rocprofv3 kernel trace, grouped by kernel and grid size (work-items), "
+           "in order of first dispatch:", "",
+           "| kernel | grid | calls | avg us | p10 us | p50 us | p90 us |", "|---|---|---|---|---|---|---|"]
+    for key in sorted(groups, key=lambda k: first[k]):
+        v = np.asarray(groups[key])
+        out.append(f"| {key[0][:70]} | {key[1]} | {v.size} | {v.mean():.2f} | "
+                   f"{np.percentile(v, 10):.2f} | {np.percentile(v, 50):.2f} | {np.percentile(v, 90):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -165,6 +195,8 @@ def main(argv):
     if len(argv) >= 6 and argv[0] == "parts":
         timing = json.loads(open(argv[4]).read().strip().splitlines()[-1])
         sys.stdout.write(parts(argv[1], argv[2], argv[3], timing, argv[5]))
+    elif len(argv) >= 4 and argv[0] == "trace":
+        sys.stdout.write(trace_md(argv[1], argv[2], argv[3]))
     elif len(argv) >= 4 and argv[0] == "stats":
         sys.stdout.write(stats_md(argv[1], argv[2], argv[3]))
     elif len(argv) >= 6 and argv[0] == "traffic":

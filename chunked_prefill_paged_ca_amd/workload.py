@@ -37,15 +37,23 @@ CONFIG_NAMES = {
 
 
 def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float values to the storage type and return them as float32 (input drawing only)."""
+    """Round float values to the storage type and return them as float32 (input drawing only).
+
+    bf16: round to nearest, ties to even, on the float32 bit pattern (add 0x7fff plus the lowest
+    kept bit, clear the low 16 bits) -- the same values torch's float32 -> bfloat16 conversion
+    gives for finite inputs, at numpy speed; arrays holding a non-finite value go through torch."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "fp32":
         return x
     if dtype != "bf16":
         raise ValueError(dtype)
-    import torch  # CPU conversion; round-to-nearest-even
+    if not np.isfinite(x).all():
+        import torch  # CPU conversion; round-to-nearest-even, NaN kept
 
-    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    u = x.view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 @dataclass

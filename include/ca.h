@@ -124,7 +124,12 @@ typedef struct ca_ctx ca_ctx;
  *   CA_CHUNK_SPLIT=n        keys per prefill-chunk split (rounded up to 32 and to at least
  *                           1/64 of the longest chunk row's keys);
  *   CA_SPLIT_ATTENTION=1    decode and prefill-chunk rows as two launches instead of one;
- *   CA_PROJECTION_LIBRARY=1 ca_qkv_projection always through hipBLASLt.
+ *   CA_PROJECTION_LIBRARY=1 ca_qkv_projection always through hipBLASLt;
+ *   CA_DEBUG_VALIDATE=1     ca_append_kv_rope(_packed) also checks that no two scheduled tokens
+ *                           append to the same (page, slot) (ca_plan_validate with
+ *                           CA_VALIDATE_WRITE_TARGETS; a host-side sort of the step's targets).
+ * The context's pinned staging ring (8 slots of 2 MiB) is allocated here; device workspace is
+ * allocated by the first call that needs it and grows only for a larger step.
  * Errors: CA_ERR_INVALID_ARG (null out, no such device), CA_ERR_DEVICE (a HIP error).
  */
 ca_status ca_create(int device, ca_ctx** out);
@@ -153,6 +158,22 @@ ca_status ca_destroy(ca_ctx* ctx);
  */
 ca_status ca_plan_batch(const ca_request* reqs, int32_t n, const ca_plan_params* params,
                         ca_plan* plan);
+
+/*
+ * ca_plan_validate -- host-only consistency check of a plan against a pool of num_pool_pages
+ * pages (no device work; the device calls run the same check on every new plan generation).
+ * Checks: indptr arrays start at 0 and agree with num_tokens / num_pages; every sequence has
+ * >= 1 row, >= 1 page, kv_last_page_len in [1, P] and no more rows than keys; decodes have one
+ * row; every page id lies in [0, num_pool_pages).  With CA_VALIDATE_WRITE_TARGETS it also checks
+ * that the (page, slot) each scheduled token is appended to -- position p of a sequence goes to
+ * slot p % P of its logical page p / P -- is unique over the step: the block tables must stay
+ * consistent across appends ([SS] "先验证数值与状态正确性"), and two sequences whose tables share
+ * a page they both write would race inside the append.
+ * Errors: CA_ERR_INVALID_ARG (null plan or arrays, an inconsistency above; ca_last_error names
+ * the sequences and the slot of a collision, unknown flags).
+ */
+enum { CA_VALIDATE_WRITE_TARGETS = 1 };
+ca_status ca_plan_validate(const ca_plan* plan, int64_t num_pool_pages, int32_t flags);
 
 /*
  * ca_append_kv_rope -- rotary embedding at absolute positions, then append the step's K/V.

@@ -164,17 +164,20 @@ class Session:
 
     requests -- the request indices whose cache is kept (default: all).  Untracked requests are
                 still planned (the plan only needs their sizes) but get no attention output.
+    history  -- optional callable r -> (k, v) returning the same arrays as wl.history(r) (e.g.
+                drawn once ahead of time); default wl.history.
     """
 
-    def __init__(self, wl, requests: Optional[Iterable[int]] = None):
+    def __init__(self, wl, requests: Optional[Iterable[int]] = None, history=None):
         self.wl = wl
         self.num_computed = wl.num_computed.astype(np.int32).copy()
         self.num_prompt_left = wl.num_prompt_left.astype(np.int32).copy()
         tracked = range(wl.n) if requests is None else requests
         self.k: Dict[int, np.ndarray] = {}
         self.v: Dict[int, np.ndarray] = {}
+        draw = wl.history if history is None else history
         for r in tracked:
-            hk, hv = wl.history(r)
+            hk, hv = draw(r)
             self.k[r] = hk.astype(np.float64)
             self.v[r] = hv.astype(np.float64)
 

@@ -64,8 +64,18 @@ def _gather(k_cache, v_cache, pi, si):
     return k.reshape(n, H, -1), v.reshape(n, H, -1)
 
 
-def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None):
-    """Scatter each request's drawn history (positions 0..nc-1) into its pages."""
+def draw_histories(wl, requests: Iterable[int], threads: int = 16):
+    """{r: wl.history(r)} drawn on a thread pool (each request has its own seeded generator, and
+    numpy releases the GIL while it fills an array, so the draws run side by side)."""
+    from concurrent.futures import ThreadPoolExecutor
+    reqs = list(requests)
+    with ThreadPoolExecutor(max(1, min(threads, len(reqs)))) as ex:
+        return dict(zip(reqs, ex.map(wl.history, reqs)))
+
+
+def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None, hist=None):
+    """Scatter each request's drawn history (positions 0..nc-1) into its pages (hist: histories
+    drawn ahead of time, {r: (k, v)}; default: drawn here)."""
     import torch
     reqs = range(wl.n) if requests is None else requests
     dev = k_cache.device
@@ -73,7 +83,7 @@ def write_history(wl, k_cache, v_cache, requests: Optional[Iterable[int]] = None
         nc = int(wl.num_computed[r])
         if nc == 0:
             continue
-        hk, hv = wl.history(r)
+        hk, hv = wl.history(r) if hist is None else hist[r]
         pages, slots = _slots(wl.block_tables[r], wl.page_size, 0, nc)
         pi = torch.from_numpy(pages).to(dev)
         si = torch.from_numpy(slots).to(dev)
@@ -98,6 +108,15 @@ def read_dense(k_cache, v_cache, table: np.ndarray, P: int, kv_len: int):
     pages, slots = _slots(table, P, 0, kv_len)
     pi = torch.from_numpy(pages).to(k_cache.device)
     si = torch.from_numpy(slots).to(k_cache.device)
+    k, v = _gather(k_cache, v_cache, pi, si)
+    return (k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64))
+
+
+def read_positions(k_cache, v_cache, table: np.ndarray, P: int, start: int, stop: int):
+    """Gather positions start..stop-1 of one request into dense [n, Hkv, d] float64."""
+    pages, slots = _slots(np.asarray(table), P, start, stop)
+    pi = __import__("torch").from_numpy(pages).to(k_cache.device)
+    si = __import__("torch").from_numpy(slots).to(k_cache.device)
     k, v = _gather(k_cache, v_cache, pi, si)
     return (k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64))
 

@@ -1,5 +1,7 @@
 """CPU tests of the C ABI: the library loads, exports every declared symbol, and its host plan
 equals the oracle's plan bit for bit (statuses, counts and every metadata array)."""
+import ctypes
+
 import numpy as np
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -120,6 +122,37 @@ def test_plan_rejects_bad_params(L, oracle_mod):
     _compare(oracle_mod, [-3], [0], t, 8, 0, 16, 4)
     _compare(oracle_mod, [1], [0], t, 8, 0, 16, 4, align=-1)
     _compare(oracle_mod, [3], [-1], t, 8, 0, 16, 4)
+
+
+def test_plan_validate_write_targets(L):
+    """ca_plan_validate: two block tables that share a page both sequences append to are refused
+    with CA_VALIDATE_WRITE_TARGETS (and pass the range checks without it); a shared read-only
+    prefix page is fine; a table that lists a page twice collides with itself; a page id beyond
+    a smaller pool is refused."""
+    P = 16
+    # A: 20-token prompt on pages [3, 5] (slots 0..15 of 3, 0..3 of 5); B: 10 tokens on [5]
+    overlap = ca.plan_batch([0, 0], [20, 10], [np.array([3, 5]), np.array([5])], 64, 0, P, 8)
+    overlap.validate(8)
+    with pytest.raises(ca.CaError, match="sequences 0 and 1 both append to page 5 slot 0"):
+        overlap.validate(8, write_targets=True)
+    # two decodes whose tables end on the same page: both append position 16 to page 6 slot 0
+    dec = ca.plan_batch([16, 16], [0, 0], [np.array([1, 6]), np.array([2, 6])], 64, 0, P, 8)
+    dec.validate(8)
+    with pytest.raises(ca.CaError, match="both append to page 6 slot 0"):
+        dec.validate(8, write_targets=True)
+    # a shared prefix page (read by both, written by neither) is consistent
+    shared = ca.plan_batch([16, 16], [4, 4], [np.array([3, 6]), np.array([3, 7])], 64, 0, P, 8)
+    shared.validate(8, write_targets=True)
+    # one table naming page 2 twice: positions 0..3 and 16..19 land in the same slots
+    twice = ca.plan_batch([0], [20], [np.array([2, 2])], 64, 0, P, 8)
+    with pytest.raises(ca.CaError, match="sequences 0 and 0 both append to page 2 slot 0"):
+        twice.validate(8, write_targets=True)
+    # the pool bound is the caller's: page 7 is outside a 7-page pool
+    with pytest.raises(ca.CaError, match="outside the pool"):
+        shared.validate(7)
+    with pytest.raises(ca.CaError, match="unknown flags"):
+        lib_flags = 4
+        binding._check(L.ca_plan_validate(ctypes.byref(shared.c), 8, lib_flags), "ca_plan_validate")
 
 
 # ------------------------------------------------------------------------------------------

@@ -109,6 +109,69 @@ def run_and_check(ctx, oracle, wl, steps=None, rows_per_seq=None, track=None, po
     return results, (k_cache, v_cache), sess
 
 
+def run_every_row(ctx, oracle, wl, k_cache, v_cache, hist, group=32, label=""):
+    """One step of a large workload on the GPU, then EVERY row against the oracle.
+
+    The GPU pool must already hold every request's history; `hist` holds the same histories as
+    drawn ({r: (k, v)}).  The oracle keeps a dense fp64 cache per tracked request, so it is run
+    in groups of `group` requests (a Session tracking only them, attending only their rows): its
+    fp64 memory stays bounded while every decode row, every chunk row, and every appended K/V
+    slot is compared.  Bars as in run_and_check."""
+    import torch
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor
+    from tests import harness as H
+
+    dt = wl.dtype
+    ref_plan = oracle.Session(wl, requests=[]).plan()
+    plan = H.lib_plan(wl, wl.num_computed, wl.num_prompt_left)
+    a = plan.arrays()
+    for k in ("req_ids", "qo_indptr", "kv_page_indptr", "kv_page_indices", "kv_last_page_len"):
+        assert np.array_equal(a[k], ref_plan[k]), (label, k)
+    q, k, v = StreamCursor(wl).take(ref_plan["req_ids"], np.diff(ref_plan["qo_indptr"]))
+    q_out, o, lse = H.gpu_step(ctx, wl, plan, q, k, v, k_cache, v_cache)
+    torch.cuda.synchronize()
+    go = o.float().cpu().numpy().astype(np.float64)
+    gl = lse.cpu().numpy().astype(np.float64)
+    gq = q_out.float().cpu().numpy().astype(np.float64)
+    qo = ref_plan["qo_indptr"]
+    req_ids = [int(r) for r in ref_plan["req_ids"]]
+    seq_of = {r: s_ for s_, r in enumerate(req_ids)}
+    checked = np.zeros(plan.num_tokens, dtype=bool)
+    worst, lworst = 0.0, 0.0
+    for g0 in range(0, len(req_ids), group):
+        members = req_ids[g0:g0 + group]
+        sess = oracle.Session(wl, requests=members, history=hist.__getitem__)
+        rows = np.concatenate([np.arange(qo[seq_of[r]], qo[seq_of[r] + 1]) for r in members])
+        ref = sess.step(ref_plan, q, k, v, rows=rows)
+        if g0 == 0:
+            uq = H.ulp_distance(gq, ref["q_rot"], dt)
+            assert uq.max() <= 1.0 and (uq > 0).mean() <= 1e-3, (label, "q_rot", uq.max())
+        err = np.abs(go[rows] - ref["o"][rows]).max()
+        lerr = np.abs(gl[rows] - ref["lse"][rows]).max()
+        assert np.all(np.isfinite(go[rows])), (label, g0, "non-finite output")
+        assert err <= TOL_O[dt], (label, g0, err)
+        assert lerr <= TOL_LSE[dt], (label, g0, lerr)
+        worst, lworst = max(worst, err), max(lworst, lerr)
+        checked[rows] = True
+        _log(f"[{label}] requests {g0}..{g0 + len(members) - 1}: {rows.size} rows, max|do|={err:.3e} "
+             f"max|dlse|={lerr:.3e}")
+        # the slots this step appended, for every member
+        for r in members:
+            s_ = seq_of[r]
+            n_new = int(qo[s_ + 1] - qo[s_])
+            kv_len = int(sess.num_computed[r])
+            gk, gv = H.read_positions(k_cache, v_cache, wl.block_tables[r], wl.page_size,
+                                      kv_len - n_new, kv_len)
+            uk = H.ulp_distance(gk, sess.k[r][kv_len - n_new:], dt)
+            assert uk.max() <= 1.0, (label, r, "k cache ulp", uk.max())
+            assert np.array_equal(gv, sess.v[r][kv_len - n_new:]), (label, r, "v cache")
+        del sess, ref
+    assert checked.all(), (label, "rows left unchecked", int((~checked).sum()))
+    _log(f"[{label}] every row: T={plan.num_tokens} seqs={plan.num_seqs} decodes={plan.num_decodes} "
+         f"max|do|={worst:.3e} max|dlse|={lworst:.3e}")
+    return ref_plan, go, gl
+
+
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
 def test_tiny_chunked_matches_oracle_and_one_shot(env, dt):
     """Config 1: 4 steps of (3 decodes + a 16-row chunk), then the same prompt one-shot."""
@@ -159,13 +222,18 @@ def test_mistral_value_one_every_row(env):
     assert err <= 2 ** -8
 
 
-def test_yi_share_sampled(env):
-    """Config 4 at full size: 128 decodes + one 1920-row chunk at 14336, sampled rows."""
+def test_yi_share_every_row(env):
+    """Config 4 at full size: 128 decodes + one 1920-row chunk at 14336 in the fused launch;
+    every one of the 2048 rows (and every appended slot) against the oracle."""
     from chunked_prefill_paged_ca_amd.workload import make_config
+    from tests import harness as H
     ctx, oracle = env
     wl = make_config(4)
-    dec = list(range(0, 128, 8))
-    run_and_check(ctx, oracle, wl, rows_per_seq=48, track=dec + [128], label="yi-share")
+    kc, vc = H.alloc_pool(wl)
+    hist = H.draw_histories(wl, range(wl.n))
+    H.write_history(wl, kc, vc, hist=hist)
+    p, _, _ = run_every_row(ctx, oracle, wl, kc, vc, hist, label="yi-share")
+    assert p["num_decodes"] == 128 and p["num_tokens"] == 2048
 
 
 def test_yi_chunk_alone_whole_blocks(env):
@@ -187,20 +255,22 @@ def test_yi_chunk_alone_whole_blocks(env):
     assert p["num_decodes"] == 0 and p["num_tokens"] == 1920
 
 
-def test_llama70b_share_sampled(env):
-    """Config 5 at full size on a fragmented 128K-page pool: 256 decodes + 3 chunks, sampled
-    requests (the rest of the pool holds device-drawn random values)."""
+def test_llama70b_share_every_row(env):
+    """Config 5 at full size on a fragmented 128K-page pool (unused pages hold device-drawn
+    random values): 256 decodes + chunks 640@0, 512@6000, 128@30000; every one of the 1536 rows
+    (and every appended slot) against the oracle, whose caches are built 32 requests at a time."""
     from chunked_prefill_paged_ca_amd.workload import make_config
     from tests import harness as H
     ctx, oracle = env
     wl = make_config(5)
     kc, vc = H.random_pool(wl, seed=5)
-    track = list(range(0, 256, 16)) + [int(np.argmax(wl.num_computed[:256]))] + [256, 257, 258]
-    H.write_history(wl, kc, vc, track)
-    run_and_check(ctx, oracle, wl, rows_per_seq=24, track=track, pool=(kc, vc), label="70b-share")
+    hist = H.draw_histories(wl, range(wl.n))
+    H.write_history(wl, kc, vc, hist=hist)
+    p, _, _ = run_every_row(ctx, oracle, wl, kc, vc, hist, label="70b-share")
+    assert p["num_decodes"] == 256 and p["num_tokens"] == 1536
 
 
-@pytest.mark.parametrize("c,align", [(64, 0), (512, 0), (2048, 0), (257, 32)])
+@pytest.mark.parametrize("c,align", [(64, 0), (128, 0), (256, 0), (512, 0), (2048, 0), (257, 32)])
 def test_sweep_chunked_vs_one_shot(env, c, align):
     """Config 3: one 8192-token prompt at token budget c (chunks snapped to multiples of `align`
     when set: 257 with 32 gives 32 chunks of 256) against the oracle (sampled rows each step),
@@ -486,6 +556,64 @@ def test_chunk_kernel_shapes(env, hq, hkv, d):
                   stream_len=stream)
     res, _, _ = run_and_check(ctx, oracle, wl, rows_per_seq=24, label=f"chunk-shapes-{hq}/{hkv}/{d}")
     assert res[0][0]["num_decodes"] == 1 and res[0][0]["num_tokens"] == 138
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(64, 2, 128), (32, 1, 64)])
+def test_wide_group_bf16(env, hq, hkv, d):
+    """bf16 with 32 q heads per kv head (wider than one MFMA tile of 16 columns): these shapes
+    run on the plain kernel with its split merge -- decodes of 1, 517 and 2100 keys, a 77-row
+    chunk on 300 cached keys and a 40-row chunk from position 0 -- every row against the
+    oracle."""
+    from chunked_prefill_paged_ca_amd.workload import Workload
+    ctx, oracle = env
+    nc = np.array([0, 516, 2099, 300, 0], np.int32)
+    left = np.array([0, 0, 0, 77, 40], np.int32)
+    stream = np.array([1, 1, 1, 77, 40], np.int32)
+    pool = 512
+    perm = np.random.default_rng(41).permutation(pool).astype(np.int32)
+    tabs, it = [], 0
+    for r in range(5):
+        n = -(-int(nc[r] + stream[r]) // 16)
+        tabs.append(perm[it:it + n]); it += n
+    wl = Workload(name="wide-group", config=0, seed=81, num_q_heads=hq, num_kv_heads=hkv,
+                  head_dim=d, page_size=16, dtype="bf16", token_budget=256, max_chunk=0,
+                  num_pool_pages=pool, num_computed=nc, num_prompt_left=left, block_tables=tabs,
+                  stream_len=stream)
+    res, _, _ = run_and_check(ctx, oracle, wl, label=f"wide-group-{hq}/{hkv}/{d}")
+    assert res[0][0]["num_decodes"] == 3 and res[0][0]["num_tokens"] == 120
+
+
+def test_debug_validate_refuses_colliding_writes(env):
+    """With CA_DEBUG_VALIDATE=1 the append refuses a plan whose block tables make two sequences
+    append to the same page slot, before anything is launched; a context without it runs the
+    range checks only.  A plan first seen with a large pool is refused on a later call with a
+    pool that no longer holds its pages (the cached device copy is not trusted blindly)."""
+    import os
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    ctx, _ = env
+    desc = ca.make_desc(2, 2, 64, 16, "bf16")
+    plan = ca.plan_batch([0, 0], [20, 10], [np.array([3, 5]), np.array([5])], 64, 0, 16, 8)
+    kc = torch.zeros((8, 2, 8, 16, 8), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros((8, 2, 4, 4, 16, 4), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((30, 2, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    os.environ["CA_DEBUG_VALIDATE"] = "1"
+    try:
+        dctx = ca.create(0)
+    finally:
+        del os.environ["CA_DEBUG_VALIDATE"]
+    try:
+        with pytest.raises(ca.CaError, match="both append to page 5 slot 0"):
+            dctx.append_kv_rope(desc, plan, x, y, x, x, kc, vc, 8)
+    finally:
+        dctx.close()
+    ok = ca.plan_batch([0, 0], [20, 10], [np.array([3, 5]), np.array([6])], 64, 0, 16, 8)
+    ctx.append_kv_rope(desc, ok, x, y, x, x, kc, vc, 8)
+    ctx.mixed_attention(desc, ok, y, kc, vc, 8, x)
+    with pytest.raises(ca.CaError, match="outside the pool"):
+        ctx.mixed_attention(desc, ok, y, kc[:6], vc[:6], 6, x)
+    torch.cuda.synchronize()
 
 
 def test_empty_step_is_noop(env):
