@@ -14,7 +14,7 @@ decode-heavy one), or the chunk rows' flops at 2.5 PFLOP/s bf16 MFMA (long prefi
 Its duration comes from HIP events attached to that launch itself on the bench's stream: every
 attention launch of the timed region carries them, and when the timed region has fewer than 50
 steps the same stream of steps continues, still timed, until 50 launches have been timed
-(mean and p10/p50/p90 over all of them).  `scrubbed` repeats 50 steps with a 512 MiB write
+(mean and p10/p50/p90 over all of them).  `scrubbed` repeats 50 steps with a 512 MiB read
 before each (outside the events), so L2 and the MALL hold none of the step's data: cold-HBM
 launch times.
 `traffic` is the HBM bytes the counters measured for that launch (profiles/), used only for the
