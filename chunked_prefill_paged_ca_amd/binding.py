@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.ca_mixed_attention.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
                                          vp, vp, vp, ctypes.c_int64, vp, vp, vp]
+        L.ca_mixed_attention_noalloc.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
+                                                 vp, vp, vp, ctypes.c_int64, vp, vp, vp]
         L.ca_append_kv_rope_packed.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.POINTER(CaPlan),
                                                vp, vp, vp, vp, ctypes.c_int64, vp]
         L.ca_qkv_projection.argtypes = [vp, ctypes.POINTER(CaAttnDesc), ctypes.c_int32, ctypes.c_int32,
@@ -115,7 +117,7 @@ def lib() -> ctypes.CDLL:
         L.ca_sched_free_pages.argtypes = [vp]
         L.ca_sched_free_pages.restype = ctypes.c_int64
         for fn in ("ca_create", "ca_destroy", "ca_plan_batch", "ca_append_kv_rope",
-                   "ca_mixed_attention", "ca_append_kv_rope_packed", "ca_qkv_projection",
+                   "ca_mixed_attention", "ca_mixed_attention_noalloc", "ca_append_kv_rope_packed", "ca_qkv_projection",
                    "ca_plan_validate", "ca_profile_enable", "ca_profile_read", "ca_sched_create",
                    "ca_sched_destroy", "ca_sched_add", "ca_sched_step", "ca_sched_commit",
                    "ca_sched_get"):
@@ -425,7 +427,9 @@ class Context:
         _check(st, "ca_qkv_projection")
 
     def mixed_attention(self, desc: CaAttnDesc, plan: Plan, q, k_cache, v_cache,
-                        num_pool_pages: int, o, lse=None, stream=None):
+                        num_pool_pages: int, o, lse=None, stream=None, no_alloc=False):
+        """ca_mixed_attention, or with no_alloc ca_mixed_attention_noalloc (workspace in the
+        library's static scratch array; nothing allocated)."""
         eb = 2 if desc.dtype == CA_BF16 else 4
         T, hq, hkv, d, P = plan.num_tokens, desc.num_q_heads, desc.num_kv_heads, desc.head_dim, desc.page_size
         for name, t, n, b in (("q", q, T * hq * d, eb), ("o", o, T * hq * d, eb),
@@ -433,10 +437,10 @@ class Context:
                               ("v_cache", v_cache, num_pool_pages * hkv * P * d, eb),
                               ("lse", lse, T * hq, 4)):
             _check_tensor(name, t, n, b)
-        st = lib().ca_mixed_attention(self.h, ctypes.byref(desc), ctypes.byref(plan.c), _ptr(q),
-                                      _ptr(k_cache), _ptr(v_cache), int(num_pool_pages), _ptr(o),
-                                      _ptr(lse), _stream(stream))
-        _check(st, "ca_mixed_attention")
+        fn = lib().ca_mixed_attention_noalloc if no_alloc else lib().ca_mixed_attention
+        st = fn(self.h, ctypes.byref(desc), ctypes.byref(plan.c), _ptr(q), _ptr(k_cache),
+                _ptr(v_cache), int(num_pool_pages), _ptr(o), _ptr(lse), _stream(stream))
+        _check(st, "ca_mixed_attention_noalloc" if no_alloc else "ca_mixed_attention")
 
 
 def create(device: int = 0) -> Context:

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <map>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -31,6 +32,40 @@ void clear_error() { t_last_error.clear(); }
 
 using ca::DevPlan;
 using ca::Shape;
+
+namespace ca {
+// Size of the static scratch array of ca_mixed_attention_noalloc.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}  // namespace ca
+
+// Workspace of ca_mixed_attention_noalloc: the step's metadata and split-KV partials.  One copy
+// per device, held from the library's first use on that device until the process ends, shared
+// by every no-alloc call on the device.  Host code never names it in device work: its device
+// address comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) char scratch[ca::kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` per device, looked up once per device (with that device current).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+}  // namespace
 
 namespace {
 
@@ -216,12 +251,13 @@ struct Profiler {
     int mask = 0;  // CA_PROFILE_* kinds being timed (0: off)
     std::vector<Rec> pending;
     std::vector<hipEvent_t> pool;
-    hipEvent_t get() {
+    hipEvent_t get(bool may_create = true) {
         if (!pool.empty()) {
             hipEvent_t e = pool.back();
             pool.pop_back();
             return e;
         }
+        if (!may_create) return nullptr;
         // Timing events carry no system-scope fence: they only stamp times and are never used
         // to make device memory visible to the host (a fenced event writes back and invalidates
         // the caches around the timed launch, a few microseconds each time).
@@ -262,10 +298,12 @@ struct Timed {
     const char* name;
     ca::LaunchEvents ev{};
     bool committed = false;
-    Timed(Profiler& p, const char* n, int kind) : pf(p), name(n) {
+    // may_create false: events only from the pool created ahead (ca_profile_enable); an empty
+    // pool leaves the launch untimed
+    Timed(Profiler& p, const char* n, int kind, bool may_create = true) : pf(p), name(n) {
         if ((pf.mask & kind) && pf.pending.size() < 65536) {
-            ev.start = pf.get();
-            ev.stop = pf.get();
+            ev.start = pf.get(may_create);
+            ev.stop = pf.get(may_create);
             if (!ev.start || !ev.stop) {
                 if (ev.start) pf.pool.push_back(ev.start);
                 if (ev.stop) pf.pool.push_back(ev.stop);
@@ -332,6 +370,13 @@ struct ca_ctx {
     bool debug_validate = false;
     int32_t work_max_page = -1;     // largest page id of the plan meta_buf holds
     bool work_targets_checked = false;  // its write targets were checked
+    // split partials of the current step (the growable buffers, or the static scratch array)
+    float* dacc = nullptr;
+    float2* dml = nullptr;
+    float* cacc = nullptr;
+    float2* cml = nullptr;
+    void* scratch = nullptr;  // device address of the static scratch array on this ctx's device
+    size_t meta_end = 0;      // bytes of the scratch the current metadata takes
     // host-side work lists of prepare(), kept so that a steady stream of steps reuses them
     std::vector<int4> items, merges, citems, groups, clist;
     std::vector<int32_t> wave_items;
@@ -719,41 +764,12 @@ ca_status ensure_freq(ca_ctx* ctx, const Shape& sh) {
     return CA_OK;
 }
 
-// defer: leave the metadata in its staging slot (ctx->defer_slot) for the append launch that
-// follows to copy; otherwise copy it now with the upload kernel.  writes: the caller appends to
-// the cache (with CA_DEBUG_VALIDATE its write targets are checked).
-ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
-                  hipStream_t stream, bool defer = false, bool writes = false) {
+// The step's work lists on the host, into ctx's reused vectors: decode items in `split` equal
+// shares (with their merges) and chunk workgroups of at most `csplit` keys (with their merges).
+// *slots / *cslots receive the partial slots the decode and chunk splits need.
+void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, int32_t split,
+                 int32_t csplit, int32_t* slots_out, int32_t* cslots_out) {
     const int G = sh.hq / sh.hkv;
-    int32_t dec_wgs = 0;
-    const bool mfma = sh.dtype == CA_BF16 && G <= 16;
-    WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
-                mfma ? decode_shares(ctx, plan, sh, &dec_wgs) : -1,
-                mfma ? chunk_split_keys(ctx, plan, sh, ctx->csplit_override) : -1, sh.theta};
-    const bool check_targets = writes && ctx->debug_validate;
-    if (plan->generation != 0 && key == ctx->work_key) {
-        // the plan was validated when it was first seen, but against that call's pool: its pages
-        // must also lie in this call's
-        if (ctx->work_max_page >= pool) {
-            ca::set_error("page index " + std::to_string(ctx->work_max_page) + " outside the pool");
-            return CA_ERR_INVALID_ARG;
-        }
-        if (check_targets && !ctx->work_targets_checked) {
-            int32_t top = -1;
-            ca_status st = validate_plan_arrays(plan, pool, true, &top);
-            if (st != CA_OK) return st;
-            ctx->work_targets_checked = true;
-        }
-        return CA_OK;
-    }
-    int32_t max_page = -1;
-    ca_status st = validate_plan_arrays(plan, pool, check_targets, &max_page);
-    if (st != CA_OK) return st;
-    ctx->work_key = WorkKey{};  // meta_buf is about to change; nothing matches until it is whole
-    ctx->defer_slot = -1;
-    st = ensure_freq(ctx, sh);
-    if (st != CA_OK) return st;
-
     std::vector<int4>& items = ctx->items;
     std::vector<int4>& merges = ctx->merges;
     std::vector<int4>& citems = ctx->citems;
@@ -769,7 +785,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         // decode: share w holds blocks [B w / W, B (w + 1) / W) of the B blocks of all
         // (decode row, kv head) pairs in order; each pair's run inside a share is one item, and
         // a pair cut over several shares gets one partial slot per piece and a merge
-        const int32_t W = key.split;
+        const int32_t W = split;
         const int64_t B = [&] {
             int64_t b = 0;
             for (int32_t s = 0; s < plan->num_decodes; ++s) {
@@ -811,7 +827,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         while (w < W) wave_items[++w] = static_cast<int32_t>(items.size() / 2);
         // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys);
         // a column is one (row, q head) pair, numbered row * G + head
-        const int32_t Lc = key.csplit;
+        const int32_t Lc = csplit;
         const int32_t cols_per_block = ca::chunk_cols_per_block();
         std::vector<int4>& clist = ctx->clist;
         clist.clear();
@@ -859,22 +875,129 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         if (!clist.empty()) xcd_order<2>(clist, citems);
     }
 
+    *slots_out = slots;
+    *cslots_out = cslots;
+}
+
+// Where prepare() puts a step's device data: the context's growable buffers, or (no_alloc) the
+// library's static scratch array, carved in 256-byte aligned pieces.
+constexpr size_t kScratchAlign = 256;
+size_t align_up(size_t x) { return (x + kScratchAlign - 1) / kScratchAlign * kScratchAlign; }
+
+// defer: leave the metadata in its staging slot (ctx->defer_slot) for the append launch that
+// follows to copy; otherwise copy it now with the upload kernel.  writes: the caller appends to
+// the cache (with CA_DEBUG_VALIDATE its write targets are checked).
+//
+// no_alloc (ca_mixed_attention_noalloc): nothing is allocated.  The metadata goes through a
+// staging slot allocated at ca_create (a plan too large for it is refused) into the static
+// scratch array, followed by the split partials; when the chunk partials would not fit, the
+// chunk key splits are made longer (fewer partial slots) until they do, and a plan whose
+// metadata and decode partials alone exceed the scratch is refused.  The cache of device
+// metadata is bypassed (every call uploads) and invalidated, so the growable buffers' copy is
+// rebuilt by the next ordinary call.
+ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t pool,
+                  hipStream_t stream, bool defer = false, bool writes = false,
+                  bool no_alloc = false) {
+    const int G = sh.hq / sh.hkv;
+    int32_t dec_wgs = 0;
+    const bool mfma = sh.dtype == CA_BF16 && G <= 16;
+    WorkKey key{plan->generation, sh.hq, sh.hkv, sh.d,
+                mfma ? decode_shares(ctx, plan, sh, &dec_wgs) : -1,
+                mfma ? chunk_split_keys(ctx, plan, sh, ctx->csplit_override) : -1, sh.theta};
+    const bool check_targets = writes && ctx->debug_validate;
+    if (!no_alloc && plan->generation != 0 && key == ctx->work_key) {
+        // the plan was validated when it was first seen, but against that call's pool: its pages
+        // must also lie in this call's
+        if (ctx->work_max_page >= pool) {
+            ca::set_error("page index " + std::to_string(ctx->work_max_page) + " outside the pool");
+            return CA_ERR_INVALID_ARG;
+        }
+        if (check_targets && !ctx->work_targets_checked) {
+            int32_t top = -1;
+            ca_status st = validate_plan_arrays(plan, pool, true, &top);
+            if (st != CA_OK) return st;
+            ctx->work_targets_checked = true;
+        }
+        return CA_OK;
+    }
+    int32_t max_page = -1;
+    ca_status st = validate_plan_arrays(plan, pool, check_targets, &max_page);
+    if (st != CA_OK) return st;
+    ctx->work_key = WorkKey{};  // meta_buf is about to change; nothing matches until it is whole
+    ctx->defer_slot = -1;
+    if (!no_alloc) {  // the attention alone never reads the rotary table
+        st = ensure_freq(ctx, sh);
+        if (st != CA_OK) return st;
+    }
+
+    int32_t slots = 0, cslots = 0;
+    build_lists(ctx, plan, sh, mfma, key.split, key.csplit, &slots, &cslots);
+    const std::vector<int4>& items = ctx->items;
+    const std::vector<int4>& merges = ctx->merges;
+    const std::vector<int4>& citems = ctx->citems;
+    const std::vector<int4>& groups = ctx->groups;
+    const std::vector<int32_t>& wave_items = ctx->wave_items;
+    // partial workspace of the MFMA path: decode [slots][G][d] + [slots][G], chunk
+    // [cslots][cols][d] + [cslots][cols] (fp32 and float2)
+    auto partial_bytes = [&](int32_t ds, int32_t cs) {
+        if (!mfma) return size_t(0);
+        const size_t d_ = static_cast<size_t>(ds > 0 ? ds : 1), c_ = static_cast<size_t>(cs > 0 ? cs : 1) * ca::chunk_cols_per_block();
+        return align_up(d_ * G * sh.d * sizeof(float)) + align_up(d_ * G * sizeof(float2)) +
+               align_up(c_ * sh.d * sizeof(float)) + align_up(c_ * sizeof(float2));
+    };
     const int32_t ns = plan->num_seqs;
     const int32_t T = plan->num_tokens;
     const size_t plan_ints = static_cast<size_t>(ns + 1) * 2 + ns + plan->num_pages + 3 * static_cast<size_t>(T);
     const size_t off_items = (plan_ints * sizeof(int32_t) + 15) / 16 * 16;
-    const size_t n_items = items.size() / 2, n_merges = merges.size();
-    const size_t wave_words = (wave_items.size() + 3) / 4 * 4;
-    const size_t off_out = off_items + items.size() * sizeof(int4);
-    const size_t off_merge = off_out + wave_words * sizeof(int32_t);
-    const size_t off_citem = off_merge + n_merges * sizeof(int4);
+    // staged layout after the plan arrays: decode items | first item of each decode wave (padded
+    // to 16 bytes) | decode merges | chunk items | chunk merges
+    auto meta_bytes = [&]() {
+        return (off_items + items.size() * sizeof(int4) + (wave_items.size() + 3) / 4 * 4 * sizeof(int32_t) +
+                merges.size() * sizeof(int4) + citems.size() * sizeof(int4) + groups.size() * sizeof(int4) +
+                16 + 15) / 16 * 16;
+    };
+    size_t bytes = meta_bytes();
+    char* meta_dst = nullptr;
+    char* part_base = nullptr;
+    hipError_t e = hipSuccess;
+    if (no_alloc) {
+        if (!ctx->scratch) { ca::set_error("scratch array unavailable"); return CA_ERR_INTERNAL; }
+        // fewer, longer chunk splits until metadata and partials fit (a split never exceeds the
+        // longest range one chunk workgroup may cover)
+        const int32_t cap_keys = ca::chunk_max_split_keys() / 32 * 32;
+        int32_t Lc = key.csplit;
+        while (mfma && cslots > 0 && align_up(bytes) + partial_bytes(slots, cslots) > ca::kScratchBytes &&
+               Lc < cap_keys) {
+            Lc = Lc * 2 < cap_keys ? Lc * 2 : cap_keys;
+            build_lists(ctx, plan, sh, mfma, key.split, Lc, &slots, &cslots);
+            bytes = meta_bytes();
+        }
+        if (align_up(bytes) + partial_bytes(slots, cslots) > ca::kScratchBytes) {
+            ca::set_error("ca_mixed_attention_noalloc: the step needs " +
+                          std::to_string(align_up(bytes) + partial_bytes(slots, cslots)) +
+                          " bytes of workspace, more than the " + std::to_string(ca::kScratchBytes) +
+                          "-byte scratch array");
+            return CA_ERR_CAPACITY;
+        }
+        meta_dst = static_cast<char*>(ctx->scratch);
+        part_base = meta_dst + align_up(bytes);
+    } else {
+        e = ctx->meta_buf.reserve(bytes, stream);
+        if (e != hipSuccess) return device_error("metadata allocation", e);
+        meta_dst = static_cast<char*>(ctx->meta_buf.ptr);
+    }
+    const size_t off_waves = off_items + items.size() * sizeof(int4);
+    const size_t off_merge = off_waves + (wave_items.size() + 3) / 4 * 4 * sizeof(int32_t);
+    const size_t off_citem = off_merge + merges.size() * sizeof(int4);
     const size_t off_group = off_citem + citems.size() * sizeof(int4);
-    const size_t bytes = (off_group + groups.size() * sizeof(int4) + 16 + 15) / 16 * 16;
-    hipError_t e = ctx->meta_buf.reserve(bytes, stream);
-    if (e != hipSuccess) return device_error("metadata allocation", e);
     int slot = 0;
-    e = ctx->staging.acquire(bytes, &slot);
+    e = ctx->staging.acquire(bytes, &slot, /*may_grow=*/!no_alloc);
     if (e != hipSuccess) return device_error("staging allocation", e);
+    if (slot < 0) {
+        ca::set_error("ca_mixed_attention_noalloc: the step's metadata (" + std::to_string(bytes) +
+                      " bytes) exceeds a staging slot");
+        return CA_ERR_CAPACITY;
+    }
     char* h = static_cast<char*>(ctx->staging.host[slot]);
     int32_t* hp = reinterpret_cast<int32_t*>(h);
     std::memcpy(hp, plan->qo_indptr, sizeof(int32_t) * (ns + 1));
@@ -898,8 +1021,8 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         }
     }
     std::memcpy(h + off_items, items.data(), items.size() * sizeof(int4));
-    std::memcpy(h + off_out, wave_items.data(), wave_items.size() * sizeof(int32_t));
-    std::memcpy(h + off_merge, merges.data(), n_merges * sizeof(int4));
+    std::memcpy(h + off_waves, wave_items.data(), wave_items.size() * sizeof(int32_t));
+    std::memcpy(h + off_merge, merges.data(), merges.size() * sizeof(int4));
     std::memcpy(h + off_citem, citems.data(), citems.size() * sizeof(int4));
     std::memcpy(h + off_group, groups.data(), groups.size() * sizeof(int4));
     const size_t row_pos_off = (static_cast<size_t>(2) * (ns + 1) + ns + plan->num_pages + T) * sizeof(int32_t);
@@ -910,8 +1033,8 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         ctx->hrow_pos = reinterpret_cast<const int32_t*>(hd + row_pos_off);
         ctx->hrow_page = ctx->hrow_pos + T;
     } else {
-        Timed t(ctx->prof, "upload", CA_PROFILE_UPLOAD);
-        e = ctx->staging.upload(slot, ctx->meta_buf.ptr, bytes, stream, t.ev);
+        Timed t(ctx->prof, "upload", CA_PROFILE_UPLOAD, !no_alloc);
+        e = ctx->staging.upload(slot, meta_dst, bytes, stream, t.ev);
         if (e == hipSuccess) t.commit();
         if (e != hipSuccess) {
             ctx->work_key = WorkKey{};
@@ -919,7 +1042,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         }
     }
 
-    const char* d = static_cast<const char*>(ctx->meta_buf.ptr);
+    const char* d = meta_dst;
     const int32_t* dp = reinterpret_cast<const int32_t*>(d);
     ctx->dplan.qo_indptr = dp;
     ctx->dplan.kv_page_indptr = dp + (ns + 1);
@@ -935,28 +1058,45 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     ctx->dplan.page_size = plan->page_size;
     DevWork& w = ctx->dwork;
     w.dec_items = reinterpret_cast<const int4*>(d + off_items);
-    w.dec_wave_items = reinterpret_cast<const int32_t*>(d + off_out);
+    w.dec_wave_items = reinterpret_cast<const int32_t*>(d + off_waves);
     w.merges = reinterpret_cast<const int4*>(d + off_merge);
     w.chunk_items = reinterpret_cast<const int4*>(d + off_citem);
     w.chunk_groups = reinterpret_cast<const int4*>(d + off_group);
-    w.num_dec_items = static_cast<int32_t>(n_items);
+    w.num_dec_items = static_cast<int32_t>(items.size() / 2);
     w.num_dec_waves = wave_items.empty() ? 0 : static_cast<int32_t>(wave_items.size()) - 1;
     w.dec_wgs = dec_wgs;
     w.dec_wpg = ctx->dec_wpg;
-    w.num_merges = static_cast<int32_t>(n_merges);
+    w.num_merges = static_cast<int32_t>(merges.size());
     w.num_slots = slots;
     w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
     w.num_chunk_groups = static_cast<int32_t>(groups.size() / 2);
     w.num_chunk_slots = cslots;
     if (mfma) {
         const size_t dslots = static_cast<size_t>(slots > 0 ? slots : 1);
-        e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
-        if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
         const size_t cslots_sz = static_cast<size_t>(cslots > 0 ? cslots : 1) * ca::chunk_cols_per_block();
-        if (e == hipSuccess) e = ctx->chk_acc_buf.reserve(cslots_sz * sh.d * sizeof(float), stream);
-        if (e == hipSuccess) e = ctx->chk_ml_buf.reserve(cslots_sz * sizeof(float2), stream);
-        if (e != hipSuccess) return device_error("partial allocation", e);
+        if (no_alloc) {
+            char* q = part_base;
+            ctx->dacc = reinterpret_cast<float*>(q);
+            q += align_up(dslots * G * sh.d * sizeof(float));
+            ctx->dml = reinterpret_cast<float2*>(q);
+            q += align_up(dslots * G * sizeof(float2));
+            ctx->cacc = reinterpret_cast<float*>(q);
+            q += align_up(cslots_sz * sh.d * sizeof(float));
+            ctx->cml = reinterpret_cast<float2*>(q);
+        } else {
+            e = ctx->dec_acc_buf.reserve(dslots * G * sh.d * sizeof(float), stream);
+            if (e == hipSuccess) e = ctx->dec_ml_buf.reserve(dslots * G * sizeof(float2), stream);
+            if (e == hipSuccess) e = ctx->chk_acc_buf.reserve(cslots_sz * sh.d * sizeof(float), stream);
+            if (e == hipSuccess) e = ctx->chk_ml_buf.reserve(cslots_sz * sizeof(float2), stream);
+            if (e != hipSuccess) return device_error("partial allocation", e);
+            ctx->dacc = static_cast<float*>(ctx->dec_acc_buf.ptr);
+            ctx->dml = static_cast<float2*>(ctx->dec_ml_buf.ptr);
+            ctx->cacc = static_cast<float*>(ctx->chk_acc_buf.ptr);
+            ctx->cml = static_cast<float2*>(ctx->chk_ml_buf.ptr);
+        }
     }
+    ctx->meta_end = align_up(bytes);  // scratch bytes the metadata takes (no_alloc)
+    if (no_alloc) return CA_OK;        // the scratch copy is not cached
     ctx->work_key = key;
     ctx->work_max_page = max_page;
     ctx->work_targets_checked = check_targets;
@@ -997,7 +1137,13 @@ ca_status ca_create(int device, ca_ctx** out) {
     if (e != hipSuccess) {
         ctx->staging.release();
         delete ctx;
-        return device_error("hipEventCreate", e);
+        return device_error("staging allocation", e);
+    }
+    e = scratch_address(device, &ctx->scratch);
+    if (e != hipSuccess) {
+        ctx->staging.release();
+        delete ctx;
+        return device_error("hipGetSymbolAddress(scratch)", e);
     }
     *out = ctx;
     return CA_OK;
@@ -1144,10 +1290,16 @@ ca_status ca_qkv_projection(ca_ctx* ctx, const ca_attn_desc* desc, int32_t num_t
     return CA_OK;
 }
 
-ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
-                             const void* q, const void* k_cache, const void* v_cache,
-                             int64_t num_pool_pages, void* o, float* lse, void* hip_stream) {
-    ca::clear_error();
+}  // extern "C"
+
+namespace {
+
+// ca_mixed_attention and ca_mixed_attention_noalloc (no_alloc: workspace in the static scratch
+// array, nothing allocated; see prepare()).
+ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         int64_t num_pool_pages, void* o, float* lse, void* hip_stream,
+                         bool no_alloc) {
     if (!ctx) { ca::set_error("null ctx"); return CA_ERR_INVALID_ARG; }
     ca_status st = check_plan(plan);
     if (st != CA_OK) return st;
@@ -1167,16 +1319,16 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess) return device_error("hipSetDevice", g.err);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    st = prepare(ctx, plan, sh, num_pool_pages, stream);
+    st = prepare(ctx, plan, sh, num_pool_pages, stream, /*defer=*/false, /*writes=*/false, no_alloc);
     if (st != CA_OK) return st;
 
     const int G = sh.hq / sh.hkv;
     if (sh.dtype == CA_BF16 && G <= 16) {
         const DevWork& w = ctx->dwork;
-        float* cacc = static_cast<float*>(ctx->chk_acc_buf.ptr);
-        float2* cml = static_cast<float2*>(ctx->chk_ml_buf.ptr);
-        float* dacc = static_cast<float*>(ctx->dec_acc_buf.ptr);
-        float2* dml = static_cast<float2*>(ctx->dec_ml_buf.ptr);
+        float* cacc = ctx->cacc;
+        float2* cml = ctx->cml;
+        float* dacc = ctx->dacc;
+        float2* dml = ctx->dml;
         hipError_t e = hipSuccess;
         // One launch holds both kinds of work (attn_mixed.hip): decode workgroups stream the
         // decode K/V on part of the CUs while chunk workgroups run on the rest.  (Two launches on
@@ -1185,21 +1337,21 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
         // stalled the host between steps.)  CA_SPLIT_ATTENTION=1 runs the parts as two launches
         // of the same kernel, each over the whole device, to time them separately.
         if (!ctx->split_attention) {
-            Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION);
+            Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION, !no_alloc);
             e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
                                      w.num_dec_waves, w.chunk_items, w.num_chunk_items, q, k_cache,
                                      v_cache, dacc, dml, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
         } else {
             if (w.num_chunk_items > 0) {
-                Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION);
+                Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_wpg, w.dec_items, w.dec_wave_items, 0,
                                          w.chunk_items, w.num_chunk_items, q, k_cache, v_cache,
                                          dacc, dml, cacc, cml, o, lse, stream, t.ev);
                 if (e == hipSuccess) t.commit();
             }
             if (e == hipSuccess && w.num_dec_waves > 0) {
-                Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION);
+                Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
                                          w.num_dec_waves, w.chunk_items, 0, q, k_cache, v_cache,
                                          dacc, dml, cacc, cml, o, lse, stream, t.ev);
@@ -1207,7 +1359,7 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
             }
         }
         if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
-            Timed t(ctx->prof, "merge", CA_PROFILE_MERGE);
+            Timed t(ctx->prof, "merge", CA_PROFILE_MERGE, !no_alloc);
             e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
                                  w.num_chunk_groups, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
@@ -1218,17 +1370,52 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
     // fp32 storage, or groups wider than one MFMA tile: the plain kernel serves every row
     const int nsplit = 8;
     const size_t floats = ca::generic_partial_floats(plan->num_tokens, sh, nsplit);
-    hipError_t e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
-    if (e != hipSuccess) return device_error("partials allocation", e);
+    float* partial = nullptr;
+    hipError_t e = hipSuccess;
+    if (no_alloc) {
+        if (ctx->meta_end + floats * sizeof(float) > ca::kScratchBytes) {
+            ca::set_error("ca_mixed_attention_noalloc: the step needs " +
+                          std::to_string(ctx->meta_end + floats * sizeof(float)) +
+                          " bytes of workspace, more than the " + std::to_string(ca::kScratchBytes) +
+                          "-byte scratch array");
+            return CA_ERR_CAPACITY;
+        }
+        partial = reinterpret_cast<float*>(static_cast<char*>(ctx->scratch) + ctx->meta_end);
+    } else {
+        e = ctx->partial_buf.reserve(floats * sizeof(float), stream);
+        if (e != hipSuccess) return device_error("partials allocation", e);
+        partial = static_cast<float*>(ctx->partial_buf.ptr);
+    }
     {
-        Timed t(ctx->prof, "generic", CA_PROFILE_ATTENTION);
+        Timed t(ctx->prof, "generic", CA_PROFILE_ATTENTION, !no_alloc);
         e = ca::launch_attention_generic(ctx->dplan, sh, 0, q, k_cache, v_cache, o, lse,
-                                         static_cast<float*>(ctx->partial_buf.ptr), nsplit, stream,
+                                         partial, nsplit, stream,
                                          t.ev);
         if (e == hipSuccess) t.commit();
     }
     if (e != hipSuccess) return device_error("attention launch", e);
     return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             int64_t num_pool_pages, void* o, float* lse, void* hip_stream) {
+    ca::clear_error();
+    return attention_impl(ctx, desc, plan, q, k_cache, v_cache, num_pool_pages, o, lse, hip_stream,
+                          false);
+}
+
+ca_status ca_mixed_attention_noalloc(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                                     const void* q, const void* k_cache, const void* v_cache,
+                                     int64_t num_pool_pages, void* o, float* lse,
+                                     void* hip_stream) {
+    ca::clear_error();
+    return attention_impl(ctx, desc, plan, q, k_cache, v_cache, num_pool_pages, o, lse, hip_stream,
+                          true);
 }
 
 ca_status ca_plan_validate(const ca_plan* plan, int64_t num_pool_pages, int32_t flags) {

@@ -207,6 +207,30 @@ ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_pla
                              int64_t num_pool_pages, void* o, float* lse, void* hip_stream);
 
 /*
+ * ca_mixed_attention_noalloc -- ca_mixed_attention for callers that cannot allocate memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * same results (within the bf16 / fp32 tolerance of ca_mixed_attention; the chunk rows may be cut
+ * into fewer key splits), and it calls no hipMalloc, hipFree, hipHostMalloc or other allocating
+ * routine:
+ *   - its workspace (the step's metadata and the split-KV partials) is a static device array of
+ *     64 MiB in this library, one per device, held from ca_create on that device until the
+ *     process ends; when the chunk partials would not fit, the chunk rows' key splits are made
+ *     longer until they do;
+ *   - the metadata reaches the device through the pinned staging slots ca_create allocated.
+ * The caller still owns q, the caches, o and lse.  Every no-alloc call on a device shares that
+ * device's array and leaves the last call's contents in it: calls that overlap on one device
+ * (two streams, two contexts, two threads) race; calls on one stream are ordered.  No part of
+ * the array needs to start at zero.  It never reuses or updates the device metadata that
+ * ca_append_kv_rope / ca_mixed_attention keep for a plan (it uploads its own copy every call).
+ * Errors: those of ca_mixed_attention, and CA_ERR_CAPACITY when the step's metadata exceeds a
+ * staging slot (2 MiB) or its metadata and decode partials exceed the 64 MiB array (ca_last_error
+ * gives the size needed).
+ */
+ca_status ca_mixed_attention_noalloc(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
+                                     const void* q, const void* k_cache, const void* v_cache,
+                                     int64_t num_pool_pages, void* o, float* lse, void* hip_stream);
+
+/*
  * Kernel timing (the tracing layer).  When enabled, every launch the library makes carries a
  * start/stop HIP event pair attached to the dispatch itself (hipExtLaunchKernel), so the
  * figures are device time of that launch alone and timing adds no packet to the stream.
