@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libca.so")
-SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "linear.cpp", "linear_skinny.hip", "append_rope.hip",
+SOURCES = ["api.hip", "plan.cpp", "sched.cpp", "linear.cpp", "linear_skinny.hip", "linear_tiled.hip",
+           "append_rope.hip",
            "attn_generic.hip", "attn_mixed.hip", "merge.hip"]
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]  # the QKV projection's GEMM
 PROBE_LIB = os.path.join(PKG, "libca_probe.so")

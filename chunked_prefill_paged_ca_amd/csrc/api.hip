@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
@@ -364,6 +365,8 @@ struct ca_ctx {
     bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
     ca::Linear* linear = nullptr;  // hipBLASLt state of ca_qkv_projection (created on first use)
+    DevBuf proj_part;              // fp32 K-split partials of the tiled projection
+    int32_t proj_tile[3] = {0, 0, 0};  // CA_PROJECTION_TILE=bm,bn,split: tile shape of the tiled projection
     bool projection_library = false;  // CA_PROJECTION_LIBRARY=1: the library GEMM for every T
     // CA_DEBUG_VALIDATE=1: the append also checks that no two scheduled tokens write the same
     // (page, slot) (a sort of the step's write targets on the host).
@@ -1133,6 +1136,14 @@ ca_status ca_create(int device, ca_ctx** out) {
     if (const char* env = std::getenv("CA_CHUNK_SPLIT")) ctx->csplit_override = std::atoi(env);
     if (const char* env = std::getenv("CA_PROJECTION_LIBRARY")) ctx->projection_library = std::atoi(env) != 0;
     if (const char* env = std::getenv("CA_DEBUG_VALIDATE")) ctx->debug_validate = std::atoi(env) != 0;
+    if (const char* env = std::getenv("CA_PROJECTION_TILE")) {
+        int bm = 0, bn = 0, sp = 0;
+        if (std::sscanf(env, "%d,%d,%d", &bm, &bn, &sp) == 3) {
+            ctx->proj_tile[0] = bm;
+            ctx->proj_tile[1] = bn;
+            ctx->proj_tile[2] = sp;
+        }
+    }
     e = ctx->staging.init();
     if (e != hipSuccess) {
         ctx->staging.release();
@@ -1156,6 +1167,7 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->staging.release();
     ctx->meta_buf.release();
     ctx->partial_buf.release();
+    ctx->proj_part.release();
     ctx->dec_acc_buf.release();
     ctx->dec_ml_buf.release();
     ctx->chk_acc_buf.release();
@@ -1277,6 +1289,28 @@ ca_status ca_qkv_projection(ca_ctx* ctx, const ca_attn_desc* desc, int32_t num_t
     // or with CA_PROJECTION_LIBRARY=1, the library GEMM
     if (!ctx->projection_library && ca::skinny_projection_fits(num_tokens, hidden, N)) {
         const hipError_t e = ca::launch_skinny_projection(num_tokens, hidden, N, x, w, qkv, stream, t.ev);
+        if (e != hipSuccess) return device_error("ca_qkv_projection", e);
+        t.commit();
+        return CA_OK;
+    }
+    // beyond 16 tokens: the tiled MFMA kernel (hidden and N multiples of 64)
+    const ca::TiledPlan pl = ctx->projection_library ? ca::TiledPlan{}
+                                                     : ca::plan_tiled_projection(num_tokens, hidden, N, ctx->num_cus);
+    if (pl.ok) {
+        ca::TiledPlan use = pl;
+        if (ctx->proj_tile[0] > 0) {  // a forced shape, if the kernel has it and it divides the problem
+            use.bm = ctx->proj_tile[0];
+            use.bn = ctx->proj_tile[1];
+            use.nsplit = ctx->proj_tile[2];
+            if (!ca::tiled_shape_fits(use, num_tokens, hidden, N)) {
+                ca::set_error("ca_qkv_projection: CA_PROJECTION_TILE does not fit this product");
+                return CA_ERR_INVALID_ARG;
+            }
+        }
+        hipError_t e = ctx->proj_part.reserve(ca::tiled_partial_bytes(use, num_tokens, N), stream);
+        if (e != hipSuccess) return device_error("projection partial allocation", e);
+        e = ca::launch_tiled_projection(use, num_tokens, hidden, N, x, w, qkv,
+                                        static_cast<float*>(ctx->proj_part.ptr), stream, t.ev);
         if (e != hipSuccess) return device_error("ca_qkv_projection", e);
         t.commit();
         return CA_OK;

@@ -85,6 +85,21 @@ bool skinny_projection_fits(int64_t T, int64_t K, int64_t N);
 hipError_t launch_skinny_projection(int64_t T, int64_t K, int64_t N, const void* x, const void* w,
                                     void* out, hipStream_t stream, const LaunchEvents& ev);
 
+// The same product beyond 16 tokens (linear_tiled.hip): an LDS-tiled MFMA GEMM over BM x BN
+// output tiles, with K split over `nsplit` workgroups (fp32 partials, then a fixed-order sum)
+// when the tiles alone would not fill the device.  It takes K a multiple of 64 and N a multiple
+// of 64 (plan.ok false otherwise); partials need tiled_partial_bytes of device memory.
+struct TiledPlan {
+    int bm = 0, bn = 0, nsplit = 0;
+    bool ok = false;
+};
+TiledPlan plan_tiled_projection(int64_t T, int64_t K, int64_t N, int num_cus);
+size_t tiled_partial_bytes(const TiledPlan& pl, int64_t T, int64_t N);
+bool tiled_shape_fits(const TiledPlan& pl, int64_t T, int64_t K, int64_t N);
+hipError_t launch_tiled_projection(const TiledPlan& pl, int64_t T, int64_t K, int64_t N, const void* x,
+                                   const void* w, void* out, float* part, hipStream_t stream,
+                                   const LaunchEvents& ev);
+
 // q_row, kv_row: elements between consecutive token rows of q_in and of k_new / v_new.
 // row_pos, row_page: [num_tokens] per-row position and destination page (device memory or the
 // device-mapped host staging).  meta_n16 > 0: the same launch also copies meta_n16 16-byte units

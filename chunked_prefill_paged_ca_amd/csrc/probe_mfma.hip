@@ -72,6 +72,49 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const uint4* __restric
     out[gid] = acc;
 }
 
+// L2-resident read rate into a CU, by how the data lands: mode 0 / 2 load 16 bytes per lane into
+// registers, mode 1 / 3 copy them straight into LDS (global->LDS DMA).  Modes 0 / 1 read 1 KB
+// contiguous runs; modes 2 / 3 read 8 rows x 128 bytes per instruction with rows 8 KB apart (the
+// tile rows of a GEMM over K = 4096 bf16).  Every wave issues 16 such instructions, then waits for
+// them, `iters` times; all addresses lie in the `window`-byte buffer (a multiple of 64 KB).
+__global__ void __launch_bounds__(256) l2_rate_kernel(const uint4* __restrict__ src, size_t window,
+                                                      int iters, int mode, uint32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint4 lds[4 * 16 * 64];  // 16 KB per wave
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const size_t gw = static_cast<size_t>(blockIdx.x) * 4 + w;
+    const size_t nchunks = window / 1024;
+    const size_t nrows = window / 8192;  // 8 KB rows, a multiple of 8
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        uint4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const size_t c = (gw * 16 + u + static_cast<size_t>(it) * 7) % nchunks;
+            size_t off;  // in 16-byte units
+            if (mode < 2) {
+                off = c * 64 + lane;
+            } else {
+                const size_t row = (c * 8) % nrows + (lane >> 3);
+                const size_t col = ((c * 8) / nrows) % 64;  // 128-byte column of the row
+                off = row * 512 + col * 8 + (lane & 7);
+            }
+            if (mode == 1 || mode == 3)
+                __builtin_amdgcn_global_load_lds(src + off, lds + (w * 16 + u) * 64, 16, 0, 0);
+            else
+                v[u] = src[off];
+        }
+        if (mode == 1 || mode == 3) {
+            __builtin_amdgcn_s_waitcnt(0);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+    }
+    __syncthreads();
+    out[blockIdx.x * 256 + threadIdx.x] = acc ^ lds[threadIdx.x].x;
+}
+
 uint16_t to_bf16(float x) {
     uint32_t u;
     std::memcpy(&u, &x, 4);
@@ -171,5 +214,48 @@ extern "C" int ca_probe_read_rate(size_t bytes, double* gbs) {
     if (out) (void)hipFree(out);
     if (e != hipSuccess) return static_cast<int>(e);
     *gbs = static_cast<double>(n) * 16 / (best * 1e-3) / 1e9;
+    return 0;
+}
+
+// Aggregate read rate (GB/s) of l2_rate_kernel for `mode` over a `window`-byte buffer (>= 64 KB, a
+// multiple of 64 KB; small enough to stay in L2 it measures L2 -> CU delivery), `wgs_per_cu`
+// workgroups of 4 waves per CU; best of 5 timed launches after one warm-up.  Returns 0 or the HIP
+// error code (nothing left allocated).
+extern "C" int ca_probe_l2_rate(int mode, size_t window, int iters, int wgs_per_cu, double* gbs) {
+    if (mode < 0 || mode > 3 || window < 65536 || window % 65536 || iters <= 0 || wgs_per_cu < 1 ||
+        wgs_per_cu > 4 || !gbs)
+        return static_cast<int>(hipErrorInvalidValue);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    const int grid = cus * wgs_per_cu;
+    uint4* src = nullptr;
+    uint32_t* out = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    float best = 1e30f;
+    e = hipMalloc(&src, window);
+    if (e == hipSuccess) e = hipMalloc(&out, static_cast<size_t>(grid) * 256 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(src, 0x5a, window);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    for (int r = 0; r < 6 && e == hipSuccess; ++r) {
+        e = hipEventRecord(e0, nullptr);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(l2_rate_kernel, dim3(grid), dim3(256), 0, nullptr, src, window, iters, mode, out);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e == hipSuccess && r > 0 && ms < best) best = ms;
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (src) (void)hipFree(src);
+    if (out) (void)hipFree(out);
+    if (e != hipSuccess) return static_cast<int>(e);
+    *gbs = static_cast<double>(grid) * 4 * iters * 16 * 1024 / (best * 1e-3) / 1e9;
     return 0;
 }

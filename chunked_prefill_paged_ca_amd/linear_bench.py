@@ -11,7 +11,7 @@ the 256 MB last-level cache), so every call reads its weights from HBM as a real
 step does.  Times are HIP events around each call (CA_PROFILE_PROJECTION), mean of 40 calls.
 
 Prints a markdown table: the path the library takes at that T (the weight-streaming kernel for
-T <= 16, the hipBLASLt GEMM above), time, TFLOP/s, GB/s (algorithmic bytes: weights + x + out),
+T <= 16, the tiled MFMA kernel above), time, TFLOP/s, GB/s (algorithmic bytes: weights + x + out),
 the bound the roofline gives at that T (HBM at 8 TB/s or bf16 MFMA at 2.5 PFLOP/s) and the
 fraction of it reached, the time per token, and the hipBLASLt GEMM's time at the same T
 (a second context created with CA_PROJECTION_LIBRARY=1).
@@ -64,7 +64,7 @@ def main(argv):
     for T in Ts:
         us = time_calls(ctx, T)
         us_lib = time_calls(ctx_lib, T)
-        path = "streaming kernel" if T <= 16 and hidden % 2048 == 0 and N % 32 == 0 else "hipBLASLt"
+        path = "streaming kernel" if T <= 16 and hidden % 2048 == 0 and N % 32 == 0 else "tiled kernel"
         flops = 2.0 * T * hidden * N
         nbytes = 2.0 * (N * hidden + T * hidden + T * N)
         t_hbm, t_mfma = nbytes / HBM, flops / MFMA

@@ -27,6 +27,20 @@ def test_exports_every_header_symbol(L):
         assert hasattr(L, s), s
 
 
+def test_library_leaves_none_of_its_own_symbols_undefined(L):
+    """Every symbol of the library's own namespace is defined in libca.so (a kernel whose host
+    handle was not emitted would otherwise only fail to load on the GPU machine)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    own = [ln for ln in out.splitlines() if "_ZN2ca" in ln or " ca_" in ln]
+    assert own == [], own
+
+
 def test_probe_library_exports_its_entry_point(L):
     """The measurement probe is its own library (not part of the ca_* ABI); it loads without a
     GPU and exports its one C entry point."""

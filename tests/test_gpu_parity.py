@@ -294,13 +294,15 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
-@pytest.mark.parametrize("T,library", [(1, False), (7, False), (16, False), (17, False), (80, False),
-                                       (512, False), (523, False), (1, True)])
+@pytest.mark.parametrize("T,library", [(1, False), (7, False), (16, False), (17, False), (33, False),
+                                       (80, False), (100, False), (256, False), (512, False),
+                                       (523, False), (2048, False), (1, True), (80, True)])
 def test_qkv_projection_matches_oracle(env, T, library):
     """The Mistral-7B q/k/v projection (hidden 4096 -> (32 + 2 x 8) x 128 features) over T
     tokens against the exact product rounded once.  T <= 16 runs the weight-streaming kernel
-    (7: a ragged token tile), larger T -- and T = 1 in a context created with
-    CA_PROJECTION_LIBRARY=1 -- the library GEMM.  The GPU sums K = 4096 exact bf16 products in
+    (7: a ragged token tile), larger T the tiled MFMA kernel (17, 33, 80, 100: K split over
+    several workgroups and summed; 523: a ragged last token block; 2048: many token blocks per
+    weight tile) -- and in a context created with CA_PROJECTION_LIBRARY=1 the library GEMM.  The GPU sums K = 4096 exact bf16 products in
     fp32, whose error is at most K 2^-24 sum_k |x_k w_k| (the standard bound for a K-term
     floating-point sum); the bar is that bound plus one bf16 unit in the last place of the exact
     value.  Away from cancellation this means "equal or the neighbouring bf16 value"; an output
