@@ -76,7 +76,8 @@ def main(argv):
     ctx.close()
     ctx_lib.close()
     print(f"# QKV projection, Mistral-7B shapes (4096 -> 6144, bf16), weights read from HBM\n\n"
-          f"Command (repository root, one MI355X): `python3 -m chunked_prefill_paged_ca_amd.linear_bench`\n")
+          f"Command (repository root, one MI355X): `python3 -m chunked_prefill_paged_ca_amd.linear_bench "
+          f"{' '.join(argv)}`\n")
     print("\n".join(rows))
     return 0
 
