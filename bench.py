@@ -232,7 +232,9 @@ def timed_steps(st, ctx, steps, warmup):
     """Warm-up, then `steps` timed whole steps with every attention launch timed, continued (still
     timed, outside the wall-clock region) until MIN_TIMED_LAUNCHES launches are timed."""
     torch = st.torch
-    st.run(ctx, warmup)
+    # the warm-up steps run exactly like the timed ones (events on every attention launch), so
+    # the timing events are created and the first timed step pays nothing extra
+    st.run(ctx, warmup, time_attention=True)
     torch.cuda.synchronize()
     ctx.profile_read()
     torch.cuda.synchronize()

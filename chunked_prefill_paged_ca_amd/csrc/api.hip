@@ -360,7 +360,7 @@ struct ca_ctx {
     DevBuf chk_ml_buf;      // float2 [slots][cols]
     int32_t num_cus = 0;
     int32_t attn_wgs_per_cu[2] = {0, 0};  // d = 64, d = 128 (queried on first use)
-    int32_t dec_wgs_override = 0;  // CA_DECODE_WGS: decode workgroups of a mixed launch, 0 = auto
+    int32_t dec_wgs_override = 0;  // CA_DECODE_WGS: decode workgroups of an attention launch, 0 = auto
     int32_t dec_wpg = kDecodeWavesPerWg;  // CA_DECODE_WAVES: decode wavefronts per workgroup
     bool split_attention = false;  // CA_SPLIT_ATTENTION=1: decode and chunk as two launches
     int32_t csplit_override = 0;  // CA_CHUNK_SPLIT (keys per chunk split), 0 = automatic
@@ -609,6 +609,8 @@ int32_t decode_shares(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int32_t
                                       : static_cast<int32_t>(slots * mixed_decode_share(ctx, plan, sh));
         n = (n + 7) / 8 * 8;
         if (n > slots) n = slots;
+    } else if (ctx->dec_wgs_override > 0) {
+        n = ctx->dec_wgs_override < slots ? ctx->dec_wgs_override : slots;
     }
     const int32_t per_wg = ctx->dec_wpg;
     const int64_t W = static_cast<int64_t>(n) * per_wg;

@@ -75,8 +75,10 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const uint4* __restric
 // L2-resident read rate into a CU, by how the data lands: mode 0 / 2 load 16 bytes per lane into
 // registers, mode 1 / 3 copy them straight into LDS (global->LDS DMA).  Modes 0 / 1 read 1 KB
 // contiguous runs; modes 2 / 3 read 8 rows x 128 bytes per instruction with rows 8 KB apart (the
-// tile rows of a GEMM over K = 4096 bf16).  Every wave issues 16 such instructions, then waits for
-// them, `iters` times; all addresses lie in the `window`-byte buffer (a multiple of 64 KB).
+// tile rows of a GEMM over K = 4096 bf16); mode 4 loads 8 bytes per lane into registers (512-byte
+// runs, two instructions per KB).  Every wave moves 16 KB per round (16 or 32 instructions), then
+// waits for them, `iters` times; all addresses lie in the `window`-byte buffer (a multiple of
+// 64 KB).
 __global__ void __launch_bounds__(256) l2_rate_kernel(const uint4* __restrict__ src, size_t window,
                                                       int iters, int mode, uint32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint4 lds[4 * 16 * 64];  // 16 KB per wave
@@ -99,10 +101,15 @@ __global__ void __launch_bounds__(256) l2_rate_kernel(const uint4* __restrict__ 
                 const size_t col = ((c * 8) / nrows) % 64;  // 128-byte column of the row
                 off = row * 512 + col * 8 + (lane & 7);
             }
-            if (mode == 1 || mode == 3)
+            if (mode == 1 || mode == 3) {
                 __builtin_amdgcn_global_load_lds(src + off, lds + (w * 16 + u) * 64, 16, 0, 0);
-            else
+            } else if (mode == 4) {
+                const uint2* s2 = reinterpret_cast<const uint2*>(src + c * 64);
+                const uint2 a = s2[lane], b = s2[64 + lane];
+                v[u] = make_uint4(a.x, a.y, b.x, b.y);
+            } else {
                 v[u] = src[off];
+            }
         }
         if (mode == 1 || mode == 3) {
             __builtin_amdgcn_s_waitcnt(0);
@@ -222,7 +229,7 @@ extern "C" int ca_probe_read_rate(size_t bytes, double* gbs) {
 // workgroups of 4 waves per CU; best of 5 timed launches after one warm-up.  Returns 0 or the HIP
 // error code (nothing left allocated).
 extern "C" int ca_probe_l2_rate(int mode, size_t window, int iters, int wgs_per_cu, double* gbs) {
-    if (mode < 0 || mode > 3 || window < 65536 || window % 65536 || iters <= 0 || wgs_per_cu < 1 ||
+    if (mode < 0 || mode > 4 || window < 65536 || window % 65536 || iters <= 0 || wgs_per_cu < 1 ||
         wgs_per_cu > 4 || !gbs)
         return static_cast<int>(hipErrorInvalidValue);
     int dev = 0, cus = 0;

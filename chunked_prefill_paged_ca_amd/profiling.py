@@ -3,7 +3,9 @@
     python -m chunked_prefill_paged_ca_amd.profiling stats <kernel_stats.csv> <title> <command>
         -> markdown table of per-kernel dispatch durations on stdout
     python -m chunked_prefill_paged_ca_amd.profiling trace <kernel_trace.csv> <title> <command>
-        -> markdown table of dispatch durations per (kernel, grid size) on stdout
+           [<kernel substring>:<N>]
+        -> markdown table of dispatch durations per (kernel, grid size) on stdout, and the
+           statistics of the first N dispatches of one kernel
     python -m chunked_prefill_paged_ca_amd.profiling traffic <fetch counter_collection.csv>
            <write counter_collection.csv> <copy MiB> <command> <workload>
         -> JSON: FETCH_SIZE / WRITE_SIZE per attention launch, scaled by what the same counters
@@ -11,6 +13,7 @@
            the workload the counters were taken on (a reading holds for that workload only)
     python -m chunked_prefill_paged_ca_amd.profiling parts <SQ counter_collection.csv>
            <fetch counter_collection.csv> <write counter_collection.csv> <parts_run output> <command>
+           [<stall counter_collection.csv>]
         -> markdown: MFMA utilisation, executed bf16 MFMA flops and HBM bytes of the decode-only
            and chunk-only attention launches of parts_run.py, on stdout
 
@@ -61,27 +64,37 @@ def stats_md(path: str, title: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def trace_md(path: str, title: str, cmd: str) -> str:
+def trace_md(path: str, title: str, cmd: str, first: str = "") -> str:
     """Per-dispatch durations from a rocprofv3 kernel_trace.csv, grouped by kernel AND grid size:
     one bench run launches the same kernel for several workloads (different grids), and each
-    workload's launches are averaged on their own."""
+    workload's launches are averaged on their own.  first = "<kernel substring>:<N>" adds the
+    statistics of the first N dispatches of that kernel (e.g. the launches the bench's roofline
+    line timed, which come first in its run)."""
     rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     gcols = [c for c in ("Grid_Size_X", "Grid_Size") if rows and c in rows[0]]
     groups = defaultdict(list)
-    first = {}
+    first_at = {}
     for i, r in enumerate(rows):
         grid = int(r[gcols[0]]) if gcols else 0
         key = (short_name(r["Kernel_Name"]), grid)
         groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        first.setdefault(key, i)
+        first_at.setdefault(key, i)
     out = [f"# {title}", "", "Command (run from the repository root on one MI355X; TMPDIR=/tmp):", "",
            f"    {cmd}", "", "rocprofv3 kernel trace, grouped by kernel and grid size (work-items), "
            "in order of first dispatch:", "",
            "| kernel | grid | calls | avg us | p10 us | p50 us | p90 us |", "|---|---|---|---|---|---|---|"]
-    for key in sorted(groups, key=lambda k: first[k]):
+    for key in sorted(groups, key=lambda k: first_at[k]):
         v = np.asarray(groups[key])
         out.append(f"| {key[0][:70]} | {key[1]} | {v.size} | {v.mean():.2f} | "
                    f"{np.percentile(v, 10):.2f} | {np.percentile(v, 50):.2f} | {np.percentile(v, 90):.2f} |")
+    if first:
+        sub, n = first.rsplit(":", 1)
+        v = np.asarray([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+                        if sub in r["Kernel_Name"]][:int(n)])
+        out += ["", f"The first {v.size} dispatches of `{sub}` (in this run, the launches the bench's "
+                f"roofline line timed): avg {v.mean():.2f} us, p10 {np.percentile(v, 10):.2f}, "
+                f"p50 {np.percentile(v, 50):.2f}, p90 {np.percentile(v, 90):.2f} us."]
     return "\n".join(out) + "\n"
 
 
@@ -132,7 +145,12 @@ SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8
 
 
-def parts(sq_csv: str, fetch_csv: str, write_csv: str, timing: dict, cmd: str) -> str:
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                  "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS")
+
+
+def parts(sq_csv: str, fetch_csv: str, write_csv: str, timing: dict, cmd: str,
+          stall_csv: str = "") -> str:
     """Counters of the decode-only and chunk-only attention launches of parts_run.py.
 
     The attention dispatches alternate in launch order (timing["attention_launch_order"]).
@@ -181,6 +199,25 @@ def parts(sq_csv: str, fetch_csv: str, write_csv: str, timing: dict, cmd: str) -
     for kind, us, util, mops, tf, rd, wr, gbs, _ in rows:
         out.append(f"| {kind} | {us:.1f} | {100 * util:.1f} % | {mops / 1e9:.1f} G | {tf:.0f} | "
                    f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {gbs:.0f} |")
+    if stall_csv:
+        st = attention(_instances(stall_csv))
+        out += ["", "Where the waves' time goes (a fourth counter pass; each SQ counter summed over its "
+                "instances and averaged over the launches of each kind; shares are of SQ_WAVE_CYCLES, the "
+                "summed residency of every wave, in the same units as the per-wave ACTIVE_INST and "
+                "WAIT_INST counters):", "",
+                "| launch | issuing VALU | issuing LDS | waiting on any dependency | waiting on LDS | "
+                "LDS instructions | LDS bank-conflict cycles |", "|---|---|---|---|---|---|---|"]
+        for kind in order:
+            vs = st[kind]
+
+            def mean(c):
+                return float(np.mean([sum(v[c]) for v in vs if c in v])) if vs and c in vs[0] else float("nan")
+            wave = mean("SQ_WAVE_CYCLES")
+            out.append(f"| {kind} | {100 * mean('SQ_ACTIVE_INST_VALU') / wave:.1f} % | "
+                       f"{100 * mean('SQ_ACTIVE_INST_LDS') / wave:.1f} % | "
+                       f"{100 * mean('SQ_WAIT_INST_ANY') / wave:.1f} % | "
+                       f"{100 * mean('SQ_WAIT_INST_LDS') / wave:.1f} % | {mean('SQ_INSTS_LDS') / 1e6:.2f} M | "
+                       f"{mean('SQ_LDS_BANK_CONFLICT') / 1e6:.3f} M |")
     ca = timing["chunk_alg_flops"]
     out += ["", f"Algorithmic work: decode rows {timing['decode_alg_bytes'] / 1e6:.1f} MB "
             f"({timing['decode_alg_bytes'] / (ms['decode'] * 1e-3) / 1e9:.0f} GB/s over the decode launch, "
@@ -194,9 +231,10 @@ def parts(sq_csv: str, fetch_csv: str, write_csv: str, timing: dict, cmd: str) -
 def main(argv):
     if len(argv) >= 6 and argv[0] == "parts":
         timing = json.loads(open(argv[4]).read().strip().splitlines()[-1])
-        sys.stdout.write(parts(argv[1], argv[2], argv[3], timing, argv[5]))
+        sys.stdout.write(parts(argv[1], argv[2], argv[3], timing, argv[5],
+                               argv[6] if len(argv) > 6 else ""))
     elif len(argv) >= 4 and argv[0] == "trace":
-        sys.stdout.write(trace_md(argv[1], argv[2], argv[3]))
+        sys.stdout.write(trace_md(argv[1], argv[2], argv[3], argv[4] if len(argv) > 4 else ""))
     elif len(argv) >= 4 and argv[0] == "stats":
         sys.stdout.write(stats_md(argv[1], argv[2], argv[3]))
     elif len(argv) >= 6 and argv[0] == "traffic":

@@ -119,7 +119,7 @@ typedef struct ca_ctx ca_ctx;
  * Create a context bound to HIP device `device`.  *out receives the handle.
  * The launch shape is chosen per call from the plan and the device's CU count.  For measurement,
  * ca_create reads these overrides from the environment (unset = the default choice):
- *   CA_DECODE_WGS=n         decode workgroups of the fused attention launch;
+ *   CA_DECODE_WGS=n         decode workgroups of an attention launch (fused, or decode rows alone);
  *   CA_DECODE_WAVES=n       waves per decode workgroup, 1..8 (default 4);
  *   CA_CHUNK_SPLIT=n        keys per prefill-chunk split (rounded up to 32 and to at least
  *                           1/64 of the longest chunk row's keys);
