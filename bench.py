@@ -158,13 +158,13 @@ class Step:
         self.stream = torch.cuda.current_stream()
         self.scrub_buf = None
 
-    def run(self, ctx, n, time_attention=False, scrub=False):
-        """n whole steps (plan, append, attention); with time_attention every attention launch
-        carries timing events; with scrub a 512 MiB read precedes every step."""
+    def run(self, ctx, n, time_attention=False, scrub=False, every=1):
+        """n whole steps (plan, append, attention); with time_attention every `every`-th attention
+        launch carries timing events; with scrub a 512 MiB read precedes every step."""
         wl = self.wl
         if scrub and self.scrub_buf is None:
             self.scrub_buf = self.torch.ones(SCRUB_MIB << 18, dtype=self.torch.float32, device="cuda")
-        for _ in range(n):
+        for i in range(n):
             if scrub:
                 # a read of 512 MiB evicts the step's data from L2 and the MALL and leaves
                 # clean lines (a write would leave dirty ones for the next launch to write back)
@@ -172,11 +172,12 @@ class Step:
             plan = self.batch.plan()
             ctx.append_kv_rope(self.desc, plan, self.q_in, self.q_rot, self.k_in, self.v_in, self.kc,
                                self.vc, wl.num_pool_pages, stream=self.stream)
-            if time_attention:
+            timed = time_attention and every > 0 and i % every == 0
+            if timed:
                 ctx.profile_enable(self.ca.PROFILE_ATTENTION)
             ctx.mixed_attention(self.desc, plan, self.q_rot, self.kc, self.vc, wl.num_pool_pages,
                                 self.o, self.lse, stream=self.stream)
-            if time_attention:
+            if timed:
                 ctx.profile_enable(False)
 
     def parts(self, warmup, steps):
@@ -228,9 +229,10 @@ def attention_times(recs):
     return name, np.array([ms for n, ms in recs if n == name])
 
 
-def timed_steps(st, ctx, steps, warmup):
-    """Warm-up, then `steps` timed whole steps with every attention launch timed, continued (still
-    timed, outside the wall-clock region) until MIN_TIMED_LAUNCHES launches are timed."""
+def timed_steps(st, ctx, steps, warmup, every=1):
+    """Warm-up, then `steps` timed whole steps with every `every`-th attention launch timed (0:
+    none), continued outside the wall-clock region (every launch timed) until MIN_TIMED_LAUNCHES
+    launches are timed."""
     torch = st.torch
     # the warm-up steps run exactly like the timed ones (events on every attention launch), so
     # the timing events are created and the first timed step pays nothing extra
@@ -239,17 +241,21 @@ def timed_steps(st, ctx, steps, warmup):
     ctx.profile_read()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    st.run(ctx, steps, time_attention=True)
+    st.run(ctx, steps, time_attention=True, every=every)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     in_region = ctx.profile_read()
+    n_region = sum(1 for n, _ in in_region if n in ("attention", "generic"))
     extra = []
-    if steps < MIN_TIMED_LAUNCHES:
-        st.run(ctx, MIN_TIMED_LAUNCHES - steps, time_attention=True)
+    if n_region < MIN_TIMED_LAUNCHES:
+        st.run(ctx, MIN_TIMED_LAUNCHES - n_region, time_attention=True)
         torch.cuda.synchronize()
         extra = ctx.profile_read()
-    name, region_ms = attention_times(in_region)
-    _, extra_ms = attention_times(extra) if extra else (name, np.zeros(0))
+    name, region_ms = attention_times(in_region) if in_region else ("attention", np.zeros(0))
+    if extra:
+        name, extra_ms = attention_times(extra)
+    else:
+        extra_ms = np.zeros(0)
     all_ms = np.concatenate([region_ms, extra_ms])
     return elapsed, name, region_ms, all_ms
 
@@ -358,6 +364,9 @@ def main():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the Yi-34B, LLaMA2-70B and Llama-13B sweep legs")
     ap.add_argument("--no-scrub", action="store_true", help="skip the cold-HBM (scrubbed) pass")
+    ap.add_argument("--time-every", type=int, default=1,
+                    help="attach timing events to every N-th attention launch of the timed region "
+                         "(0: none; the launches timed after the region make up the 50)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip re-measuring the HBM and bf16 GEMM rates this device sustains")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -383,11 +392,12 @@ def main():
 
     # ---- timed region: whole steps; every attention launch carries timing events ----
     ctx = ca.create(0)
-    elapsed, attn_name, region_ms, all_ms = timed_steps(st, ctx, args.steps, args.warmup)
+    elapsed, attn_name, region_ms, all_ms = timed_steps(st, ctx, args.steps, args.warmup,
+                                                        every=args.time_every)
     ms_per_step = elapsed * 1e3 / args.steps
     value = st.T * args.steps / elapsed
     attn_ms = float(np.mean(all_ms))
-    launches = args.warmup + args.steps + max(0, MIN_TIMED_LAUNCHES - args.steps)
+    launches = args.warmup + args.steps + max(0, MIN_TIMED_LAUNCHES - int(region_ms.size))
     out = {
         "metric": "mixed chunked-prefill+decode attn tokens/s; % HBM peak and % MFMA peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -404,7 +414,8 @@ def main():
                      "launch_ms_p10_p50_p90": pct(all_ms),
                      "launches_timed": int(all_ms.size),
                      "launches_in_timed_region": int(region_ms.size),
-                     "launch_ms_timed_region_mean": round(float(np.mean(region_ms)), 5),
+                     "launch_ms_timed_region_mean": (round(float(np.mean(region_ms)), 5)
+                                                     if region_ms.size else None),
                      "attention_launches_this_leg": launches},
     }
     if not args.no_scrub:
