@@ -549,7 +549,7 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_tar
 // becomes the tail).
 constexpr double kMaxDecodeShare = 0.75;
 constexpr double kMinDecodeShare = 0.3125;
-constexpr double kDecodeStreamBps = 5.5e12;  // decode K/V read rate the estimates assume
+constexpr double kDecodeStreamBps = 6.3e12;  // decode K/V read rate the estimates assume
 double chunk_block_us(const Shape& sh) { return sh.d == 128 ? 1.3 : 0.67; }
 
 // Decode K/V stream time (us) and chunk CU-time (CU-us) of a plan, as the launch-shaping rules

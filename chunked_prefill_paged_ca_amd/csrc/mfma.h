@@ -54,6 +54,28 @@ __device__ __forceinline__ bf16x8 load_frag_pair(const uint16_t* a, const uint16
     return r;
 }
 
+// The same loads with the non-temporal hint, for data read exactly once (the decode rows' K/V
+// stream): measured on the part, a plain read stream runs ~10 % faster with it (6.1 -> 6.7 TB/s
+// over 800 MiB), since the lines it brings in are not kept in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 load_frag_nt(const uint16_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 load_frag_pair_nt(const uint16_t* a, const uint16_t* b) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a));
+    const u32x2 y = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(b));
+    const u32x4 v = {x.x, x.y, y.x, y.y};
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
 // Zero fragment elements by key: element j < 4 is kept when j < va, element 4 + j when j < vb
 // (va, vb: keys of the lane's page-a and page-b runs that are inside the range).
 __device__ __forceinline__ bf16x8 mask_frag(bf16x8 f, int va, int vb) {
