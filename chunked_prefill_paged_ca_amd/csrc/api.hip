@@ -241,6 +241,9 @@ struct DevWork {
     int32_t dec_wgs = 0;  // decode workgroups of the attention launch
     int32_t dec_wpg = 0;  // decode wavefronts per decode workgroup
     int32_t num_chunk_items = 0, num_chunk_groups = 0, num_chunk_slots = 0;
+    int32_t num_chunk_workers = 0;  // chunk workgroups of the attention launch
+    int32_t num_chunk_static = 0;   // of those, the ones that start with the launch
+    bool chunk_queue_mode = false;  // workers take items from queues (else one item each)
 };
 
 // Event pairs around the library's own launches (ca_profile_enable).
@@ -339,6 +342,7 @@ struct ca_ctx {
     Profiler prof;
     Staging staging;
     DevBuf meta_buf;        // one upload per step: plan metadata, then the work lists
+    int* queue = nullptr;   // chunk work-queue counters of the attention launch (zero between launches)
     DevPlan dplan{};
     const double* inv_freq = nullptr;  // [d / 2] rotary inverse frequencies of the current shape
     // one device table of inverse frequencies per (head dim, rotary base), filled once and kept
@@ -382,6 +386,9 @@ struct ca_ctx {
     size_t meta_end = 0;      // bytes of the scratch the current metadata takes
     // host-side work lists of prepare(), kept so that a steady stream of steps reuses them
     std::vector<int4> items, merges, citems, groups, clist;
+    std::vector<int32_t> corder;
+    int32_t chunk_workers = 0, chunk_static = 0;  // the chunk workers of the last work lists
+    bool chunk_queue_mode = false;
     std::vector<int32_t> wave_items;
 };
 
@@ -773,7 +780,7 @@ ca_status ensure_freq(ca_ctx* ctx, const Shape& sh) {
 // shares (with their merges) and chunk workgroups of at most `csplit` keys (with their merges).
 // *slots / *cslots receive the partial slots the decode and chunk splits need.
 void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, int32_t split,
-                 int32_t csplit, int32_t* slots_out, int32_t* cslots_out) {
+                 int32_t csplit, int32_t dec_wgs, int32_t* slots_out, int32_t* cslots_out) {
     const int G = sh.hq / sh.hkv;
     std::vector<int4>& items = ctx->items;
     std::vector<int4>& merges = ctx->merges;
@@ -833,7 +840,57 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
         // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys);
         // a column is one (row, q head) pair, numbered row * G + head
         const int32_t Lc = csplit;
+        // A column block's split i covers keys [i Lc, (i + 1) Lc), the last one the remainder.
+        // In queue mode (below) a block whose remainder would be longer than Lt = Lc / 4 gets a
+        // last piece of Lt keys instead and its other pieces share the rest evenly (each at most
+        // the split cap): the queues hand out the short pieces last, so the launch ends on a
+        // round of short items rather than on whichever full-length items started last.
+        const int32_t Lt = ((Lc / 4 + 31) / 32) * 32;
+        const int32_t cap = ca::chunk_max_split_keys() / 32 * 32;
+        auto piece = [&](int32_t key_end, int32_t nsplit, bool short_tail, int32_t i, int32_t* kb, int32_t* ke) {
+            if (!short_tail) {
+                *kb = i * Lc;
+                *ke = (*kb + Lc < key_end) ? *kb + Lc : key_end;
+                return;
+            }
+            const int32_t ts = (key_end - Lt) / 32 * 32;  // the short piece's first key
+            auto at = [&](int32_t j) { return static_cast<int32_t>(static_cast<int64_t>(ts / 32) * j / (nsplit - 1)) * 32; };
+            *kb = i < nsplit - 1 ? at(i) : ts;
+            *ke = i < nsplit - 1 ? at(i + 1) : key_end;
+        };
+        auto has_short_tail = [&](int32_t key_end, int32_t nsplit) {
+            if (nsplit < 2) return false;
+            const int32_t r = key_end - (nsplit - 1) * Lc;
+            const int32_t ts = (key_end - Lt) / 32 * 32;
+            return r > Lt && ts / (nsplit - 1) + 32 <= cap;
+        };
         const int32_t cols_per_block = ca::chunk_cols_per_block();
+        // How the attention launch's chunk workers take the items (attn_mixed.hip).  If every
+        // item fits on the workgroup slots free when the launch starts, one worker per item
+        // (direct mode), the list in XCD order.  Otherwise one persistent worker per workgroup
+        // slot of the device (queue mode): the workers on the slots the decode workgroups leave
+        // start at once, the others as the decode drains, and each takes items until none is
+        // left.  Measured on the part (Yi-34B step, 1096 items): with one workgroup per item the
+        // in-order dispatcher left a tenth of the chunk CUs idle behind busy XCDs and the launch
+        // ended on ~100 us of straggling full-length items; queue mode took the fused launch
+        // 580 -> 553 us (LLaMA2-70B step 1221 -> 1170 us).
+        const int32_t per_cu = ctx->attn_wgs_per_cu[sh.d == 128 ? 1 : 0];
+        const int32_t wslots = ctx->num_cus * (per_cu > 0 ? per_cu : 1);
+        const bool fused = dec_wgs > 0 && plan->num_decodes > 0 && !ctx->split_attention;
+        const int32_t early = fused ? (wslots > dec_wgs ? wslots - dec_wgs : 0) : wslots;
+        int64_t n_items = 0;
+        for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+            const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+            const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+            const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+            const int32_t ncols = q_len * G;
+            for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+                const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+                n_items += (kv_len - q_len + last / G + 1 + Lc - 1) / Lc;
+            }
+        }
+        n_items *= sh.hkv;
+        const bool queue_mode = n_items > early;
         std::vector<int4>& clist = ctx->clist;
         clist.clear();
         for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
@@ -868,7 +925,8 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
                         const int32_t key_end = kv_len - q_len + last / G + 1;
                         const int32_t nsplit = (key_end + Lc - 1) / Lc;
                         if (i < nsplit) {
-                            const int32_t kb = i * Lc, ke = (kb + Lc < key_end) ? kb + Lc : key_end;
+                            int32_t kb, ke;
+                            piece(key_end, nsplit, queue_mode && has_short_tail(key_end, nsplit), i, &kb, &ke);
                             clist.push_back(make_int4(s, g, cb, nsplit == 1 ? -1 : slot + i));
                             clist.push_back(make_int4(kb, ke, 0, 0));
                         }
@@ -877,7 +935,39 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
                 }
             }
         }
-        if (!clist.empty()) xcd_order<2>(clist, citems);
+        // Queue mode: the list forms eight queues, one per XCD (queue x: the x-th eighth of
+        // the list), each with its longer items first and the rest in list order (key range by
+        // key range), so that the last items taken are the short pieces.
+        const size_t n = clist.size() / 2;
+        if (n == 0) {
+            citems.clear();
+            ctx->chunk_workers = ctx->chunk_static = 0;
+            ctx->chunk_queue_mode = false;
+        } else if (!queue_mode) {
+            const int32_t grid = xcd_order<2>(clist, citems);
+            ctx->chunk_workers = grid;
+            ctx->chunk_static = grid;
+            ctx->chunk_queue_mode = false;
+        } else {
+            const size_t per = (n + 7) / 8;
+            citems.resize(clist.size());
+            std::vector<int32_t>& order = ctx->corder;
+            for (size_t x0 = 0; x0 < n; x0 += per) {
+                const size_t x1 = x0 + per < n ? x0 + per : n;
+                order.resize(x1 - x0);
+                for (size_t i = x0; i < x1; ++i) order[i - x0] = static_cast<int32_t>(i);
+                std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+                    return clist[2 * a + 1].y - clist[2 * a + 1].x > clist[2 * b + 1].y - clist[2 * b + 1].x;
+                });
+                for (size_t i = x0; i < x1; ++i) {
+                    citems[2 * i] = clist[2 * order[i - x0]];
+                    citems[2 * i + 1] = clist[2 * order[i - x0] + 1];
+                }
+            }
+            ctx->chunk_workers = wslots;
+            ctx->chunk_static = early;
+            ctx->chunk_queue_mode = true;
+        }
     }
 
     *slots_out = slots;
@@ -936,7 +1026,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     }
 
     int32_t slots = 0, cslots = 0;
-    build_lists(ctx, plan, sh, mfma, key.split, key.csplit, &slots, &cslots);
+    build_lists(ctx, plan, sh, mfma, key.split, key.csplit, dec_wgs, &slots, &cslots);
     const std::vector<int4>& items = ctx->items;
     const std::vector<int4>& merges = ctx->merges;
     const std::vector<int4>& citems = ctx->citems;
@@ -974,7 +1064,7 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         while (mfma && cslots > 0 && align_up(bytes) + partial_bytes(slots, cslots) > ca::kScratchBytes &&
                Lc < cap_keys) {
             Lc = Lc * 2 < cap_keys ? Lc * 2 : cap_keys;
-            build_lists(ctx, plan, sh, mfma, key.split, Lc, &slots, &cslots);
+            build_lists(ctx, plan, sh, mfma, key.split, Lc, dec_wgs, &slots, &cslots);
             bytes = meta_bytes();
         }
         if (align_up(bytes) + partial_bytes(slots, cslots) > ca::kScratchBytes) {
@@ -1074,6 +1164,9 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     w.num_merges = static_cast<int32_t>(merges.size());
     w.num_slots = slots;
     w.num_chunk_items = static_cast<int32_t>(citems.size() / 2);
+    w.num_chunk_workers = ctx->chunk_workers;
+    w.num_chunk_static = ctx->chunk_static;
+    w.chunk_queue_mode = ctx->chunk_queue_mode;
     w.num_chunk_groups = static_cast<int32_t>(groups.size() / 2);
     w.num_chunk_slots = cslots;
     if (mfma) {
@@ -1158,6 +1251,16 @@ ca_status ca_create(int device, ca_ctx** out) {
         delete ctx;
         return device_error("hipGetSymbolAddress(scratch)", e);
     }
+    // the chunk work-queue counters start at zero; each attention launch leaves them at zero
+    e = hipMalloc(&ctx->queue, 16 * sizeof(int));
+    if (e == hipSuccess) e = hipMemset(ctx->queue, 0, 16 * sizeof(int));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        if (ctx->queue) (void)hipFree(ctx->queue);
+        ctx->staging.release();
+        delete ctx;
+        return device_error("work-queue allocation", e);
+    }
     *out = ctx;
     return CA_OK;
 }
@@ -1175,6 +1278,7 @@ ca_status ca_destroy(ca_ctx* ctx) {
     ctx->chk_acc_buf.release();
     ctx->chk_ml_buf.release();
     ctx->prof.release();
+    if (ctx->queue) (void)hipFree(ctx->queue);
     for (auto& kv : ctx->freq_tables) (void)hipFree(kv.second);
     ca::linear_release(ctx->linear);
     delete ctx;
@@ -1375,22 +1479,27 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
         if (!ctx->split_attention) {
             Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION, !no_alloc);
             e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
-                                     w.num_dec_waves, w.chunk_items, w.num_chunk_items, q, k_cache,
-                                     v_cache, dacc, dml, cacc, cml, o, lse, stream, t.ev);
+                                     w.num_dec_waves, w.chunk_items, w.num_chunk_items,
+                                     w.num_chunk_workers, w.num_chunk_static, w.chunk_queue_mode,
+                                     ctx->queue, q, k_cache, v_cache, dacc, dml, cacc, cml, o, lse,
+                                     stream, t.ev);
             if (e == hipSuccess) t.commit();
         } else {
             if (w.num_chunk_items > 0) {
                 Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_wpg, w.dec_items, w.dec_wave_items, 0,
-                                         w.chunk_items, w.num_chunk_items, q, k_cache, v_cache,
-                                         dacc, dml, cacc, cml, o, lse, stream, t.ev);
+                                         w.chunk_items, w.num_chunk_items, w.num_chunk_workers,
+                                         w.num_chunk_static, w.chunk_queue_mode, ctx->queue, q,
+                                         k_cache, v_cache, dacc, dml, cacc, cml, o, lse, stream,
+                                         t.ev);
                 if (e == hipSuccess) t.commit();
             }
             if (e == hipSuccess && w.num_dec_waves > 0) {
                 Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
-                                         w.num_dec_waves, w.chunk_items, 0, q, k_cache, v_cache,
-                                         dacc, dml, cacc, cml, o, lse, stream, t.ev);
+                                         w.num_dec_waves, w.chunk_items, 0, 0, 0, false, ctx->queue, q,
+                                         k_cache, v_cache, dacc, dml, cacc, cml, o, lse, stream,
+                                         t.ev);
                 if (e == hipSuccess) t.commit();
             }
         }

@@ -7,13 +7,25 @@
 // arithmetic (a prefill chunk reuses every K/V block for all its query rows), so the two kinds
 // of work can run on the chip at the same time instead of one after the other.
 //
-// The grid is [dec_wgs decode workgroups][chunk workgroups].  Workgroups are dispatched in index
+// The grid is [dec_wgs decode workgroups][chunk workers].  Workgroups are dispatched in index
 // order, so the decode workgroups (dec_wpg wavefronts each, every wave streaming its equal share
 // of the decode K/V blocks, attn_decode.h) start first and stay resident on dec_wgs CUs until their
-// shares are done; the chunk workgroups (attn_chunk.h) run on the remaining CUs from the start
-// and take over the decode CUs as those drain.  Decode reaches the HBM bandwidth on a fraction of
+// shares are done; the chunk workers (attn_chunk.h) run on the remaining CUs from the start and
+// take over the decode CUs as those drain.  Decode reaches the HBM bandwidth on a fraction of
 // the CUs, so the chunk work fills CUs the decode stream does not need.  Either part may be
 // empty.
+//
+// Chunk workers run in one of two modes.  Direct: worker w runs chunk item w (every item fits
+// on the CUs free at the start).  Queue: one persistent worker per workgroup slot of the device;
+// the items form eight queues, queue x (items [x per, x per + size(x)), per = ceil(n / 8)) for
+// the workers on XCD x (workgroups are dealt to the XCDs round robin, so the workgroups that run
+// side by side on one XCD share their K/V pages in its L2).  The first items of each queue go
+// one each to the workers that start with the launch, without atomics; after that a worker
+// claims items through the queue's counter (a device-scope atomic add in `queue[x]`), its own
+// XCD's queue first, then the others, and leaves when all are empty.  No worker ever waits for
+// another, so every worker ends.  queue[8] counts the workers that have left; the last one sets
+// all nine counters back to zero, so each launch finds them cleared without a separate
+// clearing launch or memset (the counters are zeroed once when the context is created).
 
 #include <hip/hip_runtime.h>
 
@@ -31,6 +43,8 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
     DevPlan p, int dec_wgs, int dec_wpg, const int4* __restrict__ dec_items,
     const int32_t* __restrict__ wave_items, int num_waves, const int4* __restrict__ chunk_items,
+    int num_chunk_items, int num_workers, int num_static, bool queue_mode,
+    int* __restrict__ queue,
     const uint16_t* __restrict__ qg,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
     float scale_log2, float* __restrict__ dec_acc, float2* __restrict__ dec_ml,
@@ -54,8 +68,55 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
                                    lane);
         return;
     }
-    chunk::chunk_item<D>(blockIdx.x - dec_wgs, p, chunk_items, qg, k_cache, v_cache, hq, hkv,
-                         scale_log2, chunk_acc, chunk_ml, o, lse);
+    // Chunk worker (direct or queue mode, see the top of this file)
+    __shared__ int s_item;
+    const int w = blockIdx.x - dec_wgs;
+    const int x = w & 7;  // this worker's XCD: workgroups are dealt to the XCDs round robin
+    const int per = (num_chunk_items + 7) >> 3;
+    auto qsize = [&](int qx) { return max(0, min(per, num_chunk_items - qx * per)); };
+    auto qstatic = [&](int qx) { return min(max(0, (num_static - qx + 7) >> 3), qsize(qx)); };
+    auto take = [&](int qx, int i) {
+        const int k = qstatic(qx) + i;
+        return k < qsize(qx) ? qx * per + k : -1;
+    };
+    auto claim = [&]() -> int {  // thread 0
+        const int it = take(x, atomicAdd(queue + x, 1));
+        if (it >= 0) return it;
+        int seen[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) seen[k] = __hip_atomic_load(queue + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 1; k < 8; ++k) {
+            const int qx = (x + k) & 7;
+            if (qstatic(qx) + seen[qx] >= qsize(qx)) continue;
+            const int st = take(qx, atomicAdd(queue + qx, 1));
+            if (st >= 0) return st;
+        }
+        return -1;
+    };
+    auto next = [&]() {  // the whole workgroup: thread 0 claims, the others wait for its result
+        if (threadIdx.x == 0) s_item = claim();
+        __syncthreads();
+        const int it = s_item;
+        __syncthreads();
+        return it;
+    };
+    int item;
+    if (!queue_mode) item = w;
+    else if (w < num_static && (w >> 3) < qstatic(x)) item = x * per + (w >> 3);
+    else item = next();
+    while (item >= 0) {
+        chunk::chunk_item<D>(item, p, chunk_items, qg, k_cache, v_cache, hq, hkv, scale_log2,
+                             chunk_acc, chunk_ml, o, lse);
+        if (!queue_mode) break;
+        // the next item is claimed only now: an item claimed ahead would be held behind this
+        // one while idle workers find the queues empty
+        item = next();
+    }
+    // the last worker to finish clears the counters for the next launch
+    if (queue_mode && threadIdx.x == 0 && atomicAdd(queue + 8, 1) == num_workers - 1) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) atomicExch(queue + k, 0);
+    }
 }
 
 }  // namespace
@@ -67,14 +128,18 @@ int attention_decode_waves_per_wg() { return kDecodeWaves; }
 hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int dec_wpg,
                             const int4* dec_items, const int32_t* wave_items, int num_waves,
                             const int4* chunk_items,
-                            int num_chunk_items, const void* q, const void* k_cache,
+                            int num_chunk_items, int num_workers, int num_static,
+                            bool queue_mode, int* queue, const void* q, const void* k_cache,
                             const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
                             float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev) {
     if (num_waves <= 0) dec_wgs = 0;
     if (dec_wgs > 0 && (dec_wpg < 1 || dec_wpg > kDecodeWaves || dec_wgs * dec_wpg < num_waves))
         return hipErrorInvalidValue;
-    const int grid = dec_wgs + num_chunk_items;
+    if (num_chunk_items <= 0) num_workers = 0;
+    if (num_workers > 0 && ((queue_mode && !queue) || (!queue_mode && num_workers != num_chunk_items)))
+        return hipErrorInvalidValue;
+    const int grid = dec_wgs + num_workers;
     if (grid <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
     auto qq = static_cast<const uint16_t*>(q);
@@ -84,12 +149,14 @@ hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int 
     if (sh.d == 128)
         hipExtLaunchKernelGGL(mixed_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
                               ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
-                              chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              chunk_items, num_chunk_items, num_workers, num_static, queue_mode,
+                              queue, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     else
         hipExtLaunchKernelGGL(mixed_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
                               ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
-                              chunk_items, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              chunk_items, num_chunk_items, num_workers, num_static, queue_mode,
+                              queue, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     return hipGetLastError();
 }

@@ -125,7 +125,7 @@ size_t generic_partial_floats(int32_t num_tokens, const Shape& sh, int nsplit);
 
 namespace ca {
 // MFMA attention for a whole mixed step (bf16, G <= 16), one launch: the grid is dec_wgs decode
-// workgroups followed by num_chunk_items chunk workgroups (attn_mixed.hip).
+// workgroups followed by num_workers chunk workers (attn_mixed.hip).
 //   decode: dec_items holds two int4 per item, {kv head, key begin, key end, partial slot or -1
 //     (the item covers the whole row: output written directly)}, {row, offset of the row's page
 //     ids in kv_page_indices, page count, 0}.  Decode workgroups run dec_wpg
@@ -136,10 +136,15 @@ namespace ca {
 //     head.  chunk_items: two int4 per workgroup, {seq, kv head, first column, partial slot or
 //     -1}, {key begin, key end, 0, 0} (seq -1: padding).  Partials: chunk_acc
 //     [slot][chunk_cols_per_block()][d] fp32 and chunk_ml [slot][cols].
+//   chunk workers: direct mode (queue_mode false) needs num_workers == num_chunk_items, worker
+//     w running item w; queue mode: num_workers persistent workers, the first num_static of
+//     them starting with the launch, taking items through the counters in `queue` (9 ints, zero
+//     on entry and left zero on exit).
 hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int dec_wpg,
                             const int4* dec_items, const int32_t* wave_items, int num_waves,
                             const int4* chunk_items,
-                            int num_chunk_items, const void* q, const void* k_cache,
+                            int num_chunk_items, int num_workers, int num_static,
+                            bool queue_mode, int* queue, const void* q, const void* k_cache,
                             const void* v_cache, float* dec_acc, float2* dec_ml,
                             float* chunk_acc, float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev);

@@ -560,6 +560,82 @@ def test_chunk_kernel_shapes(env, hq, hkv, d):
     assert res[0][0]["num_decodes"] == 1 and res[0][0]["num_tokens"] == 138
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_chunk_queue_mode(env, split):
+    """Chunk items taken from the work queues (more items than free workgroup slots): a 300-row
+    chunk on 2000 cached keys cut into 64-key splits (CA_CHUNK_SPLIT=64: ~1400 items, most of
+    them claimed through the queue counters) beside three decodes, in one launch and (split)
+    as a chunk-only launch.  Checked against the oracle, then the same attention launched four
+    more times, the third and fifth through the allocation-free entry point: the counters must
+    be back at zero after each launch, and which worker ran which item must not change a bit
+    (every item has its own partial slot, merged in a fixed order), so the ordinary launches
+    agree bit for bit, and so do the two allocation-free ones (which lengthen the splits to fit
+    their scratch, so they are held to the oracle's bar instead of to the others)."""
+    import os
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd import make_desc
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, Workload
+    from tests import harness as H
+    _, oracle = env
+    nc = np.array([1800, 2000, 2400, 1100], np.int32)
+    left = np.array([0, 300, 0, 0], np.int32)
+    stream = np.array([1, 300, 1, 1], np.int32)
+    pool = 640
+    perm = np.random.default_rng(31).permutation(pool).astype(np.int32)
+    tabs, it = [], 0
+    for r in range(4):
+        n = -(-int(nc[r] + stream[r]) // 16)
+        tabs.append(perm[it:it + n]); it += n
+    wl = Workload(name="queue-mode", config=0, seed=91, num_q_heads=32, num_kv_heads=8,
+                  head_dim=128, page_size=16, dtype="bf16", token_budget=512, max_chunk=0,
+                  num_pool_pages=pool, num_computed=nc, num_prompt_left=left, block_tables=tabs,
+                  stream_len=stream)
+    env_set = {"CA_CHUNK_SPLIT": "64"}
+    if split:
+        env_set["CA_SPLIT_ATTENTION"] = "1"
+    os.environ.update(env_set)
+    try:
+        qctx = ca.create(0)
+    finally:
+        for k in env_set:
+            del os.environ[k]
+    try:
+        res, (k_cache, v_cache), _ = run_and_check(qctx, oracle, wl, rows_per_seq=40,
+                                                   label=f"queue-mode-split{int(split)}")
+        assert res[0][0]["num_decodes"] == 3
+        # the step again on the appended caches: attention only, five launches
+        sess = oracle.Session(wl)
+        ref_plan = sess.plan()
+        plan = H.lib_plan(wl, sess.num_computed, sess.num_prompt_left)
+        q, _, _ = StreamCursor(wl).take(ref_plan["req_ids"], np.diff(ref_plan["qo_indptr"]))
+        desc = make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
+        q_in = H.to_device(q, wl.dtype)
+        q_rot = torch.empty_like(q_in)
+        # rotate q only: append_kv_rope into a scratch pool so the cache above stays as it is
+        k0, v0 = H.alloc_pool(wl, fill=0.0)
+        kn = torch.zeros((plan.num_tokens, wl.num_kv_heads, wl.head_dim), dtype=q_in.dtype, device="cuda")
+        qctx.append_kv_rope(desc, plan, q_in, q_rot, kn, kn, k0, v0, wl.num_pool_pages)
+        outs = []
+        for i in range(5):
+            o = torch.empty_like(q_rot)
+            lse = torch.empty((plan.num_tokens, wl.num_q_heads), dtype=torch.float32, device="cuda")
+            qctx.mixed_attention(desc, plan, q_rot, k_cache, v_cache, wl.num_pool_pages, o, lse,
+                                 no_alloc=i in (2, 4))
+            torch.cuda.synchronize()
+            outs.append((o.cpu(), lse.cpu()))
+        mask = ~np.isnan(res[0][3]["o"][:, 0, 0])
+        for i in range(5):
+            go = outs[i][0].float().numpy().astype(np.float64)
+            assert np.abs(go[mask] - res[0][3]["o"][mask]).max() <= TOL_O["bf16"], ("launch", i)
+        for i, j in ((1, 0), (3, 0), (4, 2)):
+            assert torch.equal(outs[i][0], outs[j][0]), ("launch", i, "o differs from", j)
+            assert torch.equal(outs[i][1], outs[j][1]), ("launch", i, "lse differs from", j)
+        _log(f"[queue-mode-split{int(split)}] five launches within the bar; repeats bit-identical")
+    finally:
+        qctx.close()
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(64, 2, 128), (32, 1, 64)])
 def test_wide_group_bf16(env, hq, hkv, d):
     """bf16 with 32 q heads per kv head (wider than one MFMA tile of 16 columns): these shapes
