@@ -452,7 +452,7 @@ def main():
         rd, cp, gm = peaks.hbm_read_gbs(), peaks.hbm_copy_gbs(), peaks.gemm_tflops("randn")
         r = out["roofline"]
         meas = rd if r["bound"] == "hbm" else gm
-        out["measured_peaks"] = {"hbm_read_GBs": round(rd, 1), "hbm_copy_GBs": round(cp, 1),
+        out["measured_peaks"] = {"hbm_read_nontemporal_GBs": round(rd, 1), "hbm_copy_GBs": round(cp, 1),
                                  "bf16_gemm_8192_TFs": round(gm, 1),
                                  "roofline_frac_of_measured": round(r["achieved"] / meas, 4)}
 

@@ -53,7 +53,10 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_rate_kernel(const uint4* __r
 
 // Plain read stream: each wavefront reads whole 16 KB chunks (16 loads of 16 bytes per lane in
 // flight, each load one contiguous 1 KB run), chunks dealt round-robin over the waves, and folds
-// the data into one word so the loads stay live.  n is a multiple of 1024 (16-byte units).
+// the data into one word so the loads stay live.  n is a multiple of 1024 (16-byte units).  NT:
+// the loads carry the non-temporal hint (streamed data not kept in the caches).
+typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
 __global__ void __launch_bounds__(256) read_stream_kernel(const uint4* __restrict__ src, size_t n,
                                                           uint32_t* __restrict__ out) {
     const size_t gid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -65,7 +68,14 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const uint4* __restric
         const uint4* b = src + c * 1024;
         uint4 v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = b[i * 64 + lane];
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (NT) {
+                const probe_u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const probe_u32x4*>(b + i * 64 + lane));
+                v[i] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+                v[i] = b[i * 64 + lane];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     }
@@ -183,10 +193,10 @@ extern "C" int ca_probe_mfma_rate(int mode, int iters, double* tflops, float* ms
 }
 
 // HBM read rate of the current device: a `bytes`-long buffer (rounded down to 16 KB, at least
-// 1 MiB) read once per launch by 16 workgroups of 256 threads per CU; best of 5 timed launches
-// after one warm-up.  Writes GB/s; returns 0 or the HIP error code (nothing is left
-// allocated either way).
-extern "C" int ca_probe_read_rate(size_t bytes, double* gbs) {
+// 1 MiB) read once per launch by 16 workgroups of 256 threads per CU, with plain or (nontemporal
+// != 0) non-temporal loads; best of 5 timed launches after one warm-up.  Writes GB/s; returns 0
+// or the HIP error code (nothing is left allocated either way).
+extern "C" int ca_probe_read_rate(size_t bytes, int nontemporal, double* gbs) {
     if (bytes < (size_t(1) << 20) || !gbs) return static_cast<int>(hipErrorInvalidValue);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -206,7 +216,10 @@ extern "C" int ca_probe_read_rate(size_t bytes, double* gbs) {
     for (int r = 0; r < 6 && e == hipSuccess; ++r) {
         e = hipEventRecord(e0, nullptr);
         if (e == hipSuccess) {
-            hipLaunchKernelGGL(read_stream_kernel, dim3(grid), dim3(block), 0, nullptr, src, n, out);
+            if (nontemporal)
+                hipLaunchKernelGGL(read_stream_kernel<true>, dim3(grid), dim3(block), 0, nullptr, src, n, out);
+            else
+                hipLaunchKernelGGL(read_stream_kernel<false>, dim3(grid), dim3(block), 0, nullptr, src, n, out);
             e = hipGetLastError();
         }
         if (e == hipSuccess) e = hipEventRecord(e1, nullptr);

@@ -7,9 +7,9 @@ Prints a markdown table:
     one workgroup per CU) for constant, zero, N(0, 1) and softmax-like operands -- the rate
     depends on the operand data on this part;
   * a large bf16 GEMM through torch.matmul (8192^3, hipBLASLt) on N(0, 1) and on all-ones data;
-  * HBM: a 4 GiB read stream (libca_probe.so: each wavefront reads whole 16 KB chunks, 16
-    loads of 16 bytes per lane in flight) and a 1 GiB device-to-device copy (read + write,
-    torch).
+  * HBM: read streams of 800 MiB and 4 GiB with plain and with non-temporal loads
+    (libca_probe.so: each wavefront reads whole 16 KB chunks, 16 loads of 16 bytes per lane in
+    flight) and a 1 GiB device-to-device copy (read + write, torch).
 The datasheet figures are 2.5 PFLOP/s dense bf16 and 8 TB/s HBM.
 """
 from __future__ import annotations
@@ -29,7 +29,7 @@ def _probe():
         raise RuntimeError(f"{PROBE_LIB} is not built (run the package build first)")
     lib = ctypes.CDLL(PROBE_LIB)
     lib.ca_probe_read_rate.restype = ctypes.c_int
-    lib.ca_probe_read_rate.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)]
+    lib.ca_probe_read_rate.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.ca_probe_mfma_rate.restype = ctypes.c_int
     lib.ca_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_float)]
@@ -78,9 +78,9 @@ def hbm_copy_gbs(mib: int = 1024) -> float:
     return 2.0 * x.numel() * 4 / dt / 1e9
 
 
-def hbm_read_gbs(mib: int = 4096) -> float:
+def hbm_read_gbs(mib: int = 4096, nontemporal: bool = True) -> float:
     gbs = ctypes.c_double()
-    rc = _probe().ca_probe_read_rate(mib * (1 << 20), ctypes.byref(gbs))
+    rc = _probe().ca_probe_read_rate(mib * (1 << 20), int(nontemporal), ctypes.byref(gbs))
     if rc:
         raise RuntimeError(f"ca_probe_read_rate failed: HIP error {rc}")
     return gbs.value
@@ -100,8 +100,11 @@ def main(argv):
         print(rows[-1], file=sys.stderr, flush=True)
     c = hbm_copy_gbs()
     rows.append(f"| HBM copy 1 GiB (read + write) | {c:.0f} GB/s | {c / 8000:.1%} |")
-    r = hbm_read_gbs()
-    rows.append(f"| HBM read stream 4 GiB | {r:.0f} GB/s | {r / 8000:.1%} |")
+    for mib in (800, 4096):
+        for nt in (False, True):
+            r = hbm_read_gbs(mib, nt)
+            rows.append(f"| HBM read stream {mib} MiB, {'non-temporal' if nt else 'plain'} loads | {r:.0f} GB/s | {r / 8000:.1%} |")
+            print(rows[-1], file=sys.stderr, flush=True)
     print("# Measured ceilings on one MI355X\n\nCommand (repository root): "
           "`python3 -m chunked_prefill_paged_ca_amd.peaks`\n")
     print("\n".join(rows))
