@@ -335,10 +335,25 @@ def _ptr(x) -> Optional[int]:
     return int(x.data_ptr())
 
 
+_RAW_STREAM = None
+
+
+def _current_stream() -> Optional[int]:
+    """The calling thread's current stream on the current device, as a raw handle.  torch's
+    internal getter returns the handle directly (~0.3 us); torch.cuda.current_stream() builds a
+    Stream object first (~3 us per call, once per library call)."""
+    global _RAW_STREAM
+    import torch
+    if _RAW_STREAM is None:
+        get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        dev = getattr(torch._C, "_cuda_getDevice", None)
+        _RAW_STREAM = (lambda: get(dev())) if get and dev else (lambda: torch.cuda.current_stream().cuda_stream)
+    return int(_RAW_STREAM()) or None
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
-        import torch
-        return int(torch.cuda.current_stream().cuda_stream) or None
+        return _current_stream()
     if isinstance(stream, int):
         return stream or None
     return int(stream.cuda_stream) or None

@@ -387,6 +387,7 @@ struct ca_ctx {
     // host-side work lists of prepare(), kept so that a steady stream of steps reuses them
     std::vector<int4> items, merges, citems, groups, clist;
     std::vector<int32_t> corder;
+    std::vector<int64_t> share_bounds;  // decode share boundaries of the last work lists
     int32_t chunk_workers = 0, chunk_static = 0;  // the chunk workers of the last work lists
     bool chunk_queue_mode = false;
     std::vector<int32_t> wave_items;
@@ -513,13 +514,21 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_tar
         ca::set_error("indptr totals disagree with num_tokens / num_pages");
         return CA_ERR_INVALID_ARG;
     }
-    int32_t top = -1;
+    // range of the page ids in one branch-free pass (it vectorises); the offending id is looked
+    // for only when the range is out of the pool
+    int32_t lo = 0x7fffffff, top = -1;
     for (int32_t j = 0; j < plan->num_pages; ++j) {
-        if (plan->kv_page_indices[j] < 0 || plan->kv_page_indices[j] >= pool) {
-            ca::set_error("page index " + std::to_string(plan->kv_page_indices[j]) + " outside the pool");
-            return CA_ERR_INVALID_ARG;
+        const int32_t v = plan->kv_page_indices[j];
+        lo = v < lo ? v : lo;
+        top = v > top ? v : top;
+    }
+    if (plan->num_pages > 0 && (lo < 0 || top >= pool)) {
+        for (int32_t j = 0; j < plan->num_pages; ++j) {
+            if (plan->kv_page_indices[j] < 0 || plan->kv_page_indices[j] >= pool) {
+                ca::set_error("page index " + std::to_string(plan->kv_page_indices[j]) + " outside the pool");
+                return CA_ERR_INVALID_ARG;
+            }
         }
-        if (plan->kv_page_indices[j] > top) top = plan->kv_page_indices[j];
     }
     if (write_targets) {
         std::vector<std::pair<int64_t, int32_t>> t;  // (page * P + slot, sequence)
@@ -806,7 +815,21 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
             }
             return b * sh.hkv;
         }();
-        auto bound = [&](int64_t k) { return B * k / W; };
+        // share boundaries B w / W, built incrementally (no division per share)
+        std::vector<int64_t>& bounds = ctx->share_bounds;
+        bounds.resize(static_cast<size_t>(W) + 2);
+        {
+            const int64_t q = W > 0 ? B / W : 0, r = W > 0 ? B % W : 0;
+            int64_t b = 0, acc = 0;
+            for (int32_t k = 0; k <= W; ++k) {
+                bounds[static_cast<size_t>(k)] = b;
+                b += q;
+                acc += r;
+                if (acc >= W) { acc -= W; ++b; }
+            }
+            bounds[static_cast<size_t>(W) + 1] = B;  // never reached: the walk stops at share W
+        }
+        auto bound = [&](int64_t k) { return bounds[static_cast<size_t>(k)]; };
         wave_items.assign(static_cast<size_t>(W) + 1, 0);
         int64_t off = 0;
         int32_t w = 0;

@@ -10,8 +10,10 @@ on the plan (device), ca_sched_commit (host).  q/k/v are random device rows (the
 depend on their values; correctness of the loop is tested against the oracle elsewhere).
 
 Prints a markdown summary: whole-loop tokens per second (host and device work overlapping as
-they do in a serving loop), the scheduler's host time per round, and the device time of the
-round's kernels (HIP events attached to the launches, a separate pass).
+they do in a serving loop), the host time of each call per round in that loop (which includes
+waiting for a free staging slot when the host runs ahead of the device), the device time of the
+round's kernels (HIP events attached to the launches, a separate pass), and the calls' own host
+cost (a third pass that lets the device drain after every round).
 """
 from __future__ import annotations
 
@@ -32,7 +34,10 @@ def scenario(n: int, rounds: int, seed: int = 17):
     return arrival, prompt, cached, max_new
 
 
-def run(rounds: int, n: int, timed_kernels: bool):
+def run(rounds: int, n: int, timed_kernels: bool, sync_rounds: bool = False):
+    """One pass of the loop.  sync_rounds: wait for the device at the end of every round (outside
+    the timed host sections), so the host times below are the calls' own cost, without the waits
+    for a free staging slot that a loop running ahead of the device meets."""
     import torch
     import chunked_prefill_paged_ca_amd as ca
     torch.cuda.set_device(0)
@@ -77,6 +82,8 @@ def run(rounds: int, n: int, timed_kernels: bool):
         h0 = time.perf_counter()
         sched.commit()
         host_commit += time.perf_counter() - h0
+        if sync_rounds:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kernel_us = 0.0
@@ -100,6 +107,8 @@ def main(argv):
     args = ap.parse_args(argv)
     free = run(args.rounds, args.requests, timed_kernels=False)
     timed = run(args.rounds, args.requests, timed_kernels=True)
+    own = run(args.rounds, args.requests, timed_kernels=False, sync_rounds=True)
+    own_total = own["host_step_us"] + own["host_append_us"] + own["host_attn_us"] + own["host_commit_us"]
     tps = free["tokens"] / free["elapsed_s"]
     out = [
         f"# Serving loop: Mistral-7B layer shapes, token budget 512, 64K-page pool, {args.requests} requests",
@@ -120,6 +129,9 @@ def main(argv):
         f"| ca_append_kv_rope call, host time per round | {free['host_append_us']:.1f} us |",
         f"| ca_mixed_attention call, host time per round | {free['host_attn_us']:.1f} us |",
         f"| device time per round (upload + append + attention + merge; timed pass) | {timed['kernel_us_per_round']:.1f} us |",
+        f"| host cost per round, device idle at every call (step / append / attention / commit) | "
+        f"{own_total:.1f} us ({own['host_step_us']:.1f} / {own['host_append_us']:.1f} / "
+        f"{own['host_attn_us']:.1f} / {own['host_commit_us']:.1f}) |",
     ]
     print("\n".join(out))
     return 0
