@@ -896,7 +896,8 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
         // left.  Measured on the part (Yi-34B step, 1096 items): with one workgroup per item the
         // in-order dispatcher left a tenth of the chunk CUs idle behind busy XCDs and the launch
         // ended on ~100 us of straggling full-length items; queue mode took the fused launch
-        // 580 -> 553 us (LLaMA2-70B step 1221 -> 1170 us).
+        // 588 -> 559 us (LLaMA2-70B step 1222 -> 1172 us, Llama-13B one-shot prompt 773 ->
+        // 716 us, its last 256-row chunk 77 -> 67 us).
         const int32_t per_cu = ctx->attn_wgs_per_cu[sh.d == 128 ? 1 : 0];
         const int32_t wslots = ctx->num_cus * (per_cu > 0 ? per_cu : 1);
         const bool fused = dec_wgs > 0 && plan->num_decodes > 0 && !ctx->split_attention;
@@ -1275,8 +1276,8 @@ ca_status ca_create(int device, ca_ctx** out) {
         return device_error("hipGetSymbolAddress(scratch)", e);
     }
     // the chunk work-queue counters start at zero; each attention launch leaves them at zero
-    e = hipMalloc(&ctx->queue, 16 * sizeof(int));
-    if (e == hipSuccess) e = hipMemset(ctx->queue, 0, 16 * sizeof(int));
+    e = hipMalloc(&ctx->queue, ca::kQueueInts * sizeof(int));
+    if (e == hipSuccess) e = hipMemset(ctx->queue, 0, ca::kQueueInts * sizeof(int));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         if (ctx->queue) (void)hipFree(ctx->queue);
@@ -1526,11 +1527,16 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
                 if (e == hipSuccess) t.commit();
             }
         }
+        // a queue-mode launch leaves its work-queue counters to the merge launch (or a clearing
+        // launch) that follows it on the stream
+        int* clear = w.chunk_queue_mode && w.num_chunk_items > 0 ? ctx->queue : nullptr;
         if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
             Timed t(ctx->prof, "merge", CA_PROFILE_MERGE, !no_alloc);
-            e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
+            e = ca::launch_merge(ctx->dplan, sh, clear, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
                                  w.num_chunk_groups, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
+        } else if (e == hipSuccess && clear) {
+            e = ca::launch_clear_queue(clear, stream);
         }
         if (e != hipSuccess) return device_error("attention launch", e);
         return CA_OK;

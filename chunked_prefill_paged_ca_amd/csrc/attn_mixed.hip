@@ -23,9 +23,10 @@
 // one each to the workers that start with the launch, without atomics; after that a worker
 // claims items through the queue's counter (a device-scope atomic add in `queue[x]`), its own
 // XCD's queue first, then the others, and leaves when all are empty.  No worker ever waits for
-// another, so every worker ends.  queue[8] counts the workers that have left; the last one sets
-// all nine counters back to zero, so each launch finds them cleared without a separate
-// clearing launch or memset (the counters are zeroed once when the context is created).
+// another, so every worker ends.  The counters are zeroed when the context is created and, after
+// every queue-mode launch, by the step's merge launch that follows it on the stream (or by a
+// one-workgroup clearing launch when the step has nothing to merge): a count of finished workers
+// for the last one to clear them would cost every worker another round trip at its end.
 
 #include <hip/hip_runtime.h>
 
@@ -80,15 +81,18 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
         return k < qsize(qx) ? qx * per + k : -1;
     };
     auto claim = [&]() -> int {  // thread 0
-        const int it = take(x, atomicAdd(queue + x, 1));
-        if (it >= 0) return it;
+        // the state of every queue is read along with the claim on this XCD's own queue (one
+        // round trip between them), so that a worker whose queue is empty learns at once which
+        // others still hold items, and one that finds all empty leaves after that one trip
         int seen[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) seen[k] = __hip_atomic_load(queue + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < 8; ++k) seen[k] = __hip_atomic_load(queue + k * kQueueStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int it = take(x, atomicAdd(queue + x * kQueueStride, 1));
+        if (it >= 0) return it;
         for (int k = 1; k < 8; ++k) {
             const int qx = (x + k) & 7;
             if (qstatic(qx) + seen[qx] >= qsize(qx)) continue;
-            const int st = take(qx, atomicAdd(queue + qx, 1));
+            const int st = take(qx, atomicAdd(queue + qx * kQueueStride, 1));
             if (st >= 0) return st;
         }
         return -1;
@@ -112,14 +116,20 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
         // one while idle workers find the queues empty
         item = next();
     }
-    // the last worker to finish clears the counters for the next launch
-    if (queue_mode && threadIdx.x == 0 && atomicAdd(queue + 8, 1) == num_workers - 1) {
-#pragma unroll
-        for (int k = 0; k < 9; ++k) atomicExch(queue + k, 0);
-    }
+}
+
+// Clears the work-queue counters after a queue-mode attention launch whose step has no merge
+// launch (the merge kernel clears them otherwise).
+__global__ void __launch_bounds__(64) clear_queue_kernel(int* __restrict__ queue) {
+    if (threadIdx.x < 8) queue[threadIdx.x * kQueueStride] = 0;
 }
 
 }  // namespace
+
+hipError_t launch_clear_queue(int* queue, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
+    return hipGetLastError();
+}
 
 int chunk_cols_per_block() { return chunk::kCols; }
 int chunk_max_split_keys() { return 16 * (chunk::kMaxItemPages - 2); }
