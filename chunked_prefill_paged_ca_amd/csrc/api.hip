@@ -723,6 +723,15 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
             const int64_t whole = static_cast<int64_t>(0.9 * dec_us / chunk_block_us(sh)) * 32;
             const int64_t keep = longest < whole ? longest : whole;
             if (keep > L) L = keep;
+        } else {
+            // More chunk work than the chunk CUs finish within the decode stream: it spills onto
+            // the decode CUs as those drain (queue mode).  Splits of up to ~0.4 of the decode
+            // time keep the partials (HBM traffic beside the decode stream, and merge work) few
+            // while the queues still even out the end.  Measured on the part (LLaMA2-70B step,
+            // ~950 us of decode): splits of 3200 / 4800 / 6400 / 9600 / 14400 / 21000 keys gave
+            // 1119 / 1087 / 1041 / 1025 / 1053 / 1246 us (1173 us at the ~1.8 K-key default).
+            const int64_t spill = static_cast<int64_t>(0.4 * dec_us / chunk_block_us(sh)) * 32;
+            if (spill > L) L = spill;
         }
     }
     // the split merge handles at most 64 splits of one row block
