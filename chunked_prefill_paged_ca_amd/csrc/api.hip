@@ -1363,7 +1363,8 @@ ca_status append_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan
                                    q_row < 0 ? int64_t(sh.hq) * sh.d : q_row,
                                    kv_row < 0 ? int64_t(sh.hkv) * sh.d : kv_row,
                                    copy ? ctx->staging.dev[slot] : nullptr, copy ? ctx->meta_buf.ptr : nullptr,
-                                   copy ? static_cast<int64_t>(ctx->defer_bytes / 16) : 0, stream, t.ev);
+                                   copy ? static_cast<int64_t>(ctx->defer_bytes / 16) : 0, ctx->num_cus, stream,
+                                   t.ev);
         if (e == hipSuccess) t.commit();
     }
     ctx->defer_slot = -1;

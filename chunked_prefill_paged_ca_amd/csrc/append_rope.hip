@@ -13,14 +13,21 @@
 //     token workgroups copy it there from the pinned host staging (for the attention launch that
 //     follows in stream order), and the token workgroups read their two per-row values straight
 //     from that staging: the copy overlaps the append instead of running before it;
-//   * every q/k/v load is a 16-byte vector load, all issued before the first store (a thread
-//     writes back exactly the elements it read, so q_out may alias q_in), and unconditional so
-//     that they are in flight together; q, k and v rows are read with their own row strides, so
-//     they may be the column ranges of one packed projection output;
+//   * the workgroup is sized to the token (one q/k rotation unit of N pairs per thread, 64 to
+//     1024 threads), so every load is needed and all of them -- q/k as 16-byte vectors, V one
+//     element per thread -- are issued before the first store (a thread writes back exactly
+//     the elements it read, so q_out may alias q_in); q, k and v rows are read with their own
+//     row strides, so they may be the column ranges of one packed projection output;
+//   * V is stored as soon as it and the page id are in, before the angles are formed: one
+//     element per thread, adjacent threads on adjacent dimensions, so that the 16 dimensions of
+//     a V run (stride 4 in the 4-slot layout) go out as one partial write of one cache line,
+//     not as 16 writes from 2 threads;
 //   * the d/2 pair angles are formed in fp64 once per token, shared through LDS, and each
 //     rotated element is computed in fp64 and rounded once to the storage type.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "dtype.h"
 #include "internal.h"
@@ -28,8 +35,6 @@
 namespace ca {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnits = 4;  // q/k vector units per thread per pass
 
 template <typename T>
 struct Vec {
@@ -67,87 +72,85 @@ template <>
 __device__ __forceinline__ uint16_t narrow<uint16_t>(double x) { return double_to_bf16_bits(x); }
 
 // Workgroups [num_tokens, gridDim.x) copy meta_n16 16-byte units from meta_src to meta_dst.
-template <typename T>
-__global__ void __launch_bounds__(kThreads) append_rope_kernel(
+// blockDim.x: a multiple of 64 in [64, 1024], at least D / 2 (the threads that form the angles).
+// U: rotation units per thread in the first pass; each thread also loads U * 4 V elements
+// before its first store.
+template <typename T, int D, int U>
+__global__ void __launch_bounds__(1024) append_rope_kernel(
     const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_page,
     const double* __restrict__ inv_freq, const T* q_in, T* q_out, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ k_cache, T* __restrict__ v_cache, int hq,
-    int hkv, int d, int P, int64_t q_row, int64_t kv_row, int num_tokens,
+    int hkv, int P, int64_t q_row, int64_t kv_row, int num_tokens,
     const uint4* __restrict__ meta_src, uint4* __restrict__ meta_dst, int64_t meta_n16) {
 #pragma clang fp contract(off)
     constexpr int N = Vec<T>::N;
-    __shared__ double s_cos[64];
-    __shared__ double s_sin[64];
+    constexpr int half = D / 2;
+    constexpr int per_head = half / N;  // rotation units per head (each covers N pairs)
+    constexpr int kV = 4 * U;           // V elements per thread in the first pass
+    __shared__ double s_cos[half];
+    __shared__ double s_sin[half];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    // The position and page are read first, before anything else is set up: they come over PCIe
+    // when the same launch copies the metadata, and every later step waits for them.  (A copy
+    // workgroup reads row 0's, which exists: the launch has at least one token.)
+    const int row = t < num_tokens ? t : 0;
+    const int pos = row_pos[row];
+    const int page = row_page[row];
     if (t >= num_tokens) {  // metadata copy workgroup (uniform branch)
-        const int64_t stride = static_cast<int64_t>(gridDim.x - num_tokens) * kThreads;
-        for (int64_t i = static_cast<int64_t>(t - num_tokens) * kThreads + tid; i < meta_n16; i += stride)
+        const int64_t stride = static_cast<int64_t>(gridDim.x - num_tokens) * nt;
+        for (int64_t i = static_cast<int64_t>(t - num_tokens) * nt + tid; i < meta_n16; i += stride)
             meta_dst[i] = meta_src[i];
         return;
     }
-    const int half = d >> 1;
-    const int per_head = half / N;  // vector units per head (each covers N pairs)
     const int units = (hq + hkv) * per_head;
-    const int v_units = hkv * d / N;
-    const int pos = row_pos[t];
-    const int page = row_page[t];
+    const int vdims = hkv * D;
+
+    // Every load of the first pass is issued before any value is used; indices past the end are
+    // clamped into range (the loads stay unconditional, so they are in flight together) and only
+    // the stores are predicated.  The frequency load goes first: waiting for it does not wait
+    // for the q/k/v loads.
+    const double freq = inv_freq[tid < half ? tid : half - 1];
+    const T* vrow = v_new + t * kv_row;
+    T vv[kV];
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+        const int e = tid + j * nt;
+        vv[j] = vrow[e < vdims ? e : vdims - 1];
+    }
+    auto unit_src = [&](int u, int& h, int& i0) {
+        h = u / per_head;
+        i0 = (u - h * per_head) * N;
+        return h < hq ? q_in + t * q_row + static_cast<int64_t>(h) * D
+                      : k_new + t * kv_row + static_cast<int64_t>(h - hq) * D;
+    };
+    int hh[U], ii[U];
+    Vec<T> a[U], b[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int u = tid + j * nt;
+        const T* src = unit_src(u < units ? u : units - 1, hh[j], ii[j]);
+        a[j] = load16(src + ii[j]);
+        b[j] = load16(src + ii[j] + half);
+    }
     const int slot = pos % P;
 
-    // Loads are unconditional (indices clamped into range; only the stores are predicated), so
-    // they are all in flight together instead of each waiting at the end of its own branch.
-    // The frequency load is issued first: waiting for it does not wait for the q/k/v loads.
-    const double freq = inv_freq[tid < half ? tid : half - 1];
-    Vec<T> vv = load16(v_new + t * kv_row + (tid < v_units ? tid : v_units - 1) * N);
-
-    Vec<T> a[kUnits], b[kUnits];
-    int i0[kUnits];
-    auto load_pass = [&](int base) {
-#pragma unroll
-        for (int j = 0; j < kUnits; ++j) {
-            const int u0 = base + tid + j * kThreads;
-            const int u = u0 < units ? u0 : units - 1;
-            const int h = u / per_head;
-            i0[j] = (u - h * per_head) * N;
-            const T* src = h < hq ? q_in + t * q_row + static_cast<int64_t>(h) * d
-                                  : k_new + t * kv_row + static_cast<int64_t>(h - hq) * d;
-            a[j] = load16(src + i0[j]);
-            b[j] = load16(src + i0[j] + half);
-        }
+    // V goes unrotated into its page: dim c of the slot lands in the run of 16-dim block c / 16
+    // and 4-slot group slot / 4, at (c % 16) * 4 + slot % 4
+    T* vpage = v_cache + static_cast<int64_t>(page) * hkv * P * D;
+    auto v_store = [&](int e, T val) {
+        const int g = e / D, c = e - g * D;
+        vpage[static_cast<int64_t>(g) * P * D + (((c >> 4) * (P >> 2) + (slot >> 2)) * 16 + (c & 15)) * 4 +
+              (slot & 3)] = val;
     };
-    auto rotate_pass = [&](int base) {
 #pragma unroll
-        for (int j = 0; j < kUnits; ++j) {
-            const int u = base + tid + j * kThreads;
-            // skip a unit slot no lane of this wave uses (wave-uniform test)
-            if (__builtin_amdgcn_readfirstlane(base + j * kThreads + (tid & ~63)) >= units) continue;
-            Vec<T> ra, rb;
-#pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const double x = widen<T>(a[j].e[e]), y = widen<T>(b[j].e[e]);
-                const double c = s_cos[i0[j] + e], s = s_sin[i0[j] + e];
-                ra.e[e] = narrow<T>(x * c - y * s);
-                rb.e[e] = narrow<T>(y * c + x * s);
-            }
-            if (u < units) {
-                const int h = u / per_head;
-                if (h < hq) {
-                    T* dst = q_out + (static_cast<int64_t>(t) * hq + h) * d;
-                    store16(dst + i0[j], ra);
-                    store16(dst + i0[j] + half, rb);
-                } else {
-                    // K page: the slot's 8-dim runs, one per 8-dim block (a vector unit never
-                    // straddles two blocks: it starts at a multiple of its length, which divides 8)
-                    T* dst = k_cache + (static_cast<int64_t>(page) * hkv + (h - hq)) * P * d;
-                    const int e0 = i0[j], e1 = i0[j] + half;
-                    store16(dst + ((e0 >> 3) * P + slot) * 8 + (e0 & 7), ra);
-                    store16(dst + ((e1 >> 3) * P + slot) * 8 + (e1 & 7), rb);
-                }
-            }
-        }
-    };
+    for (int j = 0; j < kV; ++j) {
+        const int e = tid + j * nt;
+        if (e < vdims) v_store(e, vv[j]);
+    }
+    for (int e = tid + kV * nt; e < vdims; e += nt) v_store(e, vrow[e]);
 
-    load_pass(0);
     if (tid < half) {
         double sn, cs;
         sincos(static_cast<double>(pos) * freq, &sn, &cs);
@@ -155,23 +158,70 @@ __global__ void __launch_bounds__(kThreads) append_rope_kernel(
         s_sin[tid] = sn;
     }
     __syncthreads();
-    rotate_pass(0);
-    for (int base = kThreads * kUnits; base < units; base += kThreads * kUnits) {
-        load_pass(base);
-        rotate_pass(base);
-    }
 
-    // V goes unrotated into its page: dim e of the slot lands in the run of 16-dim block e / 16
-    // and 4-slot group slot / 4, at (e % 16) * 4 + slot % 4 (a vector unit stays in one block)
-    for (int vu = tid; vu < v_units; vu += kThreads) {
-        if (vu != tid) vv = load16(v_new + t * kv_row + vu * N);
-        const int g = (vu * N) / d;
-        const int e0 = vu * N - g * d;
-        T* vp = v_cache + (static_cast<int64_t>(page) * hkv + g) * P * d +
-                (((e0 >> 4) * (P >> 2) + (slot >> 2)) * 16 + (e0 & 15)) * 4 + (slot & 3);
+    auto rotate_store = [&](int u, int h, int i0, const Vec<T>& x, const Vec<T>& y) {
+        Vec<T> rx, ry;
 #pragma unroll
-        for (int e = 0; e < N; ++e) vp[4 * e] = vv.e[e];
+        for (int e = 0; e < N; ++e) {
+            const double xe = widen<T>(x.e[e]), ye = widen<T>(y.e[e]);
+            const double c = s_cos[i0 + e], s = s_sin[i0 + e];
+            rx.e[e] = narrow<T>(xe * c - ye * s);
+            ry.e[e] = narrow<T>(ye * c + xe * s);
+        }
+        if (u >= units) return;
+        if (h < hq) {
+            T* dst = q_out + (static_cast<int64_t>(t) * hq + h) * D;
+            store16(dst + i0, rx);
+            store16(dst + i0 + half, ry);
+        } else {
+            // K page: the slot's 8-dim runs, one per 8-dim block (a vector unit never straddles
+            // two blocks: it starts at a multiple of its length, which divides 8)
+            T* dst = k_cache + (static_cast<int64_t>(page) * hkv + (h - hq)) * P * D;
+            const int e0 = i0, e1 = i0 + half;
+            store16(dst + ((e0 >> 3) * P + slot) * 8 + (e0 & 7), rx);
+            store16(dst + ((e1 >> 3) * P + slot) * 8 + (e1 & 7), ry);
+        }
+    };
+    // a wave whose lanes all lie past the last unit skips the math (wave-uniform test)
+    const int wave0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+        if (wave0 + j * nt < units) rotate_store(tid + j * nt, hh[j], ii[j], a[j], b[j]);
+    for (int u0 = U * nt; u0 + wave0 < units; u0 += nt) {
+        const int u = u0 + tid;
+        int h, i0;
+        const T* src = unit_src(u < units ? u : units - 1, h, i0);
+        const Vec<T> x = load16(src + i0), y = load16(src + i0 + half);
+        rotate_store(u, h, i0, x, y);
     }
+}
+
+// Threads per token workgroup for U rotation units per thread: enough that the first pass
+// holds every rotation unit and (4 U per thread) every V element, and at least the D / 2 angle
+// threads.
+int append_threads(const Shape& sh, int U) {
+    const int n = 16 / (sh.dtype == CA_FP32 ? 4 : 2);
+    const int units = (sh.hq + sh.hkv) * (sh.d / 2 / n);
+    const int vdims = sh.hkv * sh.d;
+    int want = (units + U - 1) / U;
+    const int vthreads = (vdims + 4 * U - 1) / (4 * U);
+    want = want > vthreads ? want : vthreads;
+    want = want > sh.d / 2 ? want : sh.d / 2;
+    want = (want + 63) / 64 * 64;
+    return want < 1024 ? want : 1024;
+}
+
+// Rotation units per thread: the smallest U in {1, 2} whose workgroups all fit on the CUs at once
+// (32 resident waves per CU: 4 SIMDs x 8 waves, the kernel staying within 64 VGPRs for these),
+// else 4.  One unit per thread keeps each thread's chain (loads -> angles -> rotation -> stores)
+// shortest; when the token workgroups would not all be resident, fewer, longer-lived waves per
+// token beat a second round of workgroups.
+int append_units_per_thread(const Shape& sh, int64_t num_tokens, int num_cus) {
+    for (int U = 1; U <= 2; U *= 2) {
+        const int waves = append_threads(sh, U) / 64;
+        if (num_tokens <= static_cast<int64_t>(num_cus) * (32 / waves)) return U;
+    }
+    return 4;
 }
 
 }  // namespace
@@ -180,30 +230,38 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* 
                               const int32_t* row_page, const double* inv_freq, const void* q_in,
                               void* q_out, const void* k_new, const void* v_new, void* k_cache,
                               void* v_cache, int64_t q_row, int64_t kv_row, const void* meta_src,
-                              void* meta_dst, int64_t meta_n16, hipStream_t stream,
+                              void* meta_dst, int64_t meta_n16, int num_cus, hipStream_t stream,
                               const LaunchEvents& ev) {
     if (p.num_tokens <= 0) return hipSuccess;
+    const int U = append_units_per_thread(sh, p.num_tokens, num_cus > 0 ? num_cus : 256);
+    const int threads = append_threads(sh, U);
     // one 16-byte unit per copy thread: the staging is read over PCIe, where many small reads in
     // flight at once are what keeps the copy short
-    const int64_t copy_wgs64 = meta_n16 > 0 ? (meta_n16 + kThreads - 1) / kThreads : 0;
+    const int64_t copy_wgs64 = meta_n16 > 0 ? (meta_n16 + threads - 1) / threads : 0;
     const int copy_wgs = static_cast<int>(copy_wgs64 < 256 ? copy_wgs64 : 256);
-    const dim3 grid(p.num_tokens + copy_wgs), block(kThreads);
+    const dim3 grid(p.num_tokens + copy_wgs), block(threads);
     const uint4* msrc = static_cast<const uint4*>(meta_src);
     uint4* mdst = static_cast<uint4*>(meta_dst);
-    if (sh.dtype == CA_FP32) {
-        hipExtLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos, row_page,
-                           inv_freq, static_cast<const float*>(q_in), static_cast<float*>(q_out),
-                           static_cast<const float*>(k_new), static_cast<const float*>(v_new),
-                           static_cast<float*>(k_cache), static_cast<float*>(v_cache), sh.hq,
-                           sh.hkv, sh.d, p.page_size, q_row, kv_row, p.num_tokens, msrc, mdst, meta_n16);
-    } else {
-        hipExtLaunchKernelGGL(append_rope_kernel<uint16_t>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos,
-                           row_page, inv_freq, static_cast<const uint16_t*>(q_in),
-                           static_cast<uint16_t*>(q_out), static_cast<const uint16_t*>(k_new),
-                           static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache),
-                           static_cast<uint16_t*>(v_cache), sh.hq, sh.hkv, sh.d, p.page_size, q_row,
-                           kv_row, p.num_tokens, msrc, mdst, meta_n16);
-    }
+    auto go = [&](auto tag, auto d_tag, auto u_tag) {
+        using T = decltype(tag);
+        constexpr int D = decltype(d_tag)::value, Uc = decltype(u_tag)::value;
+        hipExtLaunchKernelGGL(append_rope_kernel<T, D, Uc>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos,
+                              row_page, inv_freq, static_cast<const T*>(q_in), static_cast<T*>(q_out),
+                              static_cast<const T*>(k_new), static_cast<const T*>(v_new), static_cast<T*>(k_cache),
+                              static_cast<T*>(v_cache), sh.hq, sh.hkv, p.page_size, q_row, kv_row, p.num_tokens,
+                              msrc, mdst, meta_n16);
+    };
+    auto by_u = [&](auto tag, auto d_tag) {
+        if (U == 1) go(tag, d_tag, std::integral_constant<int, 1>{});
+        else if (U == 2) go(tag, d_tag, std::integral_constant<int, 2>{});
+        else go(tag, d_tag, std::integral_constant<int, 4>{});
+    };
+    auto by_d = [&](auto tag) {
+        if (sh.d == 128) by_u(tag, std::integral_constant<int, 128>{});
+        else by_u(tag, std::integral_constant<int, 64>{});
+    };
+    if (sh.dtype == CA_FP32) by_d(0.0f);
+    else by_d(uint16_t(0));
     return hipGetLastError();
 }
 

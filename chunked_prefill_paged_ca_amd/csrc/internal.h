@@ -103,12 +103,13 @@ hipError_t launch_tiled_projection(const TiledPlan& pl, int64_t T, int64_t K, in
 // q_row, kv_row: elements between consecutive token rows of q_in and of k_new / v_new.
 // row_pos, row_page: [num_tokens] per-row position and destination page (device memory or the
 // device-mapped host staging).  meta_n16 > 0: the same launch also copies meta_n16 16-byte units
-// from meta_src (device-mapped host staging) to meta_dst (device memory).
+// from meta_src (device-mapped host staging) to meta_dst (device memory).  num_cus: the device's
+// CU count (sizes the token workgroups so that they are all resident at once where they can be).
 hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* row_pos,
                               const int32_t* row_page, const double* inv_freq, const void* q_in,
                               void* q_out, const void* k_new, const void* v_new, void* k_cache,
                               void* v_cache, int64_t q_row, int64_t kv_row, const void* meta_src,
-                              void* meta_dst, int64_t meta_n16, hipStream_t stream,
+                              void* meta_dst, int64_t meta_n16, int num_cus, hipStream_t stream,
                               const LaunchEvents& ev);
 
 // Generic split-KV attention for every row (one wave per (row, q head, split)), then merge.
