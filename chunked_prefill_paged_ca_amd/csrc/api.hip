@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -15,6 +16,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -110,20 +112,26 @@ __global__ void __launch_bounds__(256) upload_kernel(const uint4* __restrict__ s
         dst[i] = src[i];
 }
 
-// Ring of pinned host staging slots.  A slot is reused only after the upload that read it has
-// completed, so the host never overwrites bytes the device still needs.  Completion is tracked
-// per group of kGroup consecutive slots with one event recorded after the group's last upload:
-// an event is a marker in the stream that delays the next kernel by a few microseconds, so one
-// per group rather than one per step.  Before the first slot of a group is refilled, the
-// group's event (recorded a full ring earlier) is waited for.
+// Ring of pinned host staging slots.  A slot is reused only after the launch that read it (the
+// upload kernel, or an append launch that copies the slot itself) has completed, so the host
+// never overwrites bytes the device still needs.  Completion is reported by the attention launch
+// that follows the reader on the same stream: its first thread stores the slot's generation into
+// `done` (pinned host memory) as it starts, which by stream order is after the reader finished.
+// No event goes into the stream (an event is a marker that delays the next kernel by a few
+// microseconds).  A slot whose reader was followed by no reporting launch (a different stream,
+// no attention call) is waited for with a device synchronisation when the ring comes back to it.
 struct Staging {
     static constexpr int kSlots = 8;
-    static constexpr int kGroup = 4;
     void* host[kSlots] = {};
     void* dev[kSlots] = {};  // the same memory as the device addresses it
     size_t cap[kSlots] = {};
-    hipEvent_t ev[kSlots / kGroup] = {};
-    bool pending[kSlots / kGroup] = {};
+    uint32_t* done_host = nullptr;  // [kSlots]: generation of the slot's last reader known finished
+    uint32_t* done_dev = nullptr;   // the same memory as the device addresses it
+    uint32_t gen[kSlots] = {};      // generation of the slot's current contents
+    bool busy[kSlots] = {};         // a reader was enqueued and is not known to have finished
+    bool reported[kSlots] = {};     // a launch that reports the reader's end was enqueued after it
+    int last = -1;                  // the slot of the latest reader, not yet reported
+    hipStream_t last_stream = nullptr;
     int next = 0;
 
     // Every slot is allocated here, at context creation, with kInitialBytes (enough for the
@@ -131,12 +139,14 @@ struct Staging {
     // stream of steps never allocates: a slot grows (doubling) only for a plan larger than that.
     static constexpr size_t kInitialBytes = size_t(2) << 20;
     hipError_t init() {
-        for (int i = 0; i < kSlots / kGroup; ++i) {
-            hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming | hipEventDisableSystemFence);
-            if (e != hipSuccess) return e;
-        }
+        hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&done_host), kSlots * sizeof(uint32_t),
+                                     hipHostMallocMapped | hipHostMallocCoherent);
+        if (e != hipSuccess) { done_host = nullptr; return e; }
+        for (int i = 0; i < kSlots; ++i) done_host[i] = 0;
+        e = hipHostGetDevicePointer(reinterpret_cast<void**>(&done_dev), done_host, 0);
+        if (e != hipSuccess) return e;
         for (int i = 0; i < kSlots; ++i) {
-            hipError_t e = grow(i, kInitialBytes);
+            e = grow(i, kInitialBytes);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -158,6 +168,31 @@ struct Staging {
         cap[i] = want;
         return hipSuccess;
     }
+    // Wait until the last reader of slot i has finished.
+    hipError_t wait_done(int i) {
+        if (!busy[i]) return hipSuccess;
+        if (reported[i]) {
+            // the reporting launch is in the stream after the reader: its store arrives as the
+            // stream gets there (after a second, wait for the device and look once more)
+            const auto t0 = std::chrono::steady_clock::now();
+            while (__atomic_load_n(&done_host[i], __ATOMIC_ACQUIRE) != gen[i]) {
+                if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(1)) {
+                    hipError_t e = hipDeviceSynchronize();
+                    if (e != hipSuccess) return e;
+                    if (__atomic_load_n(&done_host[i], __ATOMIC_ACQUIRE) != gen[i]) return hipErrorUnknown;
+                    break;
+                }
+                std::this_thread::yield();
+            }
+        } else {
+            hipError_t e = hipDeviceSynchronize();  // no report follows the reader
+            if (e != hipSuccess) return e;
+            if (last == i) last = -1;
+        }
+        busy[i] = false;
+        reported[i] = false;
+        return hipSuccess;
+    }
     // The next slot of the ring, once the upload that last read it has completed.  With
     // may_grow false a plan larger than the slot is refused (*slot = -1) instead of allocating.
     hipError_t acquire(size_t bytes, int* slot, bool may_grow = true) {
@@ -165,12 +200,9 @@ struct Staging {
         const int i = next;
         if (cap[i] < bytes && !may_grow) return hipSuccess;
         next = (next + 1) % kSlots;
-        const int g = i / kGroup;
-        if (i % kGroup == 0 && pending[g]) {
-            hipError_t e = hipEventSynchronize(ev[g]);
-            if (e != hipSuccess) return e;
-            pending[g] = false;
-        }
+        hipError_t e = wait_done(i);
+        if (e != hipSuccess) return e;
+        ++gen[i];
         if (cap[i] < bytes) {
             hipError_t e = grow(i, bytes * 2);  // doubling, see DevBuf
             if (e != hipSuccess) return e;
@@ -193,26 +225,42 @@ struct Staging {
     // After the launch that reads `slot` has been enqueued on `stream` (the upload kernel, or an
     // append launch that copies the slot itself).
     hipError_t mark_read(int slot, hipStream_t stream) {
-        hipError_t e = hipSuccess;
-        if (slot % kGroup == kGroup - 1) {
-            e = hipEventRecord(ev[slot / kGroup], stream);
-            if (e != hipSuccess) return e;
-            pending[slot / kGroup] = true;
-        }
+        busy[slot] = true;
+        reported[slot] = false;
+        last = slot;
+        last_stream = stream;
         return hipSuccess;
     }
+    // For an attention launch about to be enqueued on `stream`: the report it should store (the
+    // latest reader's slot, when that reader was enqueued on the same stream), in p.
+    int report_into(ca::DevPlan& p, hipStream_t stream) const {
+        p.done_flag = nullptr;
+        p.done_value = 0;
+        if (last < 0 || last_stream != stream) return -1;
+        p.done_flag = done_dev + last;
+        p.done_value = gen[last];
+        return last;
+    }
+    // The launch carrying slot's report has been enqueued.
+    void reported_by_launch(int slot) {
+        if (slot < 0) return;
+        reported[slot] = true;
+        if (last == slot) last = -1;
+    }
     void release() {
-        for (int g = 0; g < kSlots / kGroup; ++g) {
-            if (pending[g]) (void)hipEventSynchronize(ev[g]);
-            if (ev[g]) (void)hipEventDestroy(ev[g]);
-            ev[g] = nullptr;
-            pending[g] = false;
-        }
+        bool any = false;
+        for (int i = 0; i < kSlots; ++i) any = any || busy[i];
+        if (any) (void)hipDeviceSynchronize();
         for (int i = 0; i < kSlots; ++i) {
             if (host[i]) (void)hipHostFree(host[i]);
             host[i] = nullptr;
             dev[i] = nullptr;
+            busy[i] = reported[i] = false;
         }
+        if (done_host) (void)hipHostFree(done_host);
+        done_host = nullptr;
+        done_dev = nullptr;
+        last = -1;
     }
 };
 
@@ -1497,6 +1545,13 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
     if (st != CA_OK) return st;
 
     const int G = sh.hq / sh.hkv;
+    // the first attention launch reports that the staging slot of the launch before it may be
+    // refilled (see Staging)
+    const int report = ctx->staging.report_into(ctx->dplan, stream);
+    struct ClearReport {
+        ca::DevPlan& p;
+        ~ClearReport() { p.done_flag = nullptr; }
+    } clear_report{ctx->dplan};
     if (sh.dtype == CA_BF16 && G <= 16) {
         const DevWork& w = ctx->dwork;
         float* cacc = ctx->cacc;
@@ -1537,6 +1592,9 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
                 if (e == hipSuccess) t.commit();
             }
         }
+        const bool launched = (w.num_dec_waves > 0 && w.dec_wgs > 0) ||
+                              (w.num_chunk_items > 0 && w.num_chunk_workers > 0);
+        if (e == hipSuccess && launched) ctx->staging.reported_by_launch(report);
         // a queue-mode launch leaves its work-queue counters to the merge launch (or a clearing
         // launch) that follows it on the stream
         int* clear = w.chunk_queue_mode && w.num_chunk_items > 0 ? ctx->queue : nullptr;
@@ -1576,6 +1634,7 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
                                          partial, nsplit, stream,
                                          t.ev);
         if (e == hipSuccess) t.commit();
+        if (e == hipSuccess) ctx->staging.reported_by_launch(report);
     }
     if (e != hipSuccess) return device_error("attention launch", e);
     return CA_OK;

@@ -51,6 +51,7 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
     float scale_log2, float* __restrict__ dec_acc, float2* __restrict__ dec_ml,
     float* __restrict__ chunk_acc, float2* __restrict__ chunk_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) report_done(p);
     if (static_cast<int>(blockIdx.x) < dec_wgs) {
         // wave-uniform indices: everything derived from them (item records, page ids) lives in
         // scalar registers and is read with scalar loads, which do not share the vector-load

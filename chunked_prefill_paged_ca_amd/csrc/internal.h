@@ -33,7 +33,17 @@ struct DevPlan {
     int32_t num_tokens;
     int32_t num_pages;
     int32_t page_size;
+    // When set, the attention launch's first thread stores done_value here (pinned host memory)
+    // as it starts: by stream order every earlier launch has finished by then, so the host learns
+    // that the staging slot an earlier launch read may be refilled (no event in the stream).
+    uint32_t* done_flag;
+    uint32_t done_value;
 };
+
+// The store of DevPlan::done_flag (a system-scope store: the host polls the location).
+__device__ __forceinline__ void report_done(const DevPlan& p) {
+    if (p.done_flag) __hip_atomic_store(p.done_flag, p.done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // Read-only plan metadata seen through the constant address space.  The attention kernel only
 // reads the plan arrays (they are written by earlier launches), and saying so lets the compiler

@@ -746,6 +746,78 @@ def test_profile_records_every_kernel(env):
     assert names2[0] == "upload" and "attention" in names2, names2
 
 
+def test_staging_ring_call_patterns(env):
+    """The step metadata travels through a ring of pinned staging slots; a slot is refilled only
+    once the launch that read it is known to have finished (reported by the next attention launch
+    on the same stream, else by waiting for the device).  Thirty rounds of call patterns -- append
+    then attention on one stream, the attention on a second stream ordered by an event, two appends
+    before one attention, attention alone (its own upload), the attention repeated -- wrap the
+    eight-slot ring several times; every round's outputs must equal a clean context's bit for
+    bit."""
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import StreamCursor, make_config
+    from tests import harness as H
+    ctx, _ = env
+    wl = make_config(2)
+    kc, vc = H.random_pool(wl, seed=5)
+    desc = ca.make_desc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.dtype)
+    batch = ca.RequestBatch(wl.num_computed, wl.num_prompt_left, wl.block_tables, wl.token_budget,
+                            wl.max_chunk, wl.page_size, wl.num_pool_pages)
+    plan0 = batch.plan()
+    a = plan0.arrays()
+    q_raw, k_raw, v_raw = StreamCursor(wl).take(a["req_ids"], np.diff(a["qo_indptr"]))
+    q_in, k_in, v_in = (H.to_device(x, wl.dtype) for x in (q_raw, k_raw, v_raw))
+    # reference: a fresh context, one append + attention (appending the same rows again
+    # rewrites the same cache slots with the same values)
+    ref_ctx = ca.create(0)
+    q_ref = torch.empty_like(q_in)
+    o_ref = torch.empty_like(q_in)
+    ref_ctx.append_kv_rope(desc, plan0, q_in, q_ref, k_in, v_in, kc, vc, wl.num_pool_pages)
+    ref_ctx.mixed_attention(desc, plan0, q_ref, kc, vc, wl.num_pool_pages, o_ref)
+    torch.cuda.synchronize()
+    ref_ctx.close()
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for r in range(30):
+        pattern = r % 5
+        q_rot = torch.full_like(q_in, float("nan"))
+        o = torch.full_like(q_in, float("nan"))
+        if pattern == 0:
+            ctx.append_kv_rope(desc, batch.plan(), q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages)
+            # the same plan object again: its metadata is already on the device
+            plan = batch.plan()
+            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages)
+            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o)
+        elif pattern == 1:
+            plan = batch.plan()
+            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages)
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side.wait_event(ev)
+            with torch.cuda.stream(side):
+                ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o, stream=side)
+            ev2 = torch.cuda.Event()
+            ev2.record(side)
+            main.wait_event(ev2)
+        elif pattern == 2:
+            plan = batch.plan()
+            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages)
+            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o)
+        elif pattern == 3:
+            q_rot.copy_(q_ref)
+            ctx.mixed_attention(desc, batch.plan(), q_rot, kc, vc, wl.num_pool_pages, o)
+        else:
+            plan = batch.plan()
+            ctx.append_kv_rope(desc, plan, q_in, q_rot, k_in, v_in, kc, vc, wl.num_pool_pages)
+            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o)
+            ctx.mixed_attention(desc, plan, q_rot, kc, vc, wl.num_pool_pages, o)
+        torch.cuda.synchronize()
+        assert torch.equal(q_rot, q_ref), ("staging", r, pattern, "q_rot")
+        assert torch.equal(o, o_ref), ("staging", r, pattern, "o")
+    _log("[staging] 30 rounds of 5 call patterns: outputs bit-identical to a clean context")
+
+
 def test_misaligned_buffer_is_rejected(env):
     """Device buffers must be 16-byte aligned; a view shifted by one element is refused before
     anything is launched."""
