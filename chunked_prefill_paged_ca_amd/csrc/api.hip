@@ -526,11 +526,10 @@ ca_status check_desc(const ca_attn_desc* d, const ca_plan* plan, Shape* sh) {
 // the same slot are a block-table error the append kernel cannot see -- its workgroups would race
 // on that slot -- and the block table must stay consistent across appends (pinghaoyang.com.cn
 // "Sarathi-Serve 完全拆解", section "先验证数值与状态正确性").
-ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_targets,
-                               int32_t* max_page) {
+// The structural part: counts, indptr totals, per-sequence lengths.
+ca_status validate_plan_structure(const ca_plan* plan) {
     const int32_t ns = plan->num_seqs;
     const int32_t P = plan->page_size;
-    *max_page = -1;
     if (ns == 0) return CA_OK;
     if (P <= 0) {
         ca::set_error("plan page_size must be > 0");
@@ -562,44 +561,75 @@ ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_tar
         ca::set_error("indptr totals disagree with num_tokens / num_pages");
         return CA_ERR_INVALID_ARG;
     }
-    // range of the page ids in one branch-free pass (it vectorises); the offending id is looked
-    // for only when the range is out of the pool
+    return CA_OK;
+}
+
+// The page ids against the pool, in one branch-free pass (it vectorises) that also copies them to
+// `copy` when given (the staging slot: one read of the ids instead of two); the offending id is
+// looked for only when the range is out of the pool.  *max_page: the largest id.
+ca_status check_page_range(const ca_plan* plan, int64_t pool, int32_t* copy, int32_t* max_page) {
     int32_t lo = 0x7fffffff, top = -1;
-    for (int32_t j = 0; j < plan->num_pages; ++j) {
-        const int32_t v = plan->kv_page_indices[j];
-        lo = v < lo ? v : lo;
-        top = v > top ? v : top;
-    }
-    if (plan->num_pages > 0 && (lo < 0 || top >= pool)) {
-        for (int32_t j = 0; j < plan->num_pages; ++j) {
-            if (plan->kv_page_indices[j] < 0 || plan->kv_page_indices[j] >= pool) {
-                ca::set_error("page index " + std::to_string(plan->kv_page_indices[j]) + " outside the pool");
-                return CA_ERR_INVALID_ARG;
-            }
+    const int32_t* ids = plan->kv_page_indices;
+    const int32_t n = plan->num_pages;
+    if (copy) {
+        for (int32_t j = 0; j < n; ++j) {
+            const int32_t v = ids[j];
+            copy[j] = v;
+            lo = v < lo ? v : lo;
+            top = v > top ? v : top;
         }
-    }
-    if (write_targets) {
-        std::vector<std::pair<int64_t, int32_t>> t;  // (page * P + slot, sequence)
-        t.reserve(static_cast<size_t>(plan->num_tokens));
-        for (int32_t s = 0; s < ns; ++s) {
-            const int32_t q = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
-            const int32_t p0 = plan->kv_page_indptr[s];
-            const int32_t kv_len = (plan->kv_page_indptr[s + 1] - p0 - 1) * P + plan->kv_last_page_len[s];
-            for (int32_t pos = kv_len - q; pos < kv_len; ++pos)
-                t.emplace_back(static_cast<int64_t>(plan->kv_page_indices[p0 + pos / P]) * P + pos % P, s);
-        }
-        std::sort(t.begin(), t.end());
-        for (size_t i = 1; i < t.size(); ++i) {
-            if (t[i].first == t[i - 1].first) {
-                ca::set_error("sequences " + std::to_string(t[i - 1].second) + " and " +
-                              std::to_string(t[i].second) + " both append to page " +
-                              std::to_string(t[i].first / P) + " slot " + std::to_string(t[i].first % P));
-                return CA_ERR_INVALID_ARG;
-            }
+    } else {
+        for (int32_t j = 0; j < n; ++j) {
+            const int32_t v = ids[j];
+            lo = v < lo ? v : lo;
+            top = v > top ? v : top;
         }
     }
     *max_page = top;
+    if (n > 0 && (lo < 0 || top >= pool)) {
+        for (int32_t j = 0; j < n; ++j) {
+            if (ids[j] < 0 || ids[j] >= pool) {
+                ca::set_error("page index " + std::to_string(ids[j]) + " outside the pool");
+                return CA_ERR_INVALID_ARG;
+            }
+        }
+    }
     return CA_OK;
+}
+
+// The (page, slot) write targets of the step's tokens are unique (see validate_plan_arrays).
+ca_status check_write_targets(const ca_plan* plan) {
+    const int32_t ns = plan->num_seqs;
+    const int32_t P = plan->page_size;
+    std::vector<std::pair<int64_t, int32_t>> t;  // (page * P + slot, sequence)
+    t.reserve(static_cast<size_t>(plan->num_tokens));
+    for (int32_t s = 0; s < ns; ++s) {
+        const int32_t q = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+        const int32_t p0 = plan->kv_page_indptr[s];
+        const int32_t kv_len = (plan->kv_page_indptr[s + 1] - p0 - 1) * P + plan->kv_last_page_len[s];
+        for (int32_t pos = kv_len - q; pos < kv_len; ++pos)
+            t.emplace_back(static_cast<int64_t>(plan->kv_page_indices[p0 + pos / P]) * P + pos % P, s);
+    }
+    std::sort(t.begin(), t.end());
+    for (size_t i = 1; i < t.size(); ++i) {
+        if (t[i].first == t[i - 1].first) {
+            ca::set_error("sequences " + std::to_string(t[i - 1].second) + " and " +
+                          std::to_string(t[i].second) + " both append to page " +
+                          std::to_string(t[i].first / P) + " slot " + std::to_string(t[i].first % P));
+            return CA_ERR_INVALID_ARG;
+        }
+    }
+    return CA_OK;
+}
+
+ca_status validate_plan_arrays(const ca_plan* plan, int64_t pool, bool write_targets,
+                               int32_t* max_page) {
+    *max_page = -1;
+    if (plan->num_seqs == 0) return CA_OK;
+    ca_status st = validate_plan_structure(plan);
+    if (st == CA_OK) st = check_page_range(plan, pool, nullptr, max_page);
+    if (st == CA_OK && write_targets) st = check_write_targets(plan);
+    return st;
 }
 
 // Share of the CUs the decode rows get when they share the attention launch with chunk rows:
@@ -886,10 +916,20 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
             }
             bounds[static_cast<size_t>(W) + 1] = B;  // never reached: the walk stops at share W
         }
-        auto bound = [&](int64_t k) { return bounds[static_cast<size_t>(k)]; };
+        const int64_t* bnd = bounds.data();
         wave_items.assign(static_cast<size_t>(W) + 1, 0);
+        int32_t* wi = wave_items.data();
+        // at most one item per (row, kv head) pair plus one per share boundary, and one merge per
+        // pair: the lists are sized once and written through pointers
+        const size_t max_items = static_cast<size_t>(plan->num_decodes) * sh.hkv + static_cast<size_t>(W) + 1;
+        items.resize(2 * max_items);
+        merges.resize(static_cast<size_t>(plan->num_decodes) * sh.hkv);
+        int4* it = items.data();
+        int4* mg = merges.data();
+        int32_t n_it = 0;
         int64_t off = 0;
         int32_t w = 0;
+        int64_t next_bound = bnd[1];
         for (int32_t s = 0; s < plan->num_decodes; ++s) {
             const int32_t p0 = plan->kv_page_indptr[s];
             const int32_t np = plan->kv_page_indptr[s + 1] - p0;
@@ -898,25 +938,31 @@ void build_lists(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, bool mfma, i
             const int32_t row = plan->qo_indptr[s];
             for (int32_t g = 0; g < sh.hkv; ++g) {
                 const int64_t end = off + nb;
-                const size_t first = items.size() / 2;
+                const int32_t first = n_it;
                 for (int64_t lo = off; lo < end;) {
-                    while (bound(w + 1) <= lo) wave_items[++w] = static_cast<int32_t>(items.size() / 2);
-                    const int64_t hi = end < bound(w + 1) ? end : bound(w + 1);
+                    while (next_bound <= lo) {
+                        wi[++w] = n_it;
+                        next_bound = bnd[w + 1];
+                    }
+                    const int64_t hi = end < next_bound ? end : next_bound;
                     const int32_t kb = static_cast<int32_t>(32 * (lo - off));
                     const int32_t ke = static_cast<int32_t>(32 * (hi - off) < kv_len ? 32 * (hi - off) : kv_len);
-                    items.push_back(make_int4(g, kb, ke, -1));
-                    items.push_back(make_int4(row, p0, np, 0));
+                    it[2 * n_it] = make_int4(g, kb, ke, -1);
+                    it[2 * n_it + 1] = make_int4(row, p0, np, 0);
+                    ++n_it;
                     lo = hi;
                 }
-                const int32_t pieces = static_cast<int32_t>(items.size() / 2 - first);
+                const int32_t pieces = n_it - first;
                 if (pieces > 1) {
-                    merges.push_back(make_int4(row, g, slots, pieces));
-                    for (int32_t i = 0; i < pieces; ++i) items[2 * (first + i)].w = slots++;
+                    *mg++ = make_int4(row, g, slots, pieces);
+                    for (int32_t i = 0; i < pieces; ++i) it[2 * (first + i)].w = slots++;
                 }
                 off = end;
             }
         }
-        while (w < W) wave_items[++w] = static_cast<int32_t>(items.size() / 2);
+        while (w < W) wi[++w] = n_it;
+        items.resize(2 * static_cast<size_t>(n_it));
+        merges.resize(static_cast<size_t>(mg - merges.data()));
         // chunks: one workgroup per (sequence, kv head, block of 256 columns, split of Lc keys);
         // a column is one (row, q head) pair, numbered row * G + head
         const int32_t Lc = csplit;
@@ -1096,8 +1142,11 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
         }
         return CA_OK;
     }
+    // structure first (the work lists below rely on it); the page ids are range-checked as they
+    // are copied into the staging slot
     int32_t max_page = -1;
-    ca_status st = validate_plan_arrays(plan, pool, check_targets, &max_page);
+    ca_status st = plan->num_seqs > 0 ? validate_plan_structure(plan) : CA_OK;
+    if (st == CA_OK && check_targets && plan->num_seqs > 0) st = check_write_targets(plan);
     if (st != CA_OK) return st;
     ctx->work_key = WorkKey{};  // meta_buf is about to change; nothing matches until it is whole
     ctx->defer_slot = -1;
@@ -1179,8 +1228,8 @@ ca_status prepare(ca_ctx* ctx, const ca_plan* plan, const Shape& sh, int64_t poo
     std::memcpy(hp, plan->qo_indptr, sizeof(int32_t) * (ns + 1));
     std::memcpy(hp + (ns + 1), plan->kv_page_indptr, sizeof(int32_t) * (ns + 1));
     std::memcpy(hp + 2 * (ns + 1), plan->kv_last_page_len, sizeof(int32_t) * ns);
-    if (plan->num_pages)
-        std::memcpy(hp + 2 * (ns + 1) + ns, plan->kv_page_indices, sizeof(int32_t) * plan->num_pages);
+    st = check_page_range(plan, pool, hp + 2 * (ns + 1) + ns, &max_page);
+    if (st != CA_OK) return st;
     // per row: its sequence, absolute position and destination page (the slot is pos % P)
     int32_t* hrow = hp + 2 * (ns + 1) + ns + plan->num_pages;
     int32_t* hpos = hrow + T;
