@@ -294,6 +294,17 @@ def test_sweep_chunked_vs_one_shot(env, c, align):
     assert np.abs(chunk_o - res1[0][1]).max() <= TOL_O["bf16"]
 
 
+def test_append_four_units_per_thread(env):
+    """The append launch's widest layout: 2048 tokens of the Llama-13B shape (MHA, 40 + 40 heads)
+    do not fit on the CUs at one rotation unit per thread, so each thread rotates four units and
+    stores sixteen V elements.  The rotated q and every appended K/V slot against the oracle
+    (attention sampled)."""
+    from chunked_prefill_paged_ca_amd.workload import make_config
+    ctx, oracle = env
+    wl = make_config(3, chunk=2048)
+    run_and_check(ctx, oracle, wl, steps=1, rows_per_seq=4, check_cache=True, label="append-u4")
+
+
 @pytest.mark.parametrize("T,library", [(1, False), (7, False), (16, False), (17, False), (33, False),
                                        (80, False), (100, False), (256, False), (512, False),
                                        (523, False), (2048, False), (1, True), (80, True)])
