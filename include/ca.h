@@ -20,8 +20,12 @@
  *     call returns.  A ca_ctx owns only its internal workspace (pinned staging memory, device
  *     metadata and split-KV partials), grown on demand and freed by ca_destroy.
  *   - Device work is enqueued asynchronously on the given hipStream_t (passed as void*; NULL is
- *     the null stream) and never synchronised by the library.  One ctx must not be used from
- *     two streams concurrently unless the caller orders those streams.
+ *     the null stream).  The host waits only when the ctx's ring of 8 pinned staging slots comes
+ *     back to a slot an earlier launch may still be reading: until the attention launch that
+ *     followed that reader on its stream has started (it stores a completion word into pinned
+ *     memory as it starts), or, when no attention launch followed it on that stream, for the
+ *     whole device (hipDeviceSynchronize).  One ctx must not be used from two streams
+ *     concurrently unless the caller orders those streams.
  *   - Errors: every call returns a ca_status; ca_last_error() gives a detail message for the
  *     calling thread.  Arguments are validated before anything is enqueued; on an error
  *     nothing is launched.
@@ -136,8 +140,9 @@ typedef struct ca_ctx ca_ctx;
  * Errors: CA_ERR_INVALID_ARG (null out, no such device), CA_ERR_DEVICE (a HIP error).
  */
 ca_status ca_create(int device, ca_ctx** out);
-/* Free the context's workspace (waits for nothing: the caller must have synchronised the
- * streams it used with this context). */
+/* Free the context's workspace.  The caller must have synchronised the streams it used with
+ * this context; the library itself only waits for the device when a staging slot may still be
+ * read by a launch (before its pinned memory is freed). */
 ca_status ca_destroy(ca_ctx* ctx);
 
 /*
