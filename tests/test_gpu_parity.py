@@ -191,13 +191,14 @@ def test_tiny_chunked_matches_oracle_and_one_shot(env, dt):
     assert np.abs(chunk_o - one_o).max() <= TOL_O[dt]
 
 
-@pytest.mark.parametrize("variant", ["base", "peaky", "packed"])
+@pytest.mark.parametrize("variant", ["base", "peaky", "packed", "fp32"])
 def test_mistral_mixed_full(env, variant):
     """Config 2 at full size: 80 decodes + P(300 on 1200) + Q(132 on 2048), every row checked
-    (packed: q, k, v handed over as one packed projection-shaped array)."""
+    (packed: q, k, v handed over as one packed projection-shaped array; fp32: the same step in
+    fp32 storage, through the plain kernel, against the 1e-4 bar)."""
     from chunked_prefill_paged_ca_amd.workload import make_config
     ctx, oracle = env
-    wl = make_config(2, peaky=(variant == "peaky"))
+    wl = make_config(2, peaky=(variant == "peaky"), dtype="fp32" if variant == "fp32" else None)
     res, _, _ = run_and_check(ctx, oracle, wl, label=f"mistral-{variant}", packed=(variant == "packed"))
     p = res[0][0]
     assert list(np.diff(p["qo_indptr"])[-2:]) == [300, 132] and p["num_tokens"] == 512
