@@ -812,6 +812,36 @@ int32_t chunk_split_keys(const ca_ctx* ctx, const ca_plan* plan, const Shape& sh
             if (spill > L) L = spill;
         }
     }
+    // With the device to themselves, a split length that leaves a few more items than workgroup
+    // slots runs those few as a second round of the same length: lengthen the splits (by up to
+    // twice) until one round holds every item.
+    if (!beside_decode) {
+        auto items_at = [&](int64_t len) {
+            int64_t n = 0;
+            for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
+                const int32_t q_len = plan->qo_indptr[s + 1] - plan->qo_indptr[s];
+                const int32_t np = plan->kv_page_indptr[s + 1] - plan->kv_page_indptr[s];
+                const int32_t kv_len = (np - 1) * plan->page_size + plan->kv_last_page_len[s];
+                const int32_t ncols = q_len * G;
+                for (int32_t cb = 0; cb < ncols; cb += cols_per_block) {
+                    const int32_t last = (cb + cols_per_block < ncols ? cb + cols_per_block : ncols) - 1;
+                    n += (kv_len - q_len + last / G + 1 + len - 1) / len;
+                }
+            }
+            return n * sh.hkv;
+        };
+        const int64_t L32 = ((L + 31) / 32) * 32;
+        const int64_t n0 = items_at(L32);
+        const int64_t cap = ca::chunk_max_split_keys() / 32 * 32;
+        if (n0 > wg_slots && n0 < 2 * wg_slots) {
+            for (int64_t L2 = L32 + 32; L2 <= 2 * L32 && L2 <= cap; L2 += 32) {
+                if (items_at(L2) <= wg_slots) {
+                    L = L2;
+                    break;
+                }
+            }
+        }
+    }
     // the split merge handles at most 64 splits of one row block
     int32_t longest = 0;
     for (int32_t s = plan->num_decodes; s < plan->num_seqs; ++s) {
