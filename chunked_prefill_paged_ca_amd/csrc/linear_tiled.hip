@@ -79,7 +79,7 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 0xf) | (0x7 << 4) | ((n >> 4) <
 template <int BM, int BN, int NST>
 __device__ __forceinline__ void tiled_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
-    float* __restrict__ part, int T, int K, int N, int ksplit, int ntb, int nfb, int nsplit) {
+    float* __restrict__ part, int T, int K, int N, int ntb, int nfb, int nsplit) {
     using S = TileShape<BM, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t st0[S::HALVES];
     __shared__ __attribute__((aligned(16))) uint16_t st1[S::HALVES];
@@ -104,8 +104,11 @@ __device__ __forceinline__ void tiled_body(
     const int wr = wv >> 1, wc = wv & 1;
     const int c = lane & 15, q = lane >> 4;
     const int t0 = tb * BM, f0 = fb * BN;
-    const int kbeg = sp * ksplit;
-    const int nst = ksplit / kBK;
+    // split sp covers the K stages [sp KS / nsplit, (sp + 1) KS / nsplit) of the KS = K / kBK
+    const int KS = K / kBK;
+    const int s0 = static_cast<int>(static_cast<int64_t>(sp) * KS / nsplit);
+    const int kbeg = s0 * kBK;
+    const int nst = static_cast<int>(static_cast<int64_t>(sp + 1) * KS / nsplit) - s0;
 
     // This wave's DMA sources.  A stage holds the BM x rows, then the BN w rows, each row's kBK
     // values as one 2 kBK-byte LDS row.  DMA instruction u of the wave (stage instruction
@@ -292,8 +295,8 @@ __device__ __forceinline__ void tiled_body(
 template <int BM, int BN, int NST>
 __global__ void __launch_bounds__(kThreads) tiled_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
-    float* __restrict__ part, int T, int K, int N, int ksplit, int ntb, int nfb, int nsplit) {
-    tiled_body<BM, BN, NST>(x, w, out, part, T, K, N, ksplit, ntb, nfb, nsplit);
+    float* __restrict__ part, int T, int K, int N, int ntb, int nfb, int nsplit) {
+    tiled_body<BM, BN, NST>(x, w, out, part, T, K, N, ntb, nfb, nsplit);
 }
 
 // out = sum over the nsplit partials, in split order, rounded once to bf16 (4 outputs per thread)
@@ -328,7 +331,7 @@ constexpr int ring_stages(int bm, int bn) {
 }
 
 using TiledFn = void (*)(const uint16_t*, const uint16_t*, uint16_t*, float*, int, int, int, int, int,
-                         int, int);
+                         int);
 
 // The kernel instance of a tile shape (nullptr for a shape not built).  Each instance is named
 // here, in a plain host function, so both compilation passes instantiate it.
@@ -348,6 +351,25 @@ TiledFn tiled_fn(int bm, int bn) {
         case 128128: return &tiled_kernel<128, 128, ring_stages(128, 128)>;
         default: return nullptr;
     }
+}
+
+// Workgroups of a tile shape one CU holds at once (LDS- and register-limited), asked of the
+// runtime once per shape.
+int tiled_wgs_per_cu(int bm, int bn) {
+    static int cache[5][3] = {};
+    const int i = bm / 32, j = bn / 32 - 2;
+    if (i < 1 || i > 4 || j < 0 || j > 2) return 1;
+    int& c = cache[i][j];
+    if (c == 0) {
+        int blocks = 0;
+        const TiledFn fn = tiled_fn(bm, bn);
+        if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(fn),
+                                                               kThreads, 0) == hipSuccess && blocks > 0)
+            c = blocks;
+        else
+            c = 1;
+    }
+    return c;
 }
 
 }  // namespace
@@ -373,21 +395,28 @@ TiledPlan plan_tiled_projection(int64_t T, int64_t K, int64_t N, int num_cus) {
         }
     }
     // Fewer tiles than CUs (a few dozen tokens: the product is bound by reading the weights):
-    // split K until there are two workgroups per CU, up to 8 ways (measured on the Mistral-7B
-    // projection at T = 80: 25.5 us with 4 splits, 22.3 us with 8).
+    // split K so that the workgroups fill every workgroup slot of the device once -- as many
+    // splits as one round holds, not a count that leaves a partial second round (the splits need
+    // not divide K evenly: split i takes K stages [i S / n, (i + 1) S / n)); at most 64, each at
+    // least 256 of K.  Measured on the Mistral-7B projection at T = 80 (two workgroups per CU):
+    // 8 splits (768 workgroups, a round and a half) took 22.0 us.
     const int64_t tiles = ntb * (N / pl.bn);
     pl.nsplit = 1;
-    if (tiles < cus)
-        while (tiles * pl.nsplit < 2 * cus && pl.nsplit < 8 && K % (2 * pl.nsplit * kBK) == 0 &&
-               K / (2 * pl.nsplit) >= 256)
-            pl.nsplit *= 2;
+    if (tiles < cus) {
+        const int64_t slots = static_cast<int64_t>(cus) * tiled_wgs_per_cu(pl.bm, pl.bn);
+        int64_t n = slots / tiles;
+        const int64_t by_k = K / 256;
+        n = n < by_k ? n : by_k;
+        n = n < 64 ? n : 64;
+        pl.nsplit = static_cast<int>(n > 1 ? n : 1);
+    }
     pl.ok = true;
     return pl;
 }
 
 bool tiled_shape_fits(const TiledPlan& pl, int64_t T, int64_t K, int64_t N) {
     return tiled_fn(pl.bm, pl.bn) != nullptr && T >= 1 && N % pl.bn == 0 && pl.nsplit >= 1 &&
-           pl.nsplit <= 64 && K % (static_cast<int64_t>(pl.nsplit) * kBK) == 0;
+           pl.nsplit <= 64 && K % kBK == 0 && K / kBK >= pl.nsplit;
 }
 
 size_t tiled_partial_bytes(const TiledPlan& pl, int64_t T, int64_t N) {
@@ -410,7 +439,7 @@ hipError_t launch_tiled_projection(const TiledPlan& pl, int64_t T, int64_t K, in
     const int blocks = ntb * nfb * pl.nsplit;
     const int grid = (blocks + 7) / 8 * 8;
     hipExtLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, stream, ev.start, stop, 0, xx, ww, oo, part, t, k,
-                          n, k / pl.nsplit, ntb, nfb, pl.nsplit);
+                          n, ntb, nfb, pl.nsplit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t n4 = T * N / 4;
