@@ -111,8 +111,8 @@ __device__ __forceinline__ void chunk_item(
     __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageHalves<D>];
     __shared__ __attribute__((aligned(16))) uint16_t stage2[kStageHalves<D>];
     __shared__ __attribute__((aligned(16))) uint16_t stage3[kStageHalves<D>];
-    // the item's page ids, so a block's ids are an LDS read (two spare entries: a block's pair
-    // is read as one 8-byte load, also past the last page, and the spare half then ignored)
+    // the item's page ids, so a stage's ids are one LDS read (at most 2048 pages: an item has at
+    // most 1024 blocks, so the last stage's eight ids end at entry 2048; two spare entries)
     __shared__ __attribute__((aligned(16))) int s_pages[kMaxItemPages + 2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -136,14 +136,6 @@ __device__ __forceinline__ void chunk_item(
     const int lp0 = kb >> 4;
     const int nlp = min(((ke + 31) >> 4) - lp0, np - lp0);  // <= kMaxItemPages (host-checked)
     for (int i = tid; i < nlp; i += 64 * kWaves) s_pages[i] = pages[lp0 + i];
-    // key0 is a multiple of 32 (item ranges start on 32-key blocks), so lp is even and the
-    // pair is one aligned 8-byte read
-    auto page_pair = [&](int key0, int* pa, int* pb) {
-        const int lp = (key0 >> 4) - lp0;
-        const int2 ids = *reinterpret_cast<const int2*>(s_pages + lp);
-        *pa = ids.x;
-        *pb = (lp0 + lp + 1 < np) ? ids.y : ids.x;  // a missing page is masked, never used
-    };
 
     // this wave's columns: tile nt, lane column c -> column cb + 32 w + 16 nt + c
     bf16x8 qf[kTiles][D / 32];
@@ -303,13 +295,23 @@ __device__ __forceinline__ void chunk_item(
         else if constexpr (i == 2) return stage2;
         else return stage3;
     };
-    // copy stage si (its first min(kSub, blocks left) blocks) into `slot`
+    // copy stage si (its first min(kSub, blocks left) blocks) into `slot`.  The stage's 2 kSub
+    // page ids are read from LDS at once (item ranges start on 32-key blocks, so the stage's
+    // first page sits at lp = 2 kSub si past lp0, 16-byte aligned): one LDS round trip per stage
+    // before its copies can be issued, not one per block.  Ids past the item's last page are
+    // stale and never used (its blocks stop at nblk; a block's second page past the sequence is
+    // replaced by its first and masked).
     auto dma_stage = [&](uint16_t* slot, int si) {
+        static_assert(kSub == 4, "a stage's page ids are two int4");
+        const int lp = 2 * kSub * si;
+        const int4 ia = *reinterpret_cast<const int4*>(s_pages + lp);
+        const int4 ib = *reinterpret_cast<const int4*>(s_pages + lp + 4);
+        const int ids[2 * kSub] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
             if (kSub * si + j < nblk) {
-                int pa, pb;
-                page_pair(kb + SK * si + 32 * j, &pa, &pb);
+                const int pa = ids[2 * j];
+                const int pb = (lp0 + lp + 2 * j + 1 < np) ? ids[2 * j + 1] : pa;
                 dma_block<D>(slot + 64 * D * j, k_cache, v_cache, pa, pb, g, hkv, w, lane);
             }
         }
