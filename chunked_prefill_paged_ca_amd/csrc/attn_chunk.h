@@ -15,7 +15,8 @@
 // MFMA tiles without padding.  A workgroup is 8 wavefronts of 32 columns (two waves per SIMD:
 // one wave's softmax overlaps the other's MFMAs), and one K/V tile in LDS serves all 256
 // columns.  Per 32-key block (two pages) the workgroup copies the two K pages and two V pages
-// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers); the blocks are
+// (16 KB) from HBM into LDS with 16-byte global->LDS DMA loads (no registers), issued by one
+// wave per SIMD while the SIMD's other wave computes; the blocks are
 // copied and published four at a time (a 128-key LDS stage, one barrier each), the next stage
 // in flight while one is consumed.  Each wave runs S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_16x16x32_bf16 with an online softmax per column.  The pages keep
@@ -65,14 +66,22 @@ __device__ __forceinline__ bf16x8 lds_frag_pair(const uint16_t* a, const uint16_
 }
 
 // Copy one 32-key block straight from HBM into LDS stage `stage` (16-byte DMA per lane, no
-// registers).  The stage holds 8D 16-byte units, 2D per page run; wave w's instruction u fills
-// the contiguous units (w*U + u)*64 + lane, all inside one run (2D is a multiple of 64), so
-// every instruction copies 1 KB of one page run.
+// registers).  The stage holds 8D 16-byte units, 2D per page run; copying wave w's instruction
+// u fills the contiguous units (w*U + u)*64 + lane, all inside one run (2D is a multiple of 64),
+// so every instruction copies 1 KB of one page run.  Only waves 0-3 copy, one per SIMD: a SIMD's
+// vector-memory path takes ~15 bytes per clock, so issuing a stage's copies holds the issuing
+// wave for ~1,000 cycles, and with one copying wave per SIMD the SIMD's other wave keeps the
+// matrix core busy meanwhile (measured: Yi-34B chunk 459-466 -> 453-459 us, LLaMA2-70B chunk
+// 285-287 -> 271-274 us, Llama-13B one-shot 757-791 -> 742-754 us; copies by two waves only
+// took twice as long, by all eight or by halves alternating per stage no better).
+constexpr int kCopyWaves = 4;
 template <int D>
 __device__ __forceinline__ void dma_block(uint16_t* stage, const uint16_t* __restrict__ k_cache,
                                           const uint16_t* __restrict__ v_cache, int pa, int pb,
                                           int g, int hkv, int w, int lane) {
-    constexpr int U = 8 * D / (64 * kWaves);  // instructions per wave
+    constexpr int U = 8 * D / (64 * kCopyWaves);  // instructions per copying wave
+    static_assert(kCopyWaves <= kWaves && U >= 1, "copy split");
+    if (w >= kCopyWaves) return;  // wave-uniform
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int first = (w * U + u) * 64;
@@ -283,7 +292,7 @@ __device__ __forceinline__ void chunk_item(
     // read (the DMA count of the stages issued after it may stay outstanding), and the barrier
     // both publishes that stage and frees the one about to be refilled.
     static_assert(kStages >= 2 && kStages <= 4 && kSub >= 1 && kSub * (kStages - 2) <= 8, "stage shape");
-    constexpr int U = 8 * D / (64 * kWaves);  // DMA instructions per wave per 32-key block
+    constexpr int U = 8 * D / (64 * kCopyWaves);  // DMA instructions per copying wave per 32-key block
     constexpr int SK = 32 * kSub;             // keys per stage
     const int nblk = (ke - kb + 31) >> 5;
     const int nst = (nblk + kSub - 1) / kSub;
