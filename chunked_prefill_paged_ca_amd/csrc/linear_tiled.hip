@@ -7,8 +7,13 @@
 //
 //   out[T][N] = x[T][K] . w[N][K]^T  (bf16 operands, fp32 accumulation, bf16 result)
 //
-// Workgroup = one output tile of BM tokens x BN features over a range of K; its 4 wavefronts
-// (one per SIMD) split the tile 2 x 2, each BM/2 tokens x BN/2 features.  The product runs as
+// Workgroup = one output tile of BM tokens x BN features over a range of K, 8 wavefronts: waves
+// 0-3 (one per SIMD) split the tile 2 x 2, each BM/2 tokens x BN/2 features, and only compute;
+// waves 4-7 only issue the stage copies.  A SIMD's vector-memory path takes ~15 bytes per
+// clock, so issuing a stage's copies holds the issuing wave for hundreds of cycles; on a wave of
+// its own that time runs beside the matrix work instead of before it (measured on the
+// Mistral-7B projection: T = 512 51.4 -> 38.3-39.8 us, T = 256 40.7 -> 31.5 us, T = 128
+// 27.6 -> 23.7 us, T = 100 26.6 -> 22.4 us; T <= 80 unchanged within the box's spread).  The product runs as
 // out^T = w x^T on v_mfma_f32_16x16x32_bf16 (A = 16 weight rows x 32 of K, B = x^T: 32 of K x
 // 16 tokens, C = 16 features x 16 tokens; lane (c, q) holds features 4q .. 4q+3 of token c).
 //   * Operands reach LDS by 16-byte global->LDS DMA, no registers: a stage holds BK = 64 of K of
@@ -48,8 +53,9 @@ namespace {
 #ifndef CA_TILED_VGPR
 #define CA_TILED_VGPR 0
 #endif
+static_assert(CA_TILED_VGPR == 0, "register staging is not built with copying waves");
 
-constexpr int kThreads = 256;       // 4 wavefronts, 2 x 2 over the output tile
+constexpr int kThreads = 512;       // 4 computing wavefronts (2 x 2 over the tile) + 4 copying
 constexpr int kBK = CA_TILED_BK;    // K per LDS stage
 constexpr int kKS = kBK / 32;       // 32-wide MFMA steps per stage
 static_assert(kBK % 32 == 0 && kKS >= 1 && kKS <= 8, "stage depth");
@@ -100,7 +106,9 @@ __device__ __forceinline__ void tiled_body(
     if (sp >= nsplit) return;  // grid padding (uniform over the block)
 
     const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool copier = wv0 >= 4;  // waves 4-7 copy the stages, waves 0-3 compute
+    const int wv = wv0 & 3;
     const int wr = wv >> 1, wc = wv & 1;
     const int c = lane & 15, q = lane >> 4;
     const int t0 = tb * BM, f0 = fb * BN;
@@ -131,6 +139,7 @@ __device__ __forceinline__ void tiled_body(
         }
     }
     auto dma = [&](uint16_t* stage, int si) {
+        if (!copier) return;
 #pragma unroll
         for (int u = 0; u < S::D; ++u)
             __builtin_amdgcn_global_load_lds(src[u] + si * kBK, stage + 512 * (wv * S::D + u), 16, 0, 0);
@@ -247,7 +256,7 @@ __device__ __forceinline__ void tiled_body(
         const int later = (nst - 1 < si + NST - 2 ? nst - 1 : si + NST - 2) - si;
         wait_stage(later);
         if (si + NST - 1 < nst) dma(slot(std::integral_constant<int, i + NST - 1>{}), si + NST - 1);
-        compute(slot(std::integral_constant<int, i>{}));
+        if (!copier) compute(slot(std::integral_constant<int, i>{}));
     };
     for (int si = 0; si < nst; si += NST) {
         step(std::integral_constant<int, 0>{}, si);
@@ -272,6 +281,7 @@ __device__ __forceinline__ void tiled_body(
     }
     }
 
+    if (copier) return;
     // C tile (j, i): features f0 + 16 (wc NJ + j) + 4 q .. + 3 of token t0 + 16 (wr MI + i) + c
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -349,6 +359,10 @@ TiledFn tiled_fn(int bm, int bn) {
         case 128064: return &tiled_kernel<128, 64, ring_stages(128, 64)>;
         case 128096: return &tiled_kernel<128, 96, ring_stages(128, 96)>;
         case 128128: return &tiled_kernel<128, 128, ring_stages(128, 128)>;
+        case 128192: return &tiled_kernel<128, 192, ring_stages(128, 192)>;
+        case 128256: return &tiled_kernel<128, 256, ring_stages(128, 256)>;
+        case 256096: return &tiled_kernel<256, 96, ring_stages(256, 96)>;
+        case 256128: return &tiled_kernel<256, 128, ring_stages(256, 128)>;
         default: return nullptr;
     }
 }
@@ -356,9 +370,9 @@ TiledFn tiled_fn(int bm, int bn) {
 // Workgroups of a tile shape one CU holds at once (LDS- and register-limited), asked of the
 // runtime once per shape.
 int tiled_wgs_per_cu(int bm, int bn) {
-    static int cache[5][3] = {};
+    static int cache[9][7] = {};
     const int i = bm / 32, j = bn / 32 - 2;
-    if (i < 1 || i > 4 || j < 0 || j > 2) return 1;
+    if (i < 1 || i > 8 || j < 0 || j > 6) return 1;
     int& c = cache[i][j];
     if (c == 0) {
         int blocks = 0;
@@ -375,8 +389,11 @@ int tiled_wgs_per_cu(int bm, int bn) {
 }  // namespace
 
 // Tile shape and K split for T tokens: BM = T rounded up to 32 (at most 128); then, among the
-// feature tiles that divide N, the one whose tile count fills the 256 CUs best (ties: the wider
-// tile, fewer bytes moved per flop); K split as below.
+// feature tiles (192, 128, 96, 64) that divide N, the one whose tile count fills the 256 CUs
+// best (ties: the wider tile, fewer bytes moved per flop); K split as below.  Measured on the
+// Mistral-7B projection: 1024 tokens 90.9 -> 65.5 us and 2048 tokens 141 -> 121 us with the
+// 192-wide tile (one and two full rounds) against 128 (a round and a half, three rounds).  The
+// 256-token tiles (256 x 96, 256 x 128, forced with CA_PROJECTION_TILE) were slower at every T.
 TiledPlan plan_tiled_projection(int64_t T, int64_t K, int64_t N, int num_cus) {
     TiledPlan pl{};
     if (T < 1 || K % kBK != 0 || N % 64 != 0 || K > INT32_MAX || N > INT32_MAX || T > INT32_MAX) return pl;
@@ -384,7 +401,7 @@ TiledPlan plan_tiled_projection(int64_t T, int64_t K, int64_t N, int num_cus) {
     pl.bm = T <= 32 ? 32 : (T <= 64 ? 64 : (T <= 96 ? 96 : 128));
     const int64_t ntb = (T + pl.bm - 1) / pl.bm;
     double best = -1.0;
-    for (int bn : {128, 96, 64}) {
+    for (int bn : {192, 128, 96, 64}) {
         if (N % bn) continue;
         const int64_t tiles = ntb * (N / bn);
         const int64_t rounds = (tiles + cus - 1) / cus;

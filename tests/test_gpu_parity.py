@@ -342,15 +342,56 @@ def test_qkv_projection_matches_oracle(env, T, library):
     torch.cuda.synchronize()
     if library:
         pctx.close()
+    _check_projection(oracle, x, w, out, f"T={T}")
+
+
+def _check_projection(oracle, x, w, out, label):
+    """The projection bar of test_qkv_projection_matches_oracle: the fp32 sum bound plus one bf16
+    ulp of the exact value, and at most 1e-4 of the outputs more than one ulp off."""
+    from tests import harness as H
+    hidden = x.shape[1]
     got = out.float().cpu().numpy().astype(np.float64)
     ref = oracle.linear(x, w, "bf16")
     u = H.ulp_distance(got, ref, "bf16")
     sum_bound = hidden * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T)
     allowed = sum_bound + np.abs(ref) * 2.0 ** -7 + 2.0 ** -133
-    _log(f"[projection T={T}] max ulp {u.max():.0f}, outputs not equal {(u > 0).mean():.5f}, "
+    _log(f"[projection {label}] max ulp {u.max():.0f}, outputs not equal {(u > 0).mean():.5f}, "
          f"worst |err|/allowed {(np.abs(got - ref) / allowed).max():.3f}")
     assert np.all(np.abs(got - ref) <= allowed)
     assert (u > 1).mean() <= 1e-4
+
+
+@pytest.mark.parametrize("bm,bn,split,T", [(128, 192, 1, 300), (128, 256, 2, 200), (256, 96, 2, 300),
+                                           (256, 128, 1, 523), (32, 64, 5, 40), (96, 64, 7, 80),
+                                           (64, 128, 3, 64)])
+def test_projection_forced_tile_shapes(env, bm, bn, split, T):
+    """Every tile shape the tiled projection kernel is built with, forced through
+    CA_PROJECTION_TILE=bm,bn,split (a context created with it set), with ragged last token
+    blocks (300 = 2 x 128 + 44, 523) and K splits that do not divide the 64 K stages evenly (5, 7,
+    3: split i takes stages [64 i / n, 64 (i + 1) / n)), against the exact product at the bar of
+    test_qkv_projection_matches_oracle."""
+    import os
+    import torch
+    import chunked_prefill_paged_ca_amd as ca
+    from chunked_prefill_paged_ca_amd.workload import projection_inputs
+    from tests import harness as H
+    _, oracle = env
+    Hq, Hkv, d, hidden = 32, 8, 128, 4096
+    N = (Hq + 2 * Hkv) * d
+    x, w = projection_inputs(T, hidden, N, seed=101 + T + bm + bn + split)
+    desc = ca.make_desc(Hq, Hkv, d, 16, "bf16")
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    os.environ["CA_PROJECTION_TILE"] = f"{bm},{bn},{split}"
+    try:
+        pctx = ca.create(0)
+    finally:
+        del os.environ["CA_PROJECTION_TILE"]
+    try:
+        pctx.qkv_projection(desc, T, hidden, H.to_device(x, "bf16"), H.to_device(w, "bf16"), out)
+        torch.cuda.synchronize()
+    finally:
+        pctx.close()
+    _check_projection(oracle, x, w, out, f"tile {bm}x{bn} split {split} T={T}")
 
 
 def test_projected_step_matches_oracle(env):
