@@ -129,9 +129,11 @@ typedef struct ca_ctx ca_ctx;
  *                           1/64 of the longest chunk row's keys);
  *   CA_SPLIT_ATTENTION=1    decode and prefill-chunk rows as two launches instead of one;
  *   CA_PROJECTION_LIBRARY=1 ca_qkv_projection always through hipBLASLt;
- *   CA_PROJECTION_TILE=bm,bn,s  tile shape of ca_qkv_projection's tiled kernel (bm tokens in
- *                           32..128, bn features in 64/96/128, K split over s workgroups); a
- *                           shape that does not fit the product is CA_ERR_INVALID_ARG;
+ *   CA_PROJECTION_TILE=bm,bn,s  tile shape of ca_qkv_projection's tiled kernel (bm x bn one of
+ *                           32/64/96/128 x 64/96/128, 128 x 192, 128 x 256, 256 x 96,
+ *                           256 x 128; K split over s workgroups, 1 <= s <= min(64, K / 64));
+ *                           a shape that is not built or does not fit the product is
+ *                           CA_ERR_INVALID_ARG;
  *   CA_DEBUG_VALIDATE=1     ca_append_kv_rope(_packed) also checks that no two scheduled tokens
  *                           append to the same (page, slot) (ca_plan_validate with
  *                           CA_VALIDATE_WRITE_TARGETS; a host-side sort of the step's targets).
