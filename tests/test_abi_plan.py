@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(L):
 
 def test_library_leaves_none_of_its_own_symbols_undefined(L):
     """Every symbol of the library's own namespace is defined in libca.so (a kernel whose host
-    handle was not emitted would otherwise only fail to load on the GPU machine)."""
+    handle was not emitted would otherwise only fail to load on a machine with a GPU)."""
     import shutil
     import subprocess
     nm = shutil.which("nm")
