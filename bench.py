@@ -377,7 +377,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no cross-GPU exchange; see the sharding notes in the design doc)",
+              "(the path has no cross-GPU exchange: it shards by heads or by requests, one independent "
+              "launch per GPU)",
               file=sys.stderr)
         sys.exit(2)
 
