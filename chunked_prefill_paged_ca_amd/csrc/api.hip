@@ -390,7 +390,10 @@ struct ca_ctx {
     Profiler prof;
     Staging staging;
     DevBuf meta_buf;        // one upload per step: plan metadata, then the work lists
-    int* queue = nullptr;   // chunk work-queue counters of the attention launch (zero between launches)
+    // two sets of chunk work-queue counters, used by turns: the attention launch claims from
+    // set queue_parity and zeroes the other, which the next queue-mode launch uses
+    int* queue = nullptr;
+    int32_t queue_parity = 0;
     DevPlan dplan{};
     const double* inv_freq = nullptr;  // [d / 2] rotary inverse frequencies of the current shape
     // one device table of inverse frequencies per (head dim, rotary base), filled once and kept
@@ -1411,9 +1414,10 @@ ca_status ca_create(int device, ca_ctx** out) {
         delete ctx;
         return device_error("hipGetSymbolAddress(scratch)", e);
     }
-    // the chunk work-queue counters start at zero; each attention launch leaves them at zero
-    e = hipMalloc(&ctx->queue, ca::kQueueInts * sizeof(int));
-    if (e == hipSuccess) e = hipMemset(ctx->queue, 0, ca::kQueueInts * sizeof(int));
+    // both sets of chunk work-queue counters start at zero; each attention launch zeroes the set
+    // it hands to the next one
+    e = hipMalloc(&ctx->queue, 2 * ca::kQueueInts * sizeof(int));
+    if (e == hipSuccess) e = hipMemset(ctx->queue, 0, 2 * ca::kQueueInts * sizeof(int));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         if (ctx->queue) (void)hipFree(ctx->queue);
@@ -1644,46 +1648,50 @@ ca_status attention_impl(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* p
         // workgroups only started where a CU drained completely, and the fork/join events
         // stalled the host between steps.)  CA_SPLIT_ATTENTION=1 runs the parts as two launches
         // of the same kernel, each over the whole device, to time them separately.
+        // the queue counter set of this launch, and the one it zeroes for the next queue-mode launch
+        auto queue_set = [&](int k) { return ctx->queue + ((ctx->queue_parity + k) & 1) * ca::kQueueInts; };
+        auto launched_queue = [&](bool queue_mode) { if (queue_mode) ctx->queue_parity ^= 1; };
         if (!ctx->split_attention) {
             Timed t(ctx->prof, "attention", CA_PROFILE_ATTENTION, !no_alloc);
             e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
                                      w.num_dec_waves, w.chunk_items, w.num_chunk_items,
                                      w.num_chunk_workers, w.num_chunk_static, w.chunk_queue_mode,
-                                     ctx->queue, q, k_cache, v_cache, dacc, dml, cacc, cml, o, lse,
-                                     stream, t.ev);
-            if (e == hipSuccess) t.commit();
+                                     queue_set(0), queue_set(1), q, k_cache, v_cache, dacc, dml, cacc,
+                                     cml, o, lse, stream, t.ev);
+            if (e == hipSuccess) {
+                t.commit();
+                launched_queue(w.chunk_queue_mode && w.num_chunk_items > 0);
+            }
         } else {
             if (w.num_chunk_items > 0) {
                 Timed t(ctx->prof, "chunk", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, 0, w.dec_wpg, w.dec_items, w.dec_wave_items, 0,
                                          w.chunk_items, w.num_chunk_items, w.num_chunk_workers,
-                                         w.num_chunk_static, w.chunk_queue_mode, ctx->queue, q,
-                                         k_cache, v_cache, dacc, dml, cacc, cml, o, lse, stream,
+                                         w.num_chunk_static, w.chunk_queue_mode, queue_set(0), queue_set(1),
+                                         q, k_cache, v_cache, dacc, dml, cacc, cml, o, lse, stream,
                                          t.ev);
-                if (e == hipSuccess) t.commit();
+                if (e == hipSuccess) {
+                    t.commit();
+                    launched_queue(w.chunk_queue_mode);
+                }
             }
             if (e == hipSuccess && w.num_dec_waves > 0) {
                 Timed t(ctx->prof, "decode", CA_PROFILE_ATTENTION, !no_alloc);
                 e = ca::launch_attention(ctx->dplan, sh, w.dec_wgs, w.dec_wpg, w.dec_items, w.dec_wave_items,
-                                         w.num_dec_waves, w.chunk_items, 0, 0, 0, false, ctx->queue, q,
-                                         k_cache, v_cache, dacc, dml, cacc, cml, o, lse, stream,
-                                         t.ev);
+                                         w.num_dec_waves, w.chunk_items, 0, 0, 0, false, queue_set(0),
+                                         queue_set(1), q, k_cache, v_cache, dacc, dml, cacc, cml, o,
+                                         lse, stream, t.ev);
                 if (e == hipSuccess) t.commit();
             }
         }
         const bool launched = (w.num_dec_waves > 0 && w.dec_wgs > 0) ||
                               (w.num_chunk_items > 0 && w.num_chunk_workers > 0);
         if (e == hipSuccess && launched) ctx->staging.reported_by_launch(report);
-        // a queue-mode launch leaves its work-queue counters to the merge launch (or a clearing
-        // launch) that follows it on the stream
-        int* clear = w.chunk_queue_mode && w.num_chunk_items > 0 ? ctx->queue : nullptr;
         if (e == hipSuccess && (w.num_merges > 0 || w.num_chunk_groups > 0)) {
             Timed t(ctx->prof, "merge", CA_PROFILE_MERGE, !no_alloc);
-            e = ca::launch_merge(ctx->dplan, sh, clear, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
+            e = ca::launch_merge(ctx->dplan, sh, w.merges, w.num_merges, dacc, dml, w.chunk_groups,
                                  w.num_chunk_groups, cacc, cml, o, lse, stream, t.ev);
             if (e == hipSuccess) t.commit();
-        } else if (e == hipSuccess && clear) {
-            e = ca::launch_clear_queue(clear, stream);
         }
         if (e != hipSuccess) return device_error("attention launch", e);
         return CA_OK;

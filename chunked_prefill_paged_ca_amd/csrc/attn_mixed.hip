@@ -23,10 +23,10 @@
 // one each to the workers that start with the launch, without atomics; after that a worker
 // claims items through the queue's counter (a device-scope atomic add in `queue[x]`), its own
 // XCD's queue first, then the others, and leaves when all are empty.  No worker ever waits for
-// another, so every worker ends.  The counters are zeroed when the context is created and, after
-// every queue-mode launch, by the step's merge launch that follows it on the stream (or by a
-// one-workgroup clearing launch when the step has nothing to merge): a count of finished workers
-// for the last one to clear them would cost every worker another round trip at its end.
+// another, so every worker ends.  Two counter sets are used by turns: a launch claims from one
+// and its first thread zeroes the other, which the next queue-mode launch on the stream claims
+// from (a count of finished workers for the last one to clear them would cost every worker
+// another round trip at its end).
 
 #include <hip/hip_runtime.h>
 
@@ -45,13 +45,16 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
     DevPlan p, int dec_wgs, int dec_wpg, const int4* __restrict__ dec_items,
     const int32_t* __restrict__ wave_items, int num_waves, const int4* __restrict__ chunk_items,
     int num_chunk_items, int num_workers, int num_static, bool queue_mode,
-    int* __restrict__ queue,
+    int* __restrict__ queue, int* __restrict__ queue_other,
     const uint16_t* __restrict__ qg,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int hq, int hkv,
     float scale_log2, float* __restrict__ dec_acc, float2* __restrict__ dec_ml,
     float* __restrict__ chunk_acc, float2* __restrict__ chunk_ml, uint16_t* __restrict__ o,
     float* __restrict__ lse) {
     if (blockIdx.x == 0 && threadIdx.x == 0) report_done(p);
+    // the other work-queue counter set, for the next queue-mode launch (see the top of the file)
+    if (blockIdx.x == 0 && threadIdx.x < 8)
+        __hip_atomic_store(queue_other + threadIdx.x * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (static_cast<int>(blockIdx.x) < dec_wgs) {
         // wave-uniform indices: everything derived from them (item records, page ids) lives in
         // scalar registers and is read with scalar loads, which do not share the vector-load
@@ -119,18 +122,7 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(
     }
 }
 
-// Clears the work-queue counters after a queue-mode attention launch whose step has no merge
-// launch (the merge kernel clears them otherwise).
-__global__ void __launch_bounds__(64) clear_queue_kernel(int* __restrict__ queue) {
-    if (threadIdx.x < 8) queue[threadIdx.x * kQueueStride] = 0;
-}
-
 }  // namespace
-
-hipError_t launch_clear_queue(int* queue, hipStream_t stream) {
-    hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
-    return hipGetLastError();
-}
 
 int chunk_cols_per_block() { return chunk::kCols; }
 int chunk_max_split_keys() { return 16 * (chunk::kMaxItemPages - 2); }
@@ -140,7 +132,8 @@ hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int 
                             const int4* dec_items, const int32_t* wave_items, int num_waves,
                             const int4* chunk_items,
                             int num_chunk_items, int num_workers, int num_static,
-                            bool queue_mode, int* queue, const void* q, const void* k_cache,
+                            bool queue_mode, int* queue, int* queue_other,
+                            const void* q, const void* k_cache,
                             const void* v_cache, float* dec_acc, float2* dec_ml, float* chunk_acc,
                             float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev) {
@@ -150,6 +143,7 @@ hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int 
     if (num_chunk_items <= 0) num_workers = 0;
     if (num_workers > 0 && ((queue_mode && !queue) || (!queue_mode && num_workers != num_chunk_items)))
         return hipErrorInvalidValue;
+    if (!queue_other) return hipErrorInvalidValue;
     const int grid = dec_wgs + num_workers;
     if (grid <= 0) return hipSuccess;
     const float scale_log2 = sh.scale * 1.4426950408889634f;
@@ -161,13 +155,13 @@ hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int 
         hipExtLaunchKernelGGL(mixed_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
                               ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
                               chunk_items, num_chunk_items, num_workers, num_static, queue_mode,
-                              queue, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              queue, queue_other, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     else
         hipExtLaunchKernelGGL(mixed_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, ev.start,
                               ev.stop, 0, p, dec_wgs, dec_wpg, dec_items, wave_items, num_waves,
                               chunk_items, num_chunk_items, num_workers, num_static, queue_mode,
-                              queue, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
+                              queue, queue_other, qq, kc, vc, sh.hq, sh.hkv, scale_log2, dec_acc, dec_ml,
                               chunk_acc, chunk_ml, oo, lse);
     return hipGetLastError();
 }

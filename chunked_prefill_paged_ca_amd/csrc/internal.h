@@ -150,21 +150,22 @@ namespace ca {
 //   chunk workers: direct mode (queue_mode false) needs num_workers == num_chunk_items, worker
 //     w running item w; queue mode: num_workers persistent workers, the first num_static of
 //     them starting with the launch, taking items through the counters in `queue`
-//     (kQueueInts ints, zero on entry; a queue-mode launch must be followed by launch_merge with
-//     clear = queue, or by launch_clear_queue, before the next one).
+//     (kQueueInts ints, zero on entry).  Every launch zeroes the other counter set
+//     `queue_other` (kQueueInts ints), which the caller gives to the next queue-mode launch on
+//     the stream: two sets used alternately need no clearing launch.
 hipError_t launch_attention(const DevPlan& p, const Shape& sh, int dec_wgs, int dec_wpg,
                             const int4* dec_items, const int32_t* wave_items, int num_waves,
                             const int4* chunk_items,
                             int num_chunk_items, int num_workers, int num_static,
-                            bool queue_mode, int* queue, const void* q, const void* k_cache,
+                            bool queue_mode, int* queue, int* queue_other,
+                            const void* q, const void* k_cache,
                             const void* v_cache, float* dec_acc, float2* dec_ml,
                             float* chunk_acc, float2* chunk_ml, void* o, float* lse, hipStream_t stream,
                             const LaunchEvents& ev);
 // Work-queue counters: eight, each alone in a 128-byte line (kQueueStride ints apart) so that
 // the atomics of the eight queues do not contend for one line.
 constexpr int kQueueStride = 32;
-constexpr int kQueueInts = 8 * kQueueStride;  // ints of the work-queue counter buffer
-hipError_t launch_clear_queue(int* queue, hipStream_t stream);
+constexpr int kQueueInts = 8 * kQueueStride;  // ints of one work-queue counter set
 int chunk_cols_per_block();
 int attention_decode_waves_per_wg();
 // Attention workgroups one CU holds at once.
@@ -175,7 +176,7 @@ int attention_wgs_per_cu(int d);
 // {splits, first row of the sequence, rows of the sequence, 0} (partials
 // [slot][chunk_cols_per_block()][d]).  Running maxima are in log2 units.  16 lanes per output
 // (row, q head).
-hipError_t launch_merge(const DevPlan& p, const Shape& sh, int* clear, const int4* dec_merges, int num_dec,
+hipError_t launch_merge(const DevPlan& p, const Shape& sh, const int4* dec_merges, int num_dec,
                         const float* dec_acc, const float2* dec_ml, const int4* chunk_groups,
                         int num_chunk, const float* chunk_acc, const float2* chunk_ml, void* o,
                         float* lse, hipStream_t stream, const LaunchEvents& ev);

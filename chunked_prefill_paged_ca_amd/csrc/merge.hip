@@ -87,12 +87,10 @@ __device__ __forceinline__ void combine(const float2* __restrict__ ml, int64_t m
 
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(
-    int* __restrict__ clear, int hq, int hkv, int cols, const int4* __restrict__ dec_merges, int num_dec,
+    int hq, int hkv, int cols, const int4* __restrict__ dec_merges, int num_dec,
     const float* __restrict__ dec_acc, const float2* __restrict__ dec_ml,
     const int4* __restrict__ chunk_groups, int num_chunk, const float* __restrict__ chunk_acc,
     const float2* __restrict__ chunk_ml, uint16_t* __restrict__ o, float* __restrict__ lse) {
-    // the attention launch before this one left its work-queue counters for it to clear
-    if (clear && blockIdx.x == 0 && threadIdx.x < 8) clear[threadIdx.x * kQueueStride] = 0;
     const int G = hq / hkv;
     const int sub = threadIdx.x & (kLanes - 1);
     int col = (blockIdx.x * 256 + threadIdx.x) / kLanes;
@@ -126,7 +124,7 @@ __global__ void __launch_bounds__(256) merge_kernel(
 
 }  // namespace
 
-hipError_t launch_merge(const DevPlan& p, const Shape& sh, int* clear, const int4* dec_merges, int num_dec,
+hipError_t launch_merge(const DevPlan& p, const Shape& sh, const int4* dec_merges, int num_dec,
                         const float* dec_acc, const float2* dec_ml, const int4* chunk_groups,
                         int num_chunk, const float* chunk_acc, const float2* chunk_ml, void* o,
                         float* lse, hipStream_t stream, const LaunchEvents& ev) {
@@ -134,15 +132,15 @@ hipError_t launch_merge(const DevPlan& p, const Shape& sh, int* clear, const int
     const int G = sh.hq / sh.hkv;
     const int cols = chunk_cols_per_block();
     const int64_t columns = static_cast<int64_t>(num_dec) * G + static_cast<int64_t>(num_chunk) * cols;
-    if (columns <= 0) return clear ? launch_clear_queue(clear, stream) : hipSuccess;
+    if (columns <= 0) return hipSuccess;
     const int64_t per_block = 256 / kLanes;
     const dim3 grid(static_cast<unsigned>((columns + per_block - 1) / per_block)), block(256);
     auto oo = static_cast<uint16_t*>(o);
     if (sh.d == 128)
-        hipExtLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, ev.start, ev.stop, 0, clear, sh.hq, sh.hkv, cols, dec_merges,
+        hipExtLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, ev.start, ev.stop, 0, sh.hq, sh.hkv, cols, dec_merges,
                            num_dec, dec_acc, dec_ml, chunk_groups, num_chunk, chunk_acc, chunk_ml, oo, lse);
     else
-        hipExtLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, ev.start, ev.stop, 0, clear, sh.hq, sh.hkv, cols, dec_merges,
+        hipExtLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, ev.start, ev.stop, 0, sh.hq, sh.hkv, cols, dec_merges,
                            num_dec, dec_acc, dec_ml, chunk_groups, num_chunk, chunk_acc, chunk_ml, oo, lse);
     return hipGetLastError();
 }

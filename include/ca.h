@@ -212,8 +212,9 @@ ca_status ca_append_kv_rope(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan
  * bf16 with Hq/Hkv <= 16: one launch runs decode rows (split-KV, partials merged by log-sum-exp
  * weights) beside chunk rows (LDS-staged bf16 MFMA); fp32 storage uses a plain fp32 kernel.
  * When the chunk work outnumbers the workgroup slots, persistent workers take it from work
- * queues whose counters (in ctx) the call's last launch clears again: the launches of one call
- * must stay in the order the call enqueues them, which one stream guarantees.
+ * queues whose counters live in ctx (two sets, used by turns: each attention launch zeroes the
+ * set the next one claims from): the calls on one ctx must run in the order they are enqueued,
+ * which one stream (or events between streams) guarantees.
  */
 ca_status ca_mixed_attention(ca_ctx* ctx, const ca_attn_desc* desc, const ca_plan* plan,
                              const void* q, const void* k_cache, const void* v_cache,
