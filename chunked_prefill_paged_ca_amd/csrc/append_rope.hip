@@ -50,17 +50,17 @@ __device__ __forceinline__ Vec<T> load16(const T* p) {
     return v;
 }
 
-// Every store of the launch carries the non-temporal hint: nothing here reads what it wrote, and
-// the attention launch that follows reads it once.  Measured on the Mistral-7B step: the append
-// launch itself unchanged (9.6 -> 9.7 us), the attention launch after it 2.5-3.5 us shorter
-// (141 -> 139 us), as the streamed lines no longer sit dirty in L2 when it starts.
+// NT: every store of the launch carries the non-temporal hint (nothing here reads what it
+// wrote; the attention launch that follows reads it once).  That pays off for small appends and
+// costs for large ones (launch_append_rope chooses; measured there).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
+template <bool NT, typename T>
 __device__ __forceinline__ void store16(T* p, const Vec<T>& v) {
     u32x4 raw;
     __builtin_memcpy(&raw, &v, sizeof(raw));
-    __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
+    if constexpr (NT) __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = raw;
 }
 
 template <typename T>
@@ -81,7 +81,7 @@ __device__ __forceinline__ uint16_t narrow<uint16_t>(double x) { return double_t
 // blockDim.x: a multiple of 64 in [64, 1024], at least D / 2 (the threads that form the angles).
 // U: rotation units per thread in the first pass; each thread also loads U * 4 V elements
 // before its first store.
-template <typename T, int D, int U>
+template <typename T, int D, int U, bool NT>
 __global__ void __launch_bounds__(1024) append_rope_kernel(
     const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_page,
     const double* __restrict__ inv_freq, const T* q_in, T* q_out, const T* __restrict__ k_new,
@@ -147,9 +147,10 @@ __global__ void __launch_bounds__(1024) append_rope_kernel(
     T* vpage = v_cache + static_cast<int64_t>(page) * hkv * P * D;
     auto v_store = [&](int e, T val) {
         const int g = e / D, c = e - g * D;
-        __builtin_nontemporal_store(
-            val, &vpage[static_cast<int64_t>(g) * P * D + (((c >> 4) * (P >> 2) + (slot >> 2)) * 16 + (c & 15)) * 4 +
-                        (slot & 3)]);
+        T* dst = &vpage[static_cast<int64_t>(g) * P * D + (((c >> 4) * (P >> 2) + (slot >> 2)) * 16 + (c & 15)) * 4 +
+                        (slot & 3)];
+        if constexpr (NT) __builtin_nontemporal_store(val, dst);
+        else *dst = val;
     };
 #pragma unroll
     for (int j = 0; j < kV; ++j) {
@@ -178,15 +179,15 @@ __global__ void __launch_bounds__(1024) append_rope_kernel(
         if (u >= units) return;
         if (h < hq) {
             T* dst = q_out + (static_cast<int64_t>(t) * hq + h) * D;
-            store16(dst + i0, rx);
-            store16(dst + i0 + half, ry);
+            store16<NT>(dst + i0, rx);
+            store16<NT>(dst + i0 + half, ry);
         } else {
             // K page: the slot's 8-dim runs, one per 8-dim block (a vector unit never straddles
             // two blocks: it starts at a multiple of its length, which divides 8)
             T* dst = k_cache + (static_cast<int64_t>(page) * hkv + (h - hq)) * P * D;
             const int e0 = i0, e1 = i0 + half;
-            store16(dst + ((e0 >> 3) * P + slot) * 8 + (e0 & 7), rx);
-            store16(dst + ((e1 >> 3) * P + slot) * 8 + (e1 & 7), ry);
+            store16<NT>(dst + ((e0 >> 3) * P + slot) * 8 + (e0 & 7), rx);
+            store16<NT>(dst + ((e1 >> 3) * P + slot) * 8 + (e1 & 7), ry);
         }
     };
     // a wave whose lanes all lie past the last unit skips the math (wave-uniform test)
@@ -241,6 +242,14 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* 
                               const LaunchEvents& ev) {
     if (p.num_tokens <= 0) return hipSuccess;
     const int U = append_units_per_thread(sh, p.num_tokens, num_cus > 0 ? num_cus : 256);
+    // Non-temporal stores while the step appends at most 16384 (token, kv head) pairs.  Measured
+    // (same box, plain -> non-temporal): Mistral-7B step (4096 pairs) append 9.3 -> 9.2 us and
+    // the attention launch after it 139.4 -> 136.0 us; LLaMA2-70B share (12288) append 23.8 ->
+    // 27.2 us, attention 1024 -> 997 us; but a Llama-13B prompt (MHA, 40 kv heads) appended in
+    // steps of 512 / 2048 / 8192 tokens (20480+ pairs) 15.6 -> 25 / 52 -> 105 / 191 -> 418 us per
+    // step: the K and V slots of a token are 16-byte and 2-byte pieces of many cache lines, and
+    // streamed past L2 such partial lines cost far more than merged ones.
+    const bool nt = static_cast<int64_t>(p.num_tokens) * sh.hkv <= 16384;
     const int threads = append_threads(sh, U);
     // one 16-byte unit per copy thread: the staging is read over PCIe, where many small reads in
     // flight at once are what keeps the copy short
@@ -249,19 +258,24 @@ hipError_t launch_append_rope(const DevPlan& p, const Shape& sh, const int32_t* 
     const dim3 grid(p.num_tokens + copy_wgs), block(threads);
     const uint4* msrc = static_cast<const uint4*>(meta_src);
     uint4* mdst = static_cast<uint4*>(meta_dst);
-    auto go = [&](auto tag, auto d_tag, auto u_tag) {
+    auto go = [&](auto tag, auto d_tag, auto u_tag, auto nt_tag) {
         using T = decltype(tag);
         constexpr int D = decltype(d_tag)::value, Uc = decltype(u_tag)::value;
-        hipExtLaunchKernelGGL(append_rope_kernel<T, D, Uc>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos,
+        constexpr bool NTc = decltype(nt_tag)::value;
+        hipExtLaunchKernelGGL(append_rope_kernel<T, D, Uc, NTc>, grid, block, 0, stream, ev.start, ev.stop, 0, row_pos,
                               row_page, inv_freq, static_cast<const T*>(q_in), static_cast<T*>(q_out),
                               static_cast<const T*>(k_new), static_cast<const T*>(v_new), static_cast<T*>(k_cache),
                               static_cast<T*>(v_cache), sh.hq, sh.hkv, p.page_size, q_row, kv_row, p.num_tokens,
                               msrc, mdst, meta_n16);
     };
+    auto by_nt = [&](auto tag, auto d_tag, auto u_tag) {
+        if (nt) go(tag, d_tag, u_tag, std::true_type{});
+        else go(tag, d_tag, u_tag, std::false_type{});
+    };
     auto by_u = [&](auto tag, auto d_tag) {
-        if (U == 1) go(tag, d_tag, std::integral_constant<int, 1>{});
-        else if (U == 2) go(tag, d_tag, std::integral_constant<int, 2>{});
-        else go(tag, d_tag, std::integral_constant<int, 4>{});
+        if (U == 1) by_nt(tag, d_tag, std::integral_constant<int, 1>{});
+        else if (U == 2) by_nt(tag, d_tag, std::integral_constant<int, 2>{});
+        else by_nt(tag, d_tag, std::integral_constant<int, 4>{});
     };
     auto by_d = [&](auto tag) {
         if (sh.d == 128) by_u(tag, std::integral_constant<int, 128>{});
