@@ -619,8 +619,10 @@ def test_chunk_queue_mode(env, split):
     chunk on 2000 cached keys cut into 64-key splits (CA_CHUNK_SPLIT=64: ~1400 items, most of
     them claimed through the queue counters) beside three decodes, in one launch and (split)
     as a chunk-only launch.  Checked against the oracle, then the same attention launched four
-    more times, the third and fifth through the allocation-free entry point: the counters must
-    be back at zero after each launch, and which worker ran which item must not change a bit
+    more times, the third and fifth through the allocation-free entry point: each launch must
+    leave zeroed the counter set the next one claims from (the two sets alternate; with split,
+    a decode-only launch sits between the queue-mode ones), and which worker ran which item
+    must not change a bit
     (every item has its own partial slot, merged in a fixed order), so the ordinary launches
     agree bit for bit, and so do the two allocation-free ones (which lengthen the splits to fit
     their scratch, so they are held to the oracle's bar instead of to the others)."""
